@@ -1,0 +1,278 @@
+"""Plain fp64 CPU oracle of the sparsely-gated Mixture-of-Experts layer forward.
+
+TEST INFRASTRUCTURE ONLY.  This is the parity authority for the HIP path.
+Only the tests, the smoke check and the bench's CPU-baseline leg may import
+it; the product path never calls it and shares no code with it.
+
+Every stored input (fp32, or bf16 held as uint16 bit patterns) is widened
+exactly to fp64 and all arithmetic below runs in fp64.  Matrix products use
+numpy's BLAS (dgemm) and erf comes from scipy; nothing is blocked, fused or
+reordered beyond the definitions cited on each function.
+
+Sources (web pages on Mixture-of-Experts):
+  [LH]  "Mixture of Experts: Scaling Parameters Without Scaling Compute"
+        (ai-lecture-hall), section "The MoE layer" (the three-step definition
+        and the PyTorch listing) and section "The central problem: load
+        balancing" (the aux loss and expert capacity).
+  [LD]  "Mixture-of-Experts — making a model wider without using all of it for
+        every token" (llmdaily, day 59), sections "Replace one MLP with many
+        experts" and "Experts also have capacity limits".
+  [AB]  "Mixture of experts: big models, small bills" (aiinbed), section
+        "Experts and the router" and its "Run it" demo (stable descending sort).
+
+Readings where the pages are silent or garbled (all listed in the design notes):
+  * experts are numbered from 0;
+  * the router has no bias unless a workload supplies an fp32 logit bias;
+  * top-k ranks experts by logit, descending, equal logits -> lower index
+    first; softmax is monotone, so this is the same order as by probability;
+  * renormalisation divides the chosen probabilities by their sum;
+  * y sums the weighted expert outputs (each expert's output bias included)
+    in slot order; no residual is added inside the layer;
+  * GELU is the exact erf form;
+  * f_i counts the top-1 choice of every token before any capacity drop,
+    P_i averages the full softmax over all tokens, aux = E * sum_i f_i P_i;
+  * capacity (top-1 only) keeps, per expert, the C lowest-index tokens that
+    chose it; a dropped token's layer output is 0;
+  * rows of one expert's segment are ordered by token index.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+from scipy.special import erf as _erf
+
+MARGIN_MIN = 1e-3
+
+
+# ----------------------------------------------------------------------------
+# Input widening
+# ----------------------------------------------------------------------------
+def widen(a):
+    """Exact fp64 value of a stored array (fp32, or uint16 bf16 bit patterns)."""
+    if a is None:
+        return None
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    if a.dtype in (np.float32, np.float64):
+        return a.astype(np.float64)
+    raise TypeError(f"unsupported stored dtype {a.dtype}")
+
+
+# ----------------------------------------------------------------------------
+# Router: logits, softmax, top-k, weights   [LH "The MoE layer", steps 1-2]
+# ----------------------------------------------------------------------------
+def router_logits(x64, wr64, br64=None):
+    """g = W_r x for every token (rows of x), plus the optional fp32 logit bias."""
+    g = x64 @ wr64.T
+    if br64 is not None:
+        g = g + br64[None, :]
+    return g
+
+
+def softmax(g):
+    """p = softmax(g) over the experts axis (max subtracted; same value)."""
+    z = np.exp(g - g.max(axis=-1, keepdims=True))
+    return z / z.sum(axis=-1, keepdims=True)
+
+
+def topk_by_logit(g, k):
+    """Indices of the k largest logits per row, in rank order.
+
+    Ties go to the lower expert index: a stable sort of the negated logits keeps
+    equal keys in index order, as the stable descending sort of [AB]'s demo does.
+    Returns (idx int64 [T,k], margin [T]) where margin is the smallest gap
+    between consecutive ranked logits among ranks 0..k (k+1 is the first
+    unselected expert; with k == E there is no boundary gap).
+    """
+    order = np.argsort(-g, axis=-1, kind="stable")
+    idx = order[:, :k]
+    ranked = np.take_along_axis(g, order, axis=-1)
+    last = min(k + 1, g.shape[-1])
+    if last >= 2:
+        gaps = ranked[:, :last - 1] - ranked[:, 1:last]
+        margin = gaps.min(axis=-1)
+    else:
+        margin = np.full(g.shape[0], np.inf)
+    return idx, margin
+
+
+def routing_weights(p, idx, renormalize):
+    """Probabilities of the chosen experts, renormalised over the k chosen if asked."""
+    w = np.take_along_axis(p, idx, axis=-1)
+    if renormalize:
+        w = w / w.sum(axis=-1, keepdims=True)
+    return w
+
+
+# ----------------------------------------------------------------------------
+# Capacity and dispatch layout   [LH "The central problem", expert capacity]
+# ----------------------------------------------------------------------------
+def capacity_keep(idx, n_experts, capacity):
+    """Boolean keep mask [T,k].  Capacity applies to top-1 only: per expert, the
+    `capacity` lowest-index tokens that chose it are kept, the rest dropped."""
+    T, k = idx.shape
+    keep = np.ones((T, k), dtype=bool)
+    if capacity and capacity > 0:
+        if k != 1:
+            raise ValueError("capacity is defined for top-1 routing only")
+        seen = np.zeros(n_experts, dtype=np.int64)
+        for t in range(T):
+            e = idx[t, 0]
+            keep[t, 0] = seen[e] < capacity
+            seen[e] += 1
+    return keep
+
+
+def dispatch_layout(idx, keep, n_experts):
+    """Expert-major layout of the kept assignments.
+
+    counts[e]  kept rows of expert e
+    offsets    exclusive prefix sum of counts, offsets[E] = R
+    dest[t,s]  row of assignment (t,s) in the expert-major buffers, -1 if dropped
+    src[r]     assignment id t*k+s stored at row r (rows ordered by expert, then token)
+    """
+    T, k = idx.shape
+    counts = np.zeros(n_experts, dtype=np.int64)
+    for e in range(n_experts):
+        counts[e] = int(np.sum((idx == e) & keep))
+    offsets = np.zeros(n_experts + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(counts)
+    dest = np.full((T, k), -1, dtype=np.int64)
+    src = np.zeros(int(offsets[-1]), dtype=np.int64)
+    fill = offsets[:-1].copy()
+    for t in range(T):              # token order gives the row order inside each segment
+        for s in range(k):
+            if keep[t, s]:
+                e = idx[t, s]
+                dest[t, s] = fill[e]
+                src[fill[e]] = t * k + s
+                fill[e] += 1
+    return counts, offsets, dest, src
+
+
+# ----------------------------------------------------------------------------
+# Expert FFN   [LH "The MoE layer" listing: Linear(d, d_ff) -> GELU -> Linear(d_ff, d)]
+# ----------------------------------------------------------------------------
+def gelu_erf(z):
+    """Exact GELU: z * Phi(z) = z * (1 + erf(z / sqrt 2)) / 2."""
+    return 0.5 * z * (1.0 + _erf(z / math.sqrt(2.0)))
+
+
+def expert_ffn(rows64, w1e, b1e, w2e, b2e):
+    """W2 GELU(W1 v + b1) + b2 for every row v (fp64 in, fp64 out)."""
+    h = rows64 @ w1e.T
+    if b1e is not None:
+        h += b1e[None, :]
+    h = gelu_erf(h)
+    o = h @ w2e.T
+    if b2e is not None:
+        o += b2e[None, :]
+    return o
+
+
+# ----------------------------------------------------------------------------
+# Aux loss   [LH "The central problem", Switch-style loss; listing's last lines]
+# ----------------------------------------------------------------------------
+def aux_loss(idx, p, n_experts):
+    """aux = E * sum_i f_i * P_i.
+
+    f_i: fraction of tokens whose top-1 choice is i (before capacity).
+    P_i: mean over all tokens of the softmax probability of expert i.
+    Returns (aux, f, P, top1_count).
+    """
+    T = idx.shape[0]
+    top1_count = np.bincount(idx[:, 0], minlength=n_experts).astype(np.int64)
+    f = top1_count / T
+    P = p.mean(axis=0)
+    return float(n_experts * np.sum(f * P)), f, P, top1_count
+
+
+# ----------------------------------------------------------------------------
+# The layer
+# ----------------------------------------------------------------------------
+def route(inputs, desc):
+    """Router half of the layer for all tokens: everything but the expert FFNs."""
+    x64 = widen(inputs["x"])
+    g = router_logits(x64, widen(inputs["w_router"]), widen(inputs.get("b_router")))
+    p = softmax(g)
+    idx, margin = topk_by_logit(g, desc["top_k"])
+    w = routing_weights(p, idx, desc["renormalize"])
+    keep = capacity_keep(idx, desc["n_experts"], desc.get("capacity", 0))
+    counts, offsets, dest, src = dispatch_layout(idx, keep, desc["n_experts"])
+    aux, f, P, top1 = aux_loss(idx, p, desc["n_experts"])
+    return {"logits": g, "probs": p, "topk_idx": idx, "topk_w": w, "margin": margin,
+            "keep": keep, "counts": counts, "offsets": offsets, "dest": dest, "src": src,
+            "aux": aux, "f": f, "P": P, "top1_count": top1, "x64": x64}
+
+
+def forward(inputs, desc, tokens=None, chunk_rows=4096, check_margin=True):
+    """The whole layer forward: y [T,d] (or the rows `tokens` of it) and aux.
+
+    `tokens` (sorted or not) restricts the expert FFN work to those tokens'
+    rows; routing, capacity and aux always use all tokens, since capacity
+    depends on token order.  y rows are sum_s w[t,s] * FFN_{idx[t,s]}(x_t) over
+    kept slots, accumulated in slot order; 0 when every slot was dropped.
+    """
+    r = route(inputs, desc)
+    if check_margin:
+        bad = np.flatnonzero(r["margin"] <= MARGIN_MIN)
+        if bad.size:
+            raise ValueError(f"top-k logit margin <= {MARGIN_MIN} at tokens {bad[:8].tolist()}")
+    T, k = r["topk_idx"].shape
+    sel = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    y = np.zeros((sel.size, desc["d_model"]), dtype=np.float64)
+    contrib = np.zeros((sel.size, k, desc["d_model"]), dtype=np.float64)
+    x64 = r["x64"]
+    for e in range(desc["n_experts"]):
+        pos, slot = np.nonzero((r["topk_idx"][sel] == e) & r["keep"][sel])
+        if pos.size == 0:
+            continue                      # experts with no rows do no work
+        w1e = widen(inputs["w1"][e])
+        w2e = widen(inputs["w2"][e])
+        b1e = widen(inputs["b1"][e]) if inputs.get("b1") is not None else None
+        b2e = widen(inputs["b2"][e]) if inputs.get("b2") is not None else None
+        for c0 in range(0, pos.size, chunk_rows):
+            pp, ss = pos[c0:c0 + chunk_rows], slot[c0:c0 + chunk_rows]
+            contrib[pp, ss] = expert_ffn(x64[sel[pp]], w1e, b1e, w2e, b2e)
+    w = r["topk_w"][sel]
+    for s in range(k):                    # slot order
+        y += np.where(r["keep"][sel][:, s:s + 1], w[:, s:s + 1] * contrib[:, s], 0.0)
+    r["y"] = y
+    r["tokens"] = sel
+    return r
+
+
+def expert_outputs(inputs, desc, rows=None):
+    """Per-row expert outputs o[r] = FFN_e(x_perm[r]) in the expert-major layout,
+    and the post-GELU activations h[r]; optionally only for the given rows."""
+    r = route(inputs, desc)
+    R = int(r["offsets"][-1])
+    rows = np.arange(R) if rows is None else np.asarray(rows, dtype=np.int64)
+    k = desc["top_k"]
+    seg = np.searchsorted(r["offsets"], rows, side="right") - 1
+    d, F = desc["d_model"], desc["d_ff"]
+    o = np.zeros((rows.size, d))
+    h = np.zeros((rows.size, F))
+    for e in np.unique(seg):
+        m = seg == e
+        v = r["x64"][r["src"][rows[m]] // k]
+        w1e, w2e = widen(inputs["w1"][e]), widen(inputs["w2"][e])
+        hh = v @ w1e.T
+        if inputs.get("b1") is not None:
+            hh += widen(inputs["b1"][e])[None, :]
+        hh = gelu_erf(hh)
+        h[m] = hh
+        oo = hh @ w2e.T
+        if inputs.get("b2") is not None:
+            oo += widen(inputs["b2"][e])[None, :]
+        o[m] = oo
+    return {"rows": rows, "expert": seg, "h": h, "o": o, "route": r}
+
+
+def desc_of(spec):
+    """The option set of a workload as a plain dict."""
+    return {"tokens": spec.tokens, "d_model": spec.d_model, "d_ff": spec.d_ff,
+            "n_experts": spec.n_experts, "top_k": spec.top_k,
+            "renormalize": bool(spec.renormalize), "capacity": spec.capacity}

@@ -1,0 +1,78 @@
+"""Test inputs: the named workloads plus small shapes, all margin-repaired.
+
+Named workloads read their stored router bias and redrawn rows from
+``synth/input_params.json``.  Small test shapes are repaired here with the
+oracle's routing (the same rule: every top-k logit margin > 1e-3), so the GPU's
+fp32 router cannot legitimately choose differently from the fp64 oracle.
+"""
+from __future__ import annotations
+
+import functools
+
+import numpy as np
+
+import synth
+from synth import workloads as W
+from oracle import moe_oracle as O
+
+Workload = W.Workload
+
+# Small shapes that still span several tiles and end in a ragged tail.
+SMALL = {
+    "mid_small_bf16": Workload("mid_small_bf16", 300, 256, 512, 16, 2, True, 0, True, "bf16"),
+    "prefill_small_bf16": Workload("prefill_small_bf16", 1000, 512, 1024, 8, 2, True, 0, False,
+                                   "bf16", router_bias=True),
+    "switch_small_bf16": Workload("switch_small_bf16", 777, 256, 512, 64, 1, False,
+                                  W.capacity_for(777, 64), True, "bf16", router_bias=True),
+    "decode_small_bf16": Workload("decode_small_bf16", 5, 512, 1024, 8, 2, True, 0, True, "bf16"),
+    "top1_norenorm_fp32": Workload("top1_norenorm_fp32", 50, 128, 256, 4, 1, False, 0, True, "f32"),
+    "dense_mlp_fp32": Workload("dense_mlp_fp32", 33, 128, 384, 1, 1, True, 0, True, "f32"),
+    "topk_eq_e_bf16": Workload("topk_eq_e_bf16", 70, 256, 256, 4, 4, True, 0, True, "bf16"),
+    "single_token_bf16": Workload("single_token_bf16", 1, 256, 512, 8, 2, True, 0, True, "bf16"),
+    "capacity_one_bf16": Workload("capacity_one_bf16", 64, 128, 256, 8, 1, True, 1, True, "bf16"),
+}
+
+
+def small_router_bias(spec):
+    """A fixed skew for the small skewed shapes (no calibration needed)."""
+    E = spec.n_experts
+    if spec.top_k == 1:                     # hot experts: every 8th
+        b = np.zeros(E, np.float32)
+        b[::8] = 1.0
+        return b
+    return (-np.log(np.arange(1, E + 1))).astype(np.float32)
+
+
+def repair(spec, router_bias=None, max_rounds=50):
+    """Redraw token rows until every top-k logit margin exceeds 1e-3."""
+    wr64 = O.widen(W.make_router(spec))
+    b64 = None if router_bias is None else np.asarray(router_bias, np.float32).astype(np.float64)
+    redraw = {}
+    for _ in range(max_rounds):
+        g = O.router_logits(O.widen(W.make_x(spec, redraw)), wr64, b64)
+        _, margin = O.topk_by_logit(g, spec.top_k)
+        bad = np.flatnonzero(margin <= O.MARGIN_MIN)
+        if bad.size == 0:
+            return redraw
+        for r in bad.tolist():
+            redraw[r] = redraw.get(r, 0) + 1
+    raise RuntimeError("margin repair did not converge")
+
+
+@functools.lru_cache(maxsize=8)
+def inputs_for(name: str, seed: int = 0):
+    """(spec, inputs) for a named workload or a small test shape."""
+    if name in W.WORKLOADS:
+        spec = W.WORKLOADS[name]
+        if seed != 0:
+            spec = spec.with_(seed=seed)
+            rb = small_router_bias(spec) if spec.router_bias else None
+            return spec, synth.make_inputs(spec, redraw=repair(spec, rb), router_bias=rb, params={})
+        return spec, synth.make_inputs(spec)
+    spec = SMALL[name].with_(seed=seed)
+    rb = small_router_bias(spec) if spec.router_bias else None
+    return spec, synth.make_inputs(spec, redraw=repair(spec, rb), router_bias=rb, params={})
+
+
+def desc_of(spec):
+    return O.desc_of(spec)

@@ -1,0 +1,92 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check a pin catches each.
+
+This shows the pins are not vacuous: a dropped term, a wrong tie rule, a wrong
+GELU form, a missing renormalisation or a wrong capacity rule each fails at
+least one of them.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from oracle import moe_oracle as O
+from tests import test_oracle_pins as P
+
+
+def _tanh_gelu(z):
+    return 0.5 * z * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (z + 0.044715 * z ** 3)))
+
+
+def _no_renorm(p, idx, renormalize):
+    return np.take_along_axis(p, idx, axis=-1)
+
+
+def _ties_to_higher(g, k):
+    E = g.shape[-1]
+    rev = g[:, ::-1]
+    order = E - 1 - np.argsort(-rev, axis=-1, kind="stable")
+    idx = order[:, :k]
+    ranked = np.take_along_axis(g, order, axis=-1)
+    last = min(k + 1, E)
+    margin = (ranked[:, :last - 1] - ranked[:, 1:last]).min(axis=-1) if last >= 2 else np.full(g.shape[0], np.inf)
+    return idx, margin
+
+
+def _keep_last(idx, n_experts, capacity):
+    T, k = idx.shape
+    keep = np.ones((T, k), dtype=bool)
+    if capacity:
+        seen = np.zeros(n_experts, dtype=np.int64)
+        for t in reversed(range(T)):
+            e = idx[t, 0]
+            keep[t, 0] = seen[e] < capacity
+            seen[e] += 1
+    return keep
+
+
+def _aux_all_slots(idx, p, n_experts):
+    T = idx.shape[0]
+    cnt = np.bincount(idx.ravel(), minlength=n_experts)
+    f = cnt / T
+    P_ = p.mean(axis=0)
+    return float(n_experts * np.sum(f * P_)), f, P_, cnt
+
+
+def _ffn_no_out_bias(rows64, w1e, b1e, w2e, b2e):
+    h = rows64 @ w1e.T
+    if b1e is not None:
+        h += b1e[None, :]
+    return O.gelu_erf(h) @ w2e.T
+
+
+def _ffn_transposed(rows64, w1e, b1e, w2e, b2e):
+    # second matrix applied with the wrong orientation (square only when d == d_ff)
+    h = O.gelu_erf(rows64 @ w1e.T + (b1e[None, :] if b1e is not None else 0))
+    o = h @ w2e.T[::-1, ::-1]
+    return o + (b2e[None, :] if b2e is not None else 0)
+
+
+MUTATIONS = [
+    ("gelu_erf", _tanh_gelu, [P.test_gelu_against_math_erf_and_identities,
+                              P.test_single_expert_reduces_to_dense_mlp]),
+    ("routing_weights", _no_renorm, [P.test_eight_expert_example_top2]),
+    ("topk_by_logit", _ties_to_higher, [P.test_exact_ties_go_to_lower_index]),
+    ("capacity_keep", _keep_last, [P.test_capacity_hand_case]),
+    ("aux_loss", _aux_all_slots, [P.test_oracle_matches_listing_structure_toy]),
+    ("expert_ffn", _ffn_no_out_bias, [P.test_single_expert_reduces_to_dense_mlp]),
+    ("expert_ffn", _ffn_transposed, [P.test_oracle_matches_listing_structure_toy]),
+]
+
+
+@pytest.mark.parametrize("name,fake,pins", MUTATIONS, ids=[f"{m[0]}:{m[1].__name__}" for m in MUTATIONS])
+def test_planted_mistake_is_caught(monkeypatch, name, fake, pins):
+    from tests import _inputs
+    _inputs.inputs_for.cache_clear()
+    monkeypatch.setattr(O, name, fake)
+    caught = 0
+    for pin in pins:
+        try:
+            pin()
+        except (AssertionError, ValueError, IndexError):
+            caught += 1
+    assert caught == len(pins), f"mutation of {name} slipped past {len(pins) - caught} pin(s)"
