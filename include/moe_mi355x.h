@@ -1,0 +1,197 @@
+/*
+ * moe_mi355x.h -- C ABI of the sparsely-gated Mixture-of-Experts layer forward
+ * on one AMD Instinct MI355X (gfx950).
+ *
+ * The layer (web page "Mixture of Experts: Scaling Parameters Without Scaling
+ * Compute", section "The MoE layer"): for each token x the router computes
+ * logits g = W_r x and probabilities p = softmax(g), keeps the top-k experts,
+ * optionally renormalises their probabilities, runs each chosen expert
+ * FFN_e(x) = W2_e GELU(W1_e x + b1_e) + b2_e and returns the probability-
+ * weighted sum of their outputs.  The layer also returns the Switch-style
+ * auxiliary loss aux = E * sum_i f_i P_i (same page, section "The central
+ * problem: load balancing"), and for top-1 routing an optional expert capacity
+ * drops the assignments beyond C per expert, in token order (same section;
+ * also "Experts also have capacity limits" on the llmdaily day-59 page).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers.  Every array argument is a DEVICE pointer (HIP device memory, or
+ * memory the device can address) unless it says otherwise; descriptors are
+ * HOST pointers.  All device pointers must be 16-byte aligned.  Layouts are
+ * row-major; weights use the [out][in] layout of a linear layer.
+ * Ownership.  The caller allocates and frees every buffer, including the
+ * workspace sized by moe_workspace_size().  The library never allocates or
+ * frees device memory, never synchronises the stream or the device, and
+ * keeps no state between calls except a thread-local error message.
+ * Streams.  `stream` is a hipStream_t passed as void* (NULL = the null
+ * stream).  Every call only enqueues work on that stream, in order; buffers
+ * must stay alive until the stream has passed that work.
+ * Errors.  Every call validates its arguments on the host first; on any
+ * status other than MOE_OK nothing has been enqueued, and moe_last_error()
+ * describes the problem.  A failed kernel launch returns MOE_ERR_HIP; faults
+ * inside kernels surface when the caller synchronises.  No C++ exception
+ * crosses this interface.
+ * Precision.  x, the weights and the expert biases share `dtype`.  Matrix
+ * products accumulate in fp32; router logits, probabilities, the routing
+ * weights, the expert outputs `o` and the layer output `y` are fp32.  With
+ * dtype BF16 the post-GELU activations `h` are stored as moe_desc.h_mode says
+ * (rounded to bf16, nearest-even, or kept as two bf16 terms).
+ * Determinism.  No call uses floating-point atomics; repeated calls on the
+ * same inputs give bitwise-identical results.
+ * Limits.  1 <= tokens; 1 <= n_experts <= 64; 1 <= top_k <= min(8, n_experts);
+ * d_model and d_ff are multiples of 128; tokens * top_k * max(d_model, d_ff)
+ * must fit in int32 (else MOE_ERR_UNSUPPORTED).
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 };
+
+enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID = -1,      /* bad argument: shape, option, null or misaligned pointer */
+  MOE_ERR_UNSUPPORTED = -2,  /* valid layer, outside what this library implements */
+  MOE_ERR_WORKSPACE = -3,    /* workspace pointer NULL or smaller than moe_workspace_size() */
+  MOE_ERR_HIP = -4           /* the HIP runtime refused a launch */
+};
+
+/* Expert-FFN kernel choice (moe_desc.ffn_path).  AUTO resolves to TILED for
+ * bf16 layers averaging >= 256 rows per expert (MFMA-bound prefill) and to
+ * STREAM otherwise (weight-streaming, HBM-bound). */
+enum { MOE_FFN_AUTO = 0, MOE_FFN_TILED = 1, MOE_FFN_STREAM = 2 };
+
+/* Storage of the post-GELU activations h for a bf16 layer (moe_desc.h_mode).
+ *   MOE_H_BF16:  h rounded to bf16, [T*k][F] bf16 (2 bytes per element).
+ *   MOE_H_SPLIT: h kept as two bf16 terms, h = hi + lo with hi = bf16(h) and
+ *                lo = bf16(h - hi): plane hi [T*k][F] followed by plane lo
+ *                [T*k][F] (4 bytes per element in total); the second product
+ *                runs one MFMA per term, so o carries ~16 bits of h.
+ *   MOE_H_AUTO:  SPLIT on the STREAM path (its MFMA work is hidden under the
+ *                weight stream), BF16 on the TILED path.
+ * For an fp32 layer h is fp32 [T*k][F] and h_mode must be AUTO.
+ * The TILED path supports MOE_H_BF16 only. */
+enum { MOE_H_AUTO = 0, MOE_H_BF16 = 1, MOE_H_SPLIT = 2 };
+
+/* Options of one layer call (host struct). */
+typedef struct moe_desc {
+  int32_t tokens;          /* T */
+  int32_t d_model;         /* d */
+  int32_t d_ff;            /* F, hidden width of every expert */
+  int32_t n_experts;       /* E */
+  int32_t top_k;           /* k */
+  int32_t renormalize;     /* 1: divide the chosen probabilities by their sum */
+  int32_t capacity;        /* C > 0: keep at most C tokens per expert (top_k == 1 only); 0: no limit */
+  int32_t dtype;           /* MOE_DTYPE_* */
+  int32_t has_expert_bias; /* 1: b1 and b2 are given; 0: both absent */
+  int32_t ffn_path;        /* MOE_FFN_*: AUTO picks by rows per expert; the others force a kernel */
+  int32_t h_mode;          /* MOE_H_*: storage of the post-GELU activations h */
+} moe_desc;
+
+/* What the library will run for a descriptor (host struct, filled by moe_query_plan). */
+typedef struct moe_plan {
+  int32_t ffn_path;        /* resolved MOE_FFN_TILED or MOE_FFN_STREAM */
+  int32_t h_mode;          /* resolved MOE_H_BF16 or MOE_H_SPLIT (MOE_H_AUTO for fp32 layers) */
+  size_t h_bytes;          /* bytes of the h buffer moe_ffn_up writes: T*k*F*(2 or 4) */
+  size_t workspace_bytes;  /* same value as moe_workspace_size() */
+} moe_plan;
+
+/* Layer parameters (device pointers). */
+typedef struct moe_weights {
+  const void* w_router;    /* [E][d]    dtype  (router has no bias on the pages) */
+  const float* b_router;   /* [E]       fp32 logit bias added before softmax, or NULL */
+  const void* w1;          /* [E][F][d] dtype */
+  const void* b1;          /* [E][F]    dtype, NULL iff !has_expert_bias */
+  const void* w2;          /* [E][d][F] dtype */
+  const void* b2;          /* [E][d]    dtype, NULL iff !has_expert_bias */
+} moe_weights;
+
+/* Routing results (device pointers).  Which fields a call reads or writes is
+ * stated at each call; in moe_forward any field may be NULL (the workspace is
+ * used instead). */
+typedef struct moe_routing {
+  int32_t* topk_idx;       /* [T][k] chosen experts in rank order: logit descending, ties -> lower index */
+  float* topk_w;           /* [T][k] routing weights: probabilities, renormalised over the k if asked */
+  int32_t* counts;         /* [E]    rows kept per expert (after capacity) */
+  int32_t* offsets;        /* [E+1]  exclusive prefix sum of counts; offsets[E] = R, total kept rows */
+  int32_t* dest;           /* [T][k] row of assignment (t,s) in x_perm/h/o, -1 if dropped */
+  int32_t* src;            /* [T*k]  rows < R hold the assignment id t*k+s; rows >= R are not written */
+  int32_t* top1_count;     /* [E]    tokens whose first choice is e, before capacity (defines f_e) */
+  float* prob_mean;        /* [E]    P_e = mean over tokens of p_e */
+} moe_routing;
+
+/* Status code -> static string. */
+const char* moe_status_string(int status);
+
+/* Detail of the last non-OK status returned on this thread ("" if none). */
+const char* moe_last_error(void);
+
+/* Bytes of workspace that any call below needs for this descriptor (host
+ * output).  One workspace of this size serves every entry point. */
+int moe_workspace_size(const moe_desc* desc, size_t* bytes);
+
+/* Resolve the descriptor's AUTO choices (host output). */
+int moe_query_plan(const moe_desc* desc, moe_plan* plan);
+
+/* Router: logits = x W_r^T (+ b_router), softmax, top-k by logit, routing
+ * weights, and the aux loss.
+ *   x [T][d] dtype.  Writes out->topk_idx and out->topk_w (both required),
+ *   out->top1_count and out->prob_mean (each optional), and *aux (device fp32
+ *   scalar, optional): aux = E * sum_e (top1_count_e / T) * P_e. */
+int moe_route(const moe_desc* desc, const void* x, const moe_weights* w, moe_routing* out,
+              float* aux, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Dispatch: per-expert histogram of the assignments, prefix scan, capacity,
+ * stable ranks in token order, and the gather of token rows into
+ * expert-contiguous rows.
+ *   Reads r->topk_idx.  Writes r->counts, r->offsets, r->dest, r->src (all
+ *   required) and x_perm [T*k][d] dtype: rows 0..R-1 get x_perm[dest[t][s]] = x[t];
+ *   rows >= R are not written.  Inside expert e's segment rows follow token order. */
+int moe_permute(const moe_desc* desc, const void* x, moe_routing* r, void* x_perm,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/* First expert product with GELU fused into its epilogue:
+ *   h[r] = GELU_erf(x_perm[r] W1_e^T + b1_e) for every row r of expert e's segment
+ *   [offsets[e], offsets[e+1]).  x_perm [T*k][d] dtype; h is stored as the
+ *   resolved h_mode says (plan.h_bytes bytes).  offsets is the device array
+ *   from moe_permute. */
+int moe_ffn_up(const moe_desc* desc, const void* x_perm, const int32_t* offsets,
+               const moe_weights* w, void* h, void* workspace, size_t workspace_bytes,
+               void* stream);
+
+/* Second expert product: o[r] = h[r] W2_e^T + b2_e, h as moe_ffn_up wrote it,
+ * o [T*k][d] fp32. */
+int moe_ffn_down(const moe_desc* desc, const void* h, const int32_t* offsets,
+                 const moe_weights* w, float* o, void* workspace, size_t workspace_bytes,
+                 void* stream);
+
+/* The grouped expert FFN: moe_ffn_up then moe_ffn_down on the same stream. */
+int moe_grouped_ffn(const moe_desc* desc, const void* x_perm, const int32_t* offsets,
+                    const moe_weights* w, void* h, float* o, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/* Combine (web page "Mixture of Experts: Scaling Parameters Without Scaling
+ * Compute", section "The MoE layer", step 3): y[t] = sum over slots s = 0..k-1
+ * with dest[t][s] >= 0 of topk_w[t][s] * o[dest[t][s]], accumulated in fp32
+ * in slot order (no atomics); y[t] = 0 when every slot was dropped.
+ *   o [T*k][d] fp32, dest [T][k], topk_w [T][k] fp32, y [T][d] fp32. */
+int moe_combine(const moe_desc* desc, const float* o, const int32_t* dest, const float* topk_w,
+                float* y, void* stream);
+
+/* The whole layer: route, permute, grouped FFN, combine.
+ *   x [T][d] dtype -> y [T][d] fp32 and *aux (device fp32 scalar, optional).
+ *   routing may be NULL; any non-NULL field of it receives that result. */
+int moe_forward(const moe_desc* desc, const void* x, const moe_weights* w, float* y, float* aux,
+                moe_routing* routing, void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,255 @@
+"""ctypes binding of libmoe_mi355x.so: the C ABI's entry points under the same
+names, taking torch tensors.  Argument marshalling only -- every step of the
+layer runs in the library's HIP kernels.  There is no fallback: if the library
+is missing the import of this module's functions raises."""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe_mi355x.so")
+
+MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
+MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
+MOE_FFN_AUTO, MOE_FFN_TILED, MOE_FFN_STREAM = 0, 1, 2
+MOE_H_AUTO, MOE_H_BF16, MOE_H_SPLIT = 0, 1, 2
+
+ENTRY_POINTS = ("moe_status_string", "moe_last_error", "moe_workspace_size", "moe_query_plan",
+                "moe_route",
+                "moe_permute", "moe_ffn_up", "moe_ffn_down", "moe_grouped_ffn", "moe_combine",
+                "moe_forward")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+class CDesc(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("tokens", "d_model", "d_ff", "n_experts", "top_k", "renormalize", "capacity",
+                 "dtype", "has_expert_bias", "ffn_path", "h_mode")]
+
+
+class CPlan(ctypes.Structure):
+    _fields_ = [("ffn_path", ctypes.c_int32), ("h_mode", ctypes.c_int32),
+                ("h_bytes", ctypes.c_size_t), ("workspace_bytes", ctypes.c_size_t)]
+
+
+class CWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("w_router", "b_router", "w1", "b1", "w2", "b2")]
+
+
+class CRouting(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("topk_idx", "topk_w", "counts", "offsets", "dest", "src", "top1_count",
+                 "prob_mean")]
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m sparse_mixture_experts_49_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    pd, pw, pr = ctypes.POINTER(CDesc), ctypes.POINTER(CWeights), ctypes.POINTER(CRouting)
+    sig = {
+        "moe_status_string": (ctypes.c_char_p, [I]),
+        "moe_last_error": (ctypes.c_char_p, []),
+        "moe_workspace_size": (I, [pd, ctypes.POINTER(S)]),
+        "moe_query_plan": (I, [pd, ctypes.POINTER(CPlan)]),
+        "moe_route": (I, [pd, P, pw, pr, P, P, S, P]),
+        "moe_permute": (I, [pd, P, pr, P, P, S, P]),
+        "moe_ffn_up": (I, [pd, P, P, pw, P, P, S, P]),
+        "moe_ffn_down": (I, [pd, P, P, pw, P, P, S, P]),
+        "moe_grouped_ffn": (I, [pd, P, P, pw, P, P, P, S, P]),
+        "moe_combine": (I, [pd, P, P, P, P, P]),
+        "moe_forward": (I, [pd, P, pw, P, P, pr, P, S, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype, fn.argtypes = res, args
+    _lib = lib
+    return lib
+
+
+@dataclasses.dataclass
+class Desc:
+    tokens: int
+    d_model: int
+    d_ff: int
+    n_experts: int
+    top_k: int
+    renormalize: bool = True
+    capacity: int = 0
+    dtype: str = "bf16"          # "bf16" or "f32"
+    has_expert_bias: bool = True
+    ffn_path: int = MOE_FFN_AUTO
+    h_mode: int = MOE_H_AUTO
+
+    def to_c(self) -> CDesc:
+        return CDesc(self.tokens, self.d_model, self.d_ff, self.n_experts, self.top_k,
+                     int(bool(self.renormalize)), self.capacity,
+                     MOE_DTYPE_BF16 if self.dtype == "bf16" else MOE_DTYPE_F32,
+                     int(bool(self.has_expert_bias)), self.ffn_path, self.h_mode)
+
+    @property
+    def torch_dtype(self):
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+
+@dataclasses.dataclass
+class Weights:
+    w_router: torch.Tensor
+    w1: torch.Tensor
+    w2: torch.Tensor
+    b_router: Optional[torch.Tensor] = None
+    b1: Optional[torch.Tensor] = None
+    b2: Optional[torch.Tensor] = None
+
+    def to_c(self) -> CWeights:
+        return CWeights(*(_ptr(getattr(self, n)) for n in ("w_router", "b_router", "w1", "b1", "w2", "b2")))
+
+
+@dataclasses.dataclass
+class Routing:
+    topk_idx: Optional[torch.Tensor] = None
+    topk_w: Optional[torch.Tensor] = None
+    counts: Optional[torch.Tensor] = None
+    offsets: Optional[torch.Tensor] = None
+    dest: Optional[torch.Tensor] = None
+    src: Optional[torch.Tensor] = None
+    top1_count: Optional[torch.Tensor] = None
+    prob_mean: Optional[torch.Tensor] = None
+
+    @classmethod
+    def allocate(cls, desc: Desc, device) -> "Routing":
+        T, k, E = desc.tokens, desc.top_k, desc.n_experts
+        i32 = dict(dtype=torch.int32, device=device)
+        return cls(topk_idx=torch.empty(T, k, **i32),
+                   topk_w=torch.empty(T, k, dtype=torch.float32, device=device),
+                   counts=torch.empty(E, **i32), offsets=torch.empty(E + 1, **i32),
+                   dest=torch.empty(T, k, **i32), src=torch.empty(T * k, **i32),
+                   top1_count=torch.empty(E, **i32),
+                   prob_mean=torch.empty(E, dtype=torch.float32, device=device))
+
+    def to_c(self) -> CRouting:
+        return CRouting(*(_ptr(getattr(self, f.name)) for f in dataclasses.fields(self)))
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the MoE library must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def _check(status: int):
+    if status != MOE_OK:
+        lib = load_library()
+        raise MoeError(status, lib.moe_last_error().decode() or lib.moe_status_string(status).decode())
+
+
+def moe_workspace_size(desc: Desc) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().moe_workspace_size(ctypes.byref(desc.to_c()), ctypes.byref(n)))
+    return n.value
+
+
+def moe_query_plan(desc: Desc) -> dict:
+    """Resolved kernel path, h storage mode, h buffer bytes and workspace bytes."""
+    p = CPlan()
+    _check(load_library().moe_query_plan(ctypes.byref(desc.to_c()), ctypes.byref(p)))
+    return {"ffn_path": p.ffn_path, "h_mode": p.h_mode, "h_bytes": p.h_bytes,
+            "workspace_bytes": p.workspace_bytes}
+
+
+def alloc_h(desc: Desc, device) -> torch.Tensor:
+    """A buffer for the post-GELU activations as moe_ffn_up writes them."""
+    plan = moe_query_plan(desc)
+    rows = desc.tokens * desc.top_k
+    if desc.dtype == "f32":
+        return torch.empty(rows, desc.d_ff, dtype=torch.float32, device=device)
+    if plan["h_mode"] == MOE_H_SPLIT:
+        return torch.empty(2, rows, desc.d_ff, dtype=torch.bfloat16, device=device)
+    return torch.empty(rows, desc.d_ff, dtype=torch.bfloat16, device=device)
+
+
+def alloc_workspace(desc: Desc, device) -> torch.Tensor:
+    return torch.empty(moe_workspace_size(desc), dtype=torch.uint8, device=device)
+
+
+def moe_route(desc, x, weights, routing, aux=None, workspace=None, stream=None):
+    ws = workspace if workspace is not None else alloc_workspace(desc, x.device)
+    _check(load_library().moe_route(ctypes.byref(desc.to_c()), _ptr(x), ctypes.byref(weights.to_c()),
+                                    ctypes.byref(routing.to_c()), _ptr(aux), _ptr(ws), ws.numel(),
+                                    _stream(stream)))
+
+
+def moe_permute(desc, x, routing, x_perm, workspace=None, stream=None):
+    ws = workspace if workspace is not None else alloc_workspace(desc, x.device)
+    _check(load_library().moe_permute(ctypes.byref(desc.to_c()), _ptr(x), ctypes.byref(routing.to_c()),
+                                      _ptr(x_perm), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def moe_ffn_up(desc, x_perm, offsets, weights, h, workspace=None, stream=None):
+    ws = workspace if workspace is not None else alloc_workspace(desc, x_perm.device)
+    _check(load_library().moe_ffn_up(ctypes.byref(desc.to_c()), _ptr(x_perm), _ptr(offsets),
+                                     ctypes.byref(weights.to_c()), _ptr(h), _ptr(ws), ws.numel(),
+                                     _stream(stream)))
+
+
+def moe_ffn_down(desc, h, offsets, weights, o, workspace=None, stream=None):
+    ws = workspace if workspace is not None else alloc_workspace(desc, h.device)
+    _check(load_library().moe_ffn_down(ctypes.byref(desc.to_c()), _ptr(h), _ptr(offsets),
+                                       ctypes.byref(weights.to_c()), _ptr(o), _ptr(ws), ws.numel(),
+                                       _stream(stream)))
+
+
+def moe_grouped_ffn(desc, x_perm, offsets, weights, h, o, workspace=None, stream=None):
+    ws = workspace if workspace is not None else alloc_workspace(desc, x_perm.device)
+    _check(load_library().moe_grouped_ffn(ctypes.byref(desc.to_c()), _ptr(x_perm), _ptr(offsets),
+                                          ctypes.byref(weights.to_c()), _ptr(h), _ptr(o), _ptr(ws),
+                                          ws.numel(), _stream(stream)))
+
+
+def moe_combine(desc, o, dest, topk_w, y, stream=None):
+    _check(load_library().moe_combine(ctypes.byref(desc.to_c()), _ptr(o), _ptr(dest), _ptr(topk_w),
+                                      _ptr(y), _stream(stream)))
+
+
+def moe_forward(desc, x, weights, y, aux=None, routing=None, workspace=None, stream=None):
+    ws = workspace if workspace is not None else alloc_workspace(desc, x.device)
+    r = ctypes.byref(routing.to_c()) if routing is not None else None
+    _check(load_library().moe_forward(ctypes.byref(desc.to_c()), _ptr(x), ctypes.byref(weights.to_c()),
+                                      _ptr(y), _ptr(aux), r, _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def forward(x: torch.Tensor, weights: Weights, desc: Desc, workspace=None, stream=None):
+    """The layer's module-style call: returns (y [T, d] fp32, aux fp32 scalar tensor)."""
+    y = torch.empty(desc.tokens, desc.d_model, dtype=torch.float32, device=x.device)
+    aux = torch.empty((), dtype=torch.float32, device=x.device)
+    moe_forward(desc, x, weights, y, aux, None, workspace, stream)
+    return y, aux

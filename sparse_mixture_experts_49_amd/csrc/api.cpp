@@ -1,0 +1,440 @@
+// C ABI of the MoE layer forward: argument validation, workspace carving and
+// the launch sequence.  Kernels live in router.hip, permute.hip, ffn.hip and
+// combine.hip.  No call allocates, frees or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <limits>
+
+#include "../../include/moe_mi355x.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return MOE_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define MOE_REQUIRE_PTR(p, name)                                                       \
+  do {                                                                                 \
+    if (!(p)) return fail(MOE_ERR_INVALID, "%s must not be NULL", name);               \
+    if (!aligned16(p)) return fail(MOE_ERR_INVALID, "%s must be 16-byte aligned", name); \
+  } while (0)
+#define MOE_OPTIONAL_PTR(p, name)                                                      \
+  do {                                                                                 \
+    if ((p) && !aligned16(p)) return fail(MOE_ERR_INVALID, "%s must be 16-byte aligned", name); \
+  } while (0)
+
+int validate_desc(const moe_desc* d) {
+  if (!d) return fail(MOE_ERR_INVALID, "desc must not be NULL");
+  if (d->tokens < 1) return fail(MOE_ERR_INVALID, "tokens must be >= 1 (got %d)", d->tokens);
+  if (d->n_experts < 1) return fail(MOE_ERR_INVALID, "n_experts must be >= 1 (got %d)", d->n_experts);
+  if (d->n_experts > 64)
+    return fail(MOE_ERR_UNSUPPORTED, "n_experts must be <= 64 (got %d)", d->n_experts);
+  if (d->top_k < 1 || d->top_k > d->n_experts)
+    return fail(MOE_ERR_INVALID, "top_k must be in [1, n_experts] (got %d)", d->top_k);
+  if (d->top_k > 8) return fail(MOE_ERR_UNSUPPORTED, "top_k must be <= 8 (got %d)", d->top_k);
+  if (d->d_model < 1 || d->d_ff < 1)
+    return fail(MOE_ERR_INVALID, "d_model and d_ff must be >= 1");
+  if (d->d_model % 128 || d->d_ff % 128)
+    return fail(MOE_ERR_UNSUPPORTED, "d_model (%d) and d_ff (%d) must be multiples of 128",
+                d->d_model, d->d_ff);
+  if (d->renormalize != 0 && d->renormalize != 1)
+    return fail(MOE_ERR_INVALID, "renormalize must be 0 or 1");
+  if (d->capacity < 0) return fail(MOE_ERR_INVALID, "capacity must be >= 0");
+  if (d->capacity > 0 && d->top_k != 1)
+    return fail(MOE_ERR_INVALID, "capacity is defined for top_k == 1 only (top_k = %d)", d->top_k);
+  if (d->dtype != MOE_DTYPE_F32 && d->dtype != MOE_DTYPE_BF16)
+    return fail(MOE_ERR_INVALID, "dtype must be MOE_DTYPE_F32 or MOE_DTYPE_BF16");
+  if (d->has_expert_bias != 0 && d->has_expert_bias != 1)
+    return fail(MOE_ERR_INVALID, "has_expert_bias must be 0 or 1");
+  if (d->ffn_path < MOE_FFN_AUTO || d->ffn_path > MOE_FFN_STREAM)
+    return fail(MOE_ERR_INVALID, "ffn_path must be MOE_FFN_AUTO, _TILED or _STREAM");
+  if (d->ffn_path == MOE_FFN_TILED && d->dtype != MOE_DTYPE_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "the LDS-tiled expert kernel is bf16 only");
+  if (d->h_mode < MOE_H_AUTO || d->h_mode > MOE_H_SPLIT)
+    return fail(MOE_ERR_INVALID, "h_mode must be MOE_H_AUTO, _BF16 or _SPLIT");
+  if (d->dtype == MOE_DTYPE_F32 && d->h_mode != MOE_H_AUTO)
+    return fail(MOE_ERR_INVALID, "h_mode must be MOE_H_AUTO for an fp32 layer (h is fp32)");
+  if (d->ffn_path == MOE_FFN_TILED && d->h_mode == MOE_H_SPLIT)
+    return fail(MOE_ERR_UNSUPPORTED, "the LDS-tiled expert kernel supports MOE_H_BF16 only");
+  const long long rows = (long long)d->tokens * d->top_k;
+  const long long widest = d->d_model > d->d_ff ? d->d_model : d->d_ff;
+  if (rows * widest > std::numeric_limits<int32_t>::max())
+    return fail(MOE_ERR_UNSUPPORTED, "tokens * top_k * max(d_model, d_ff) exceeds int32");
+  return MOE_OK;
+}
+
+int row_bound(const moe_desc* d) {
+  // Any expert holds at most one row per token, and at most `capacity`.
+  int b = d->tokens;
+  if (d->capacity > 0 && d->capacity < b) b = d->capacity;
+  return b;
+}
+
+int max_rows(const moe_desc* d) {
+  // Total rows R <= T*k, and <= E*capacity under a capacity limit.
+  long long r = (long long)d->tokens * d->top_k;
+  if (d->capacity > 0) {
+    const long long c = (long long)d->capacity * d->n_experts;
+    if (c < r) r = c;
+  }
+  return (int)r;
+}
+
+// AUTO choices, resolved from the descriptor alone (never from device data).
+struct Plan {
+  int path;      // MOE_FFN_TILED or MOE_FFN_STREAM
+  int h_mode;    // MOE_H_BF16 / MOE_H_SPLIT, or MOE_H_AUTO for fp32 layers
+  size_t h_elem; // bytes per h element
+};
+
+int resolve(const moe_desc* d, Plan& p) {
+  const bool bf16 = d->dtype == MOE_DTYPE_BF16;
+  p.path = d->ffn_path;
+  if (p.path == MOE_FFN_AUTO)
+    p.path = (bf16 && (double)max_rows(d) / d->n_experts >= 256.0) ? MOE_FFN_TILED : MOE_FFN_STREAM;
+  if (!bf16) {
+    p.h_mode = MOE_H_AUTO;
+    p.h_elem = 4;
+    return MOE_OK;
+  }
+  p.h_mode = d->h_mode;
+  if (p.h_mode == MOE_H_AUTO) p.h_mode = p.path == MOE_FFN_TILED ? MOE_H_BF16 : MOE_H_SPLIT;
+  if (p.path == MOE_FFN_TILED && p.h_mode == MOE_H_SPLIT)
+    return fail(MOE_ERR_UNSUPPORTED, "the LDS-tiled expert kernel supports MOE_H_BF16 only");
+  p.h_elem = p.h_mode == MOE_H_SPLIT ? 4 : 2;
+  return MOE_OK;
+}
+
+int validate_weights(const moe_desc* d, const moe_weights* w, bool router, bool experts) {
+  if (!w) return fail(MOE_ERR_INVALID, "weights must not be NULL");
+  if (router) {
+    MOE_REQUIRE_PTR(w->w_router, "w_router");
+    MOE_OPTIONAL_PTR(w->b_router, "b_router");
+  }
+  if (experts) {
+    MOE_REQUIRE_PTR(w->w1, "w1");
+    MOE_REQUIRE_PTR(w->w2, "w2");
+    if (d->has_expert_bias) {
+      MOE_REQUIRE_PTR(w->b1, "b1");
+      MOE_REQUIRE_PTR(w->b2, "b2");
+    } else if (w->b1 || w->b2) {
+      return fail(MOE_ERR_INVALID, "b1/b2 given but has_expert_bias == 0");
+    }
+  }
+  return MOE_OK;
+}
+
+size_t elem_bytes(const moe_desc* d) { return d->dtype == MOE_DTYPE_BF16 ? 2 : 4; }
+
+// Workspace carving: every region starts on a 256-byte boundary.
+struct Layout {
+  size_t part_psum, part_top1, blk_hist, blk_base;
+  size_t topk_idx, topk_w, counts, offsets, dest, src, top1, prob_mean;
+  size_t x_perm, h, o;
+  size_t total;
+};
+
+size_t up256(size_t v) { return (v + 255) & ~size_t(255); }
+
+Layout layout_of(const moe_desc* d) {
+  Layout L{};
+  const size_t T = d->tokens, E = d->n_experts, k = d->top_k, A = T * k;
+  const size_t rb = moe::router_blocks(d->tokens), pb = moe::permute_blocks((int)A);
+  const size_t s = elem_bytes(d);
+  size_t p = 0;
+  auto take = [&](size_t bytes) { size_t at = p; p += up256(bytes); return at; };
+  L.part_psum = take(rb * E * sizeof(double));
+  L.part_top1 = take(rb * E * sizeof(int32_t));
+  L.blk_hist = take(pb * E * sizeof(int32_t));
+  L.blk_base = take(pb * E * sizeof(int32_t));
+  L.topk_idx = take(A * 4);
+  L.topk_w = take(A * 4);
+  L.counts = take(E * 4);
+  L.offsets = take((E + 1) * 4);
+  L.dest = take(A * 4);
+  L.src = take(A * 4);
+  L.top1 = take(E * 4);
+  L.prob_mean = take(E * 4);
+  L.x_perm = take(A * d->d_model * s);
+  Plan plan{};
+  resolve(d, plan);
+  L.h = take(A * d->d_ff * plan.h_elem);
+  L.o = take(A * d->d_model * sizeof(float));
+  L.total = p;
+  return L;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<uint8_t*>(ws) + off);
+}
+
+int check_ws(const moe_desc* d, void* ws, size_t bytes, Layout& L) {
+  L = layout_of(d);
+  if (!ws) return fail(MOE_ERR_WORKSPACE, "workspace must not be NULL");
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+    return fail(MOE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (bytes < L.total)
+    return fail(MOE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", bytes, L.total);
+  return MOE_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+int launch_route(const moe_desc* d, const void* x, const moe_weights* w, int32_t* idx, float* wt,
+                 int32_t* top1, float* pmean, float* aux, const Layout& L, void* ws,
+                 hipStream_t s) {
+  moe::RouterArgs a{};
+  a.bf16 = d->dtype == MOE_DTYPE_BF16;
+  a.x = x;
+  a.w_router = w->w_router;
+  a.b_router = w->b_router;
+  a.T = d->tokens;
+  a.d = d->d_model;
+  a.E = d->n_experts;
+  a.k = d->top_k;
+  a.renorm = d->renormalize;
+  a.topk_idx = idx;
+  a.topk_w = wt;
+  a.part_psum = at<double>(ws, L.part_psum);
+  a.part_top1 = at<int32_t>(ws, L.part_top1);
+  a.top1_count = top1;
+  a.prob_mean = pmean;
+  a.aux = aux;
+  return hip_status(moe::launch_router(a, s), "router launch");
+}
+
+int launch_perm(const moe_desc* d, const void* x, const int32_t* idx, int32_t* counts,
+                int32_t* offsets, int32_t* dest, int32_t* src, void* x_perm, const Layout& L,
+                void* ws, hipStream_t s) {
+  moe::PermuteArgs a{};
+  a.bf16 = d->dtype == MOE_DTYPE_BF16;
+  a.x = x;
+  a.topk_idx = idx;
+  a.T = d->tokens;
+  a.d = d->d_model;
+  a.E = d->n_experts;
+  a.k = d->top_k;
+  a.capacity = d->capacity;
+  a.counts = counts;
+  a.offsets = offsets;
+  a.dest = dest;
+  a.src = src;
+  a.x_perm = x_perm;
+  a.blk_hist = at<int32_t>(ws, L.blk_hist);
+  a.blk_base = at<int32_t>(ws, L.blk_base);
+  return hip_status(moe::launch_permute(a, s), "permute launch");
+}
+
+int launch_one_ffn(const moe_desc* d, bool up, const void* in, const int32_t* offsets,
+                   const moe_weights* w, void* out, hipStream_t s) {
+  Plan plan{};
+  if (int st = resolve(d, plan)) return st;
+  moe::FfnArgs a{};
+  a.split = plan.h_mode == MOE_H_SPLIT;
+  a.plane = (size_t)d->tokens * d->top_k * d->d_ff;
+  a.bf16 = d->dtype == MOE_DTYPE_BF16;
+  a.up = up;
+  a.a = in;
+  a.offsets = offsets;
+  a.w = up ? w->w1 : w->w2;
+  a.bias = d->has_expert_bias ? (up ? w->b1 : w->b2) : nullptr;
+  a.out = out;
+  a.E = d->n_experts;
+  a.N = up ? d->d_ff : d->d_model;
+  a.K = up ? d->d_model : d->d_ff;
+  a.max_rows_per_expert = row_bound(d);
+  a.max_rows = max_rows(d);
+  a.path = plan.path;
+  return hip_status(moe::launch_ffn(a, s), up ? "ffn up launch" : "ffn down launch");
+}
+
+int launch_comb(const moe_desc* d, const float* o, const int32_t* dest, const float* wt, float* y,
+                hipStream_t s) {
+  moe::CombineArgs a{o, dest, wt, y, d->tokens, d->d_model, d->top_k};
+  return hip_status(moe::launch_combine(a, s), "combine launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID: return "MOE_ERR_INVALID: invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: outside the implemented limits";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing or too small";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* moe_last_error(void) { return g_err; }
+
+int moe_workspace_size(const moe_desc* desc, size_t* bytes) {
+  if (int st = validate_desc(desc)) return st;
+  Plan p{};
+  if (int st = resolve(desc, p)) return st;
+  if (!bytes) return fail(MOE_ERR_INVALID, "bytes must not be NULL");
+  *bytes = layout_of(desc).total;
+  return ok();
+}
+
+int moe_query_plan(const moe_desc* desc, moe_plan* plan) {
+  if (int st = validate_desc(desc)) return st;
+  if (!plan) return fail(MOE_ERR_INVALID, "plan must not be NULL");
+  Plan p{};
+  if (int st = resolve(desc, p)) return st;
+  plan->ffn_path = p.path;
+  plan->h_mode = p.h_mode;
+  plan->h_bytes = (size_t)desc->tokens * desc->top_k * desc->d_ff * p.h_elem;
+  plan->workspace_bytes = layout_of(desc).total;
+  return ok();
+}
+
+int moe_route(const moe_desc* desc, const void* x, const moe_weights* w, moe_routing* out,
+              float* aux, void* ws, size_t ws_bytes, void* stream) {
+  if (int st = validate_desc(desc)) return st;
+  MOE_REQUIRE_PTR(x, "x");
+  if (int st = validate_weights(desc, w, true, false)) return st;
+  if (!out) return fail(MOE_ERR_INVALID, "out must not be NULL");
+  MOE_REQUIRE_PTR(out->topk_idx, "out->topk_idx");
+  MOE_REQUIRE_PTR(out->topk_w, "out->topk_w");
+  MOE_OPTIONAL_PTR(out->top1_count, "out->top1_count");
+  MOE_OPTIONAL_PTR(out->prob_mean, "out->prob_mean");
+  Layout L;
+  if (int st = check_ws(desc, ws, ws_bytes, L)) return st;
+  return launch_route(desc, x, w, out->topk_idx, out->topk_w, out->top1_count, out->prob_mean,
+                      aux, L, ws, static_cast<hipStream_t>(stream));
+}
+
+int moe_permute(const moe_desc* desc, const void* x, moe_routing* r, void* x_perm, void* ws,
+                size_t ws_bytes, void* stream) {
+  if (int st = validate_desc(desc)) return st;
+  MOE_REQUIRE_PTR(x, "x");
+  if (!r) return fail(MOE_ERR_INVALID, "r must not be NULL");
+  MOE_REQUIRE_PTR(r->topk_idx, "r->topk_idx");
+  MOE_REQUIRE_PTR(r->counts, "r->counts");
+  MOE_REQUIRE_PTR(r->offsets, "r->offsets");
+  MOE_REQUIRE_PTR(r->dest, "r->dest");
+  MOE_REQUIRE_PTR(r->src, "r->src");
+  MOE_REQUIRE_PTR(x_perm, "x_perm");
+  Layout L;
+  if (int st = check_ws(desc, ws, ws_bytes, L)) return st;
+  return launch_perm(desc, x, r->topk_idx, r->counts, r->offsets, r->dest, r->src, x_perm, L, ws,
+                     static_cast<hipStream_t>(stream));
+}
+
+int moe_ffn_up(const moe_desc* desc, const void* x_perm, const int32_t* offsets,
+               const moe_weights* w, void* h, void* ws, size_t ws_bytes, void* stream) {
+  if (int st = validate_desc(desc)) return st;
+  MOE_REQUIRE_PTR(x_perm, "x_perm");
+  MOE_REQUIRE_PTR(offsets, "offsets");
+  MOE_REQUIRE_PTR(h, "h");
+  if (int st = validate_weights(desc, w, false, true)) return st;
+  Layout L;
+  if (int st = check_ws(desc, ws, ws_bytes, L)) return st;
+  return launch_one_ffn(desc, true, x_perm, offsets, w, h, static_cast<hipStream_t>(stream));
+}
+
+int moe_ffn_down(const moe_desc* desc, const void* h, const int32_t* offsets,
+                 const moe_weights* w, float* o, void* ws, size_t ws_bytes, void* stream) {
+  if (int st = validate_desc(desc)) return st;
+  MOE_REQUIRE_PTR(h, "h");
+  MOE_REQUIRE_PTR(offsets, "offsets");
+  MOE_REQUIRE_PTR(o, "o");
+  if (int st = validate_weights(desc, w, false, true)) return st;
+  Layout L;
+  if (int st = check_ws(desc, ws, ws_bytes, L)) return st;
+  return launch_one_ffn(desc, false, h, offsets, w, o, static_cast<hipStream_t>(stream));
+}
+
+int moe_grouped_ffn(const moe_desc* desc, const void* x_perm, const int32_t* offsets,
+                    const moe_weights* w, void* h, float* o, void* ws, size_t ws_bytes,
+                    void* stream) {
+  if (int st = validate_desc(desc)) return st;
+  MOE_REQUIRE_PTR(x_perm, "x_perm");
+  MOE_REQUIRE_PTR(offsets, "offsets");
+  MOE_REQUIRE_PTR(h, "h");
+  MOE_REQUIRE_PTR(o, "o");
+  if (int st = validate_weights(desc, w, false, true)) return st;
+  Layout L;
+  if (int st = check_ws(desc, ws, ws_bytes, L)) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (int st = launch_one_ffn(desc, true, x_perm, offsets, w, h, s)) return st;
+  return launch_one_ffn(desc, false, h, offsets, w, o, s);
+}
+
+int moe_combine(const moe_desc* desc, const float* o, const int32_t* dest, const float* topk_w,
+                float* y, void* stream) {
+  if (int st = validate_desc(desc)) return st;
+  MOE_REQUIRE_PTR(o, "o");
+  MOE_REQUIRE_PTR(dest, "dest");
+  MOE_REQUIRE_PTR(topk_w, "topk_w");
+  MOE_REQUIRE_PTR(y, "y");
+  return launch_comb(desc, o, dest, topk_w, y, static_cast<hipStream_t>(stream));
+}
+
+int moe_forward(const moe_desc* desc, const void* x, const moe_weights* w, float* y, float* aux,
+                moe_routing* routing, void* ws, size_t ws_bytes, void* stream) {
+  if (int st = validate_desc(desc)) return st;
+  MOE_REQUIRE_PTR(x, "x");
+  MOE_REQUIRE_PTR(y, "y");
+  if (int st = validate_weights(desc, w, true, true)) return st;
+  moe_routing r{};
+  if (routing) {
+    r = *routing;
+    MOE_OPTIONAL_PTR(r.topk_idx, "routing->topk_idx");
+    MOE_OPTIONAL_PTR(r.topk_w, "routing->topk_w");
+    MOE_OPTIONAL_PTR(r.counts, "routing->counts");
+    MOE_OPTIONAL_PTR(r.offsets, "routing->offsets");
+    MOE_OPTIONAL_PTR(r.dest, "routing->dest");
+    MOE_OPTIONAL_PTR(r.src, "routing->src");
+    MOE_OPTIONAL_PTR(r.top1_count, "routing->top1_count");
+    MOE_OPTIONAL_PTR(r.prob_mean, "routing->prob_mean");
+  }
+  Layout L;
+  if (int st = check_ws(desc, ws, ws_bytes, L)) return st;
+  if (!r.topk_idx) r.topk_idx = at<int32_t>(ws, L.topk_idx);
+  if (!r.topk_w) r.topk_w = at<float>(ws, L.topk_w);
+  if (!r.counts) r.counts = at<int32_t>(ws, L.counts);
+  if (!r.offsets) r.offsets = at<int32_t>(ws, L.offsets);
+  if (!r.dest) r.dest = at<int32_t>(ws, L.dest);
+  if (!r.src) r.src = at<int32_t>(ws, L.src);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  void* x_perm = at<void>(ws, L.x_perm);
+  void* h = at<void>(ws, L.h);
+  float* o = at<float>(ws, L.o);
+  if (int st = launch_route(desc, x, w, r.topk_idx, r.topk_w, r.top1_count, r.prob_mean, aux, L,
+                            ws, s))
+    return st;
+  if (int st = launch_perm(desc, x, r.topk_idx, r.counts, r.offsets, r.dest, r.src, x_perm, L, ws,
+                           s))
+    return st;
+  if (int st = launch_one_ffn(desc, true, x_perm, r.offsets, w, h, s)) return st;
+  if (int st = launch_one_ffn(desc, false, h, r.offsets, w, o, s)) return st;
+  return launch_comb(desc, o, r.dest, r.topk_w, y, s);
+}
+
+}  // extern "C"

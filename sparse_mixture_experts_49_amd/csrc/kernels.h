@@ -1,0 +1,68 @@
+// Host-side launch interface between the C ABI (api.cpp) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+struct RouterArgs {
+  bool bf16;
+  const void* x;
+  const void* w_router;
+  const float* b_router;
+  int T, d, E, k, renorm;
+  int32_t* topk_idx;
+  float* topk_w;
+  double* part_psum;       // [router_blocks(T)][E]
+  int32_t* part_top1;      // [router_blocks(T)][E]
+  int32_t* top1_count;     // optional
+  float* prob_mean;        // optional
+  float* aux;              // optional
+};
+int router_blocks(int T);
+hipError_t launch_router(const RouterArgs& a, hipStream_t s);
+
+struct PermuteArgs {
+  bool bf16;
+  const void* x;
+  const int32_t* topk_idx;
+  int T, d, E, k, capacity;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* dest;
+  int32_t* src;
+  void* x_perm;
+  int32_t* blk_hist;       // [permute_blocks(T*k)][E]
+  int32_t* blk_base;       // [permute_blocks(T*k)][E]
+};
+int permute_blocks(int assignments);
+hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
+
+struct FfnArgs {
+  bool bf16;
+  bool up;                 // true: GELU(A W1^T + b1) -> dtype h; false: A W2^T + b2 -> fp32 o
+  const void* a;           // [rows][K] dtype
+  const int32_t* offsets;  // [E+1]
+  const void* w;           // [E][N][K] dtype
+  const void* bias;        // [E][N] dtype or null
+  void* out;               // [rows][N] dtype (up) or fp32 (down)
+  int E, N, K;
+  int max_rows_per_expert; // host bound on any expert's rows (no device sync)
+  int max_rows;            // host bound on the total rows R
+  int path;                // resolved MOE_FFN_TILED or MOE_FFN_STREAM
+  bool split;              // bf16 h kept as hi + lo planes (MOE_H_SPLIT)
+  size_t plane;            // elements per h plane (T*k*F) when split
+};
+hipError_t launch_ffn(const FfnArgs& a, hipStream_t s);
+
+struct CombineArgs {
+  const float* o;
+  const int32_t* dest;
+  const float* topk_w;
+  float* y;
+  int T, d, k;
+};
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+
+}  // namespace moe

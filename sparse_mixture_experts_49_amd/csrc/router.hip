@@ -1,0 +1,266 @@
+// Router of the MoE layer on gfx950: logits on MFMA, then softmax, top-k and the
+// routing weights in registers, plus the per-block partial sums of the aux loss.
+//
+// Web page "Mixture of Experts: Scaling Parameters Without Scaling Compute",
+// section "The MoE layer": logits g = W_r x, p = softmax(g), keep the top-k
+// experts, renormalise the chosen probabilities.  Section "The central
+// problem: load balancing": aux = E * sum_i f_i P_i with f_i the fraction of
+// tokens whose first choice is i and P_i the mean router probability.
+//
+// Ranking is by logit (softmax is monotone), descending; equal logits go to
+// the lower expert index, the order a stable descending sort gives.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace moe {
+
+constexpr int kRouterTokens = 16;   // tokens per block (one MFMA row tile)
+constexpr int kRouterWaves = 4;     // the block's waves split d between them
+
+// One block = 16 tokens x all experts.  Wave w accumulates the k-chunks
+// w, w+4, w+8, ... of the d-long dot products; the four partial logit tiles
+// are summed in wave order through LDS, so the result does not depend on
+// scheduling.
+//
+// Lane layout of the loads: lane l reads row (l % 16) -- a token of x, or an
+// expert row of W_r -- and 64 contiguous bytes starting at k-chunk offset
+// (l / 16) * 64 B, so each row's 256 B per chunk come from 4 lanes.  MFMA j of
+// the chunk consumes the lane's j-th 16-byte piece; A and B use the same map.
+template <typename T, int NT>
+__global__ __launch_bounds__(256) void router_kernel(
+    const T* __restrict__ x, const T* __restrict__ wr, const float* __restrict__ br,
+    int T_, int d, int E, int k, int renorm,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+    double* __restrict__ part_psum, int32_t* __restrict__ part_top1) {
+  constexpr int kPerLane = 64 / sizeof(T);          // elements per lane per chunk
+  constexpr int kChunk = 4 * kPerLane;              // 128 bf16 or 64 fp32
+  constexpr int kPerVec = 16 / sizeof(T);
+
+  __shared__ float red[kRouterWaves][kRouterTokens][65];
+  __shared__ float prob[kRouterTokens][64];
+  __shared__ int top1[kRouterTokens];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, c = lane >> 4;
+  const int t0 = blockIdx.x * kRouterTokens;
+  const T* xrow = x + (size_t)min(t0 + r, T_ - 1) * d + c * kPerLane;
+  const T* wrow[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) wrow[nt] = wr + (size_t)min(nt * 16 + r, E - 1) * d + c * kPerLane;
+
+  f32x4 acc[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nch = d / kChunk;
+  for (int ch = wave; ch < nch; ch += kRouterWaves) {
+    const int kk = ch * kChunk;
+    u32x4 a[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) a[q] = ld16(xrow + kk + q * kPerVec);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      u32x4 b[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) b[q] = ld16(wrow[nt] + kk + q * kPerVec);
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[nt] = mfma_bf16(a[q], b[q], acc[nt]);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            acc[nt] = mfma_f32(__uint_as_float(a[q][i]), __uint_as_float(b[q][i]), acc[nt]);
+      }
+    }
+  }
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[wave][4 * c + i][nt * 16 + r] = acc[nt][i];
+  __syncthreads();
+
+  if (wave == 0) {
+    // Four lanes per token: lane quarter q holds experts q, q+4, q+8, ...
+    const int tq = lane >> 2, q = lane & 3;
+    const int t = t0 + tq;
+    constexpr int kMaxPer = 16;
+    float g[kMaxPer], p[kMaxPer];
+    float m = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kMaxPer; ++j) {
+      const int e = q + 4 * j;
+      g[j] = -INFINITY;
+      if (e < E) {
+        g[j] = ((red[0][tq][e] + red[1][tq][e]) + red[2][tq][e]) + red[3][tq][e];
+        if (br) g[j] += br[e];
+        m = fmaxf(m, g[j]);
+      }
+    }
+    m = fmaxf(m, __shfl_xor(m, 1));
+    m = fmaxf(m, __shfl_xor(m, 2));
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < kMaxPer; ++j) {
+      p[j] = (q + 4 * j < E) ? expf(g[j] - m) : 0.f;
+      s += p[j];
+    }
+    s += __shfl_xor(s, 1);
+    s += __shfl_xor(s, 2);
+    const float inv = 1.0f / s;
+#pragma unroll
+    for (int j = 0; j < kMaxPer; ++j) p[j] *= inv;
+
+    // top-k: k rounds of a quad-wide argmax over the unselected logits.
+    uint32_t taken = 0;
+    int sel_e[8];
+    float sel_p[8];
+#pragma unroll
+    for (int sl = 0; sl < 8; ++sl) {
+      sel_e[sl] = 0;
+      sel_p[sl] = 0.f;
+      if (sl < k) {
+        float bv = -INFINITY, bp = 0.f;
+        int be = 0x7fffffff;
+#pragma unroll
+        for (int j = 0; j < kMaxPer; ++j) {
+          const int e = q + 4 * j;
+          if (e < E && !((taken >> j) & 1u) && (g[j] > bv || be == 0x7fffffff)) {
+            bv = g[j];
+            be = e;
+            bp = p[j];
+          }
+        }
+#pragma unroll
+        for (int off = 1; off <= 2; off <<= 1) {
+          const float ov = __shfl_xor(bv, off);
+          const int oe = __shfl_xor(be, off);
+          const float op = __shfl_xor(bp, off);
+          if (ov > bv || (ov == bv && oe < be)) {
+            bv = ov;
+            be = oe;
+            bp = op;
+          }
+        }
+        if ((be & 3) == q) taken |= 1u << (be >> 2);
+        sel_e[sl] = be;
+        sel_p[sl] = bp;
+      }
+    }
+    float wsum = 0.f;
+#pragma unroll
+    for (int sl = 0; sl < 8; ++sl)
+      if (sl < k) wsum += sel_p[sl];
+    const float winv = renorm ? 1.0f / wsum : 1.0f;
+    if (t < T_ && q == 0) {
+#pragma unroll
+      for (int sl = 0; sl < 8; ++sl) {
+        if (sl < k) {
+          topk_idx[(size_t)t * k + sl] = sel_e[sl];
+          topk_w[(size_t)t * k + sl] = renorm ? sel_p[sl] * winv : sel_p[sl];
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kMaxPer; ++j) {
+      const int e = q + 4 * j;
+      if (e < E) prob[tq][e] = (t < T_) ? p[j] : 0.f;
+    }
+    if (q == 0) top1[tq] = (t < T_) ? sel_e[0] : -1;
+  }
+  __syncthreads();
+
+  // Per-block partials of the aux loss, summed in token order.
+  if (threadIdx.x < E) {
+    const int e = threadIdx.x;
+    double ps = 0.0;
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < kRouterTokens; ++i) {
+      ps += (double)prob[i][e];
+      cnt += (top1[i] == e);
+    }
+    part_psum[(size_t)blockIdx.x * E + e] = ps;
+    part_top1[(size_t)blockIdx.x * E + e] = cnt;
+  }
+}
+
+// Fixed-order reduction of the router partials: f, P and aux.
+// 256 threads: thread (e = tid % 64, g = tid / 64) sums blocks g, g+4, ...;
+// the four group sums are then added in group order.
+__global__ __launch_bounds__(256) void aux_finalize_kernel(
+    const double* __restrict__ part_psum, const int32_t* __restrict__ part_top1, int nblk,
+    int T_, int E, int32_t* __restrict__ top1_count, float* __restrict__ prob_mean,
+    float* __restrict__ aux) {
+  __shared__ double ps[4][64];
+  __shared__ long long pc[4][64];
+  __shared__ double fP[64];
+  const int e = threadIdx.x & 63, g = threadIdx.x >> 6;
+  double s = 0.0;
+  long long cnt = 0;
+  if (e < E) {
+    for (int b = g; b < nblk; b += 4) {
+      s += part_psum[(size_t)b * E + e];
+      cnt += part_top1[(size_t)b * E + e];
+    }
+  }
+  ps[g][e] = s;
+  pc[g][e] = cnt;
+  __syncthreads();
+  if (g == 0) {
+    double S = 0.0;
+    long long C = 0;
+    if (e < E) {
+      S = ((ps[0][e] + ps[1][e]) + ps[2][e]) + ps[3][e];
+      C = pc[0][e] + pc[1][e] + pc[2][e] + pc[3][e];
+    }
+    const double P = S / (double)T_, f = (double)C / (double)T_;
+    fP[e] = (e < E) ? f * P : 0.0;
+    if (e < E) {
+      if (top1_count) top1_count[e] = (int32_t)C;
+      if (prob_mean) prob_mean[e] = (float)P;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0 && aux) {
+    double a = 0.0;
+    for (int i = 0; i < E; ++i) a += fP[i];
+    *aux = (float)((double)E * a);
+  }
+}
+
+template <typename T>
+static hipError_t launch_router_t(const RouterArgs& a, hipStream_t s) {
+  const int nblk = (a.T + kRouterTokens - 1) / kRouterTokens;
+  const int nt = (a.E + 15) / 16;
+  const T* x = static_cast<const T*>(a.x);
+  const T* wr = static_cast<const T*>(a.w_router);
+#define MOE_ROUTER_CASE(NT)                                                                   \
+  case NT:                                                                                  \
+    router_kernel<T, NT><<<nblk, 256, 0, s>>>(x, wr, a.b_router, a.T, a.d, a.E, a.k,       \
+                                               a.renorm, a.topk_idx, a.topk_w, a.part_psum, \
+                                               a.part_top1);                                \
+    break;
+  switch (nt) {
+    MOE_ROUTER_CASE(1)
+    MOE_ROUTER_CASE(2)
+    MOE_ROUTER_CASE(3)
+    MOE_ROUTER_CASE(4)
+    default: return hipErrorInvalidValue;
+  }
+#undef MOE_ROUTER_CASE
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  aux_finalize_kernel<<<1, 256, 0, s>>>(a.part_psum, a.part_top1, nblk, a.T, a.E, a.top1_count,
+                                        a.prob_mean, a.aux);
+  return hipGetLastError();
+}
+
+int router_blocks(int T) { return (T + kRouterTokens - 1) / kRouterTokens; }
+
+hipError_t launch_router(const RouterArgs& a, hipStream_t s) {
+  return a.bf16 ? launch_router_t<uint16_t>(a, s) : launch_router_t<float>(a, s);
+}
+
+}  // namespace moe

@@ -1,0 +1,153 @@
+"""The C-ABI library without a GPU: it loads, exports every entry point the header
+declares, sizes workspaces, and rejects bad arguments with the documented status
+before any HIP call."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_mixture_experts_49_amd as moe
+from sparse_mixture_experts_49_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_mi355x.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = moe.load_library()
+    declared = _declared()
+    assert set(declared) == set(B.ENTRY_POINTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_header_structs_match_binding():
+    text = open(HEADER).read()
+    for struct, cls in (("moe_desc", B.CDesc), ("moe_weights", B.CWeights),
+                        ("moe_routing", B.CRouting), ("moe_plan", B.CPlan)):
+        body = re.search(r"typedef struct %s \{(.*?)\} %s;" % (struct, struct), text, re.S).group(1)
+        body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+        fields = re.findall(r"\*?\s*(\w+)\s*;", body)
+        assert fields == [f for f, _ in cls._fields_], struct
+
+
+def test_status_strings():
+    lib = moe.load_library()
+    for st in (B.MOE_OK, B.MOE_ERR_INVALID, B.MOE_ERR_UNSUPPORTED, B.MOE_ERR_WORKSPACE, B.MOE_ERR_HIP):
+        assert lib.moe_status_string(st)
+
+
+def _ws(desc):
+    return moe.moe_workspace_size(desc)
+
+
+def test_workspace_size_grows_with_shape():
+    small = _ws(moe.Desc(64, 256, 1024, 8, 2, dtype="f32"))
+    big = _ws(moe.Desc(16384, 4096, 14336, 8, 2))
+    assert 0 < small < big
+    # x_perm + h + o dominate: T*k*(d*s + F*s + d*4)
+    assert big >= 16384 * 2 * (4096 * 2 + 14336 * 2 + 4096 * 4)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(tokens=0), B.MOE_ERR_INVALID),
+    (dict(n_experts=0), B.MOE_ERR_INVALID),
+    (dict(n_experts=65, top_k=2), B.MOE_ERR_UNSUPPORTED),
+    (dict(top_k=0), B.MOE_ERR_INVALID),
+    (dict(top_k=9, n_experts=16), B.MOE_ERR_UNSUPPORTED),
+    (dict(top_k=9, n_experts=8), B.MOE_ERR_INVALID),
+    (dict(d_model=200), B.MOE_ERR_UNSUPPORTED),
+    (dict(d_ff=100), B.MOE_ERR_UNSUPPORTED),
+    (dict(capacity=-1), B.MOE_ERR_INVALID),
+    (dict(capacity=10, top_k=2), B.MOE_ERR_INVALID),
+    (dict(ffn_path=3), B.MOE_ERR_INVALID),
+    (dict(ffn_path=B.MOE_FFN_TILED, dtype="f32"), B.MOE_ERR_UNSUPPORTED),
+    (dict(tokens=1 << 20, d_ff=4096), B.MOE_ERR_UNSUPPORTED),
+    (dict(h_mode=3), B.MOE_ERR_INVALID),
+    (dict(h_mode=B.MOE_H_SPLIT, dtype="f32"), B.MOE_ERR_INVALID),
+    (dict(h_mode=B.MOE_H_SPLIT, ffn_path=B.MOE_FFN_TILED), B.MOE_ERR_UNSUPPORTED),
+])
+def test_invalid_descriptors(kw, status):
+    base = dict(tokens=64, d_model=256, d_ff=512, n_experts=8, top_k=2)
+    base.update(kw)
+    with pytest.raises(moe.MoeError) as ei:
+        _ws(moe.Desc(**base))
+    assert ei.value.status == status
+
+
+def _call_route(desc, x=0x1000, wr=0x2000, idx=0x3000, w=0x4000, ws=0x100000, ws_bytes=None,
+                br=None):
+    lib = moe.load_library()
+    weights = B.CWeights(wr, br, None, None, None, None)
+    routing = B.CRouting(idx, w, None, None, None, None, None, None)
+    if ws_bytes is None:
+        ws_bytes = _ws(desc)
+    st = lib.moe_route(ctypes.byref(desc.to_c()), x, ctypes.byref(weights), ctypes.byref(routing),
+                       None, ws, ws_bytes, None)
+    return st, lib.moe_last_error().decode()
+
+
+def test_null_and_misaligned_pointers_rejected_before_launch():
+    d = moe.Desc(64, 256, 512, 8, 2)
+    assert _call_route(d, x=None)[0] == B.MOE_ERR_INVALID
+    assert _call_route(d, x=0x1008)[0] == B.MOE_ERR_INVALID
+    assert _call_route(d, wr=None)[0] == B.MOE_ERR_INVALID
+    assert _call_route(d, idx=None)[0] == B.MOE_ERR_INVALID
+    assert _call_route(d, br=0x5004)[0] == B.MOE_ERR_INVALID
+    st, msg = _call_route(d, ws=None)
+    assert st == B.MOE_ERR_WORKSPACE and "workspace" in msg
+    st, msg = _call_route(d, ws_bytes=_ws(d) - 1)
+    assert st == B.MOE_ERR_WORKSPACE and "needs" in msg
+    assert _call_route(d, ws=0x100010)[0] == B.MOE_ERR_WORKSPACE
+
+
+def test_expert_bias_flag_must_match_pointers():
+    lib = moe.load_library()
+    d = moe.Desc(64, 256, 512, 8, 2, has_expert_bias=False)
+    w = B.CWeights(0x1000, None, 0x2000, 0x3000, 0x4000, None)   # b1 given without the flag
+    st = lib.moe_ffn_up(ctypes.byref(d.to_c()), 0x5000, 0x6000, ctypes.byref(w), 0x7000,
+                        0x100000, _ws(d), None)
+    assert st == B.MOE_ERR_INVALID
+    d2 = moe.Desc(64, 256, 512, 8, 2, has_expert_bias=True)
+    w2 = B.CWeights(0x1000, None, 0x2000, None, 0x4000, None)   # flag set, b1 missing
+    st = lib.moe_ffn_down(ctypes.byref(d2.to_c()), 0x5000, 0x6000, ctypes.byref(w2), 0x7000,
+                          0x100000, _ws(d2), None)
+    assert st == B.MOE_ERR_INVALID
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(RuntimeError, match="missing"):
+        B._lib_backup = B._lib
+        try:
+            B._lib = None
+            B.load_library(str(tmp_path / "nope.so"))
+        finally:
+            B._lib = B._lib_backup
+
+
+def test_plan_resolution_of_the_named_workloads():
+    """AUTO: tiled kernel + bf16 h for prefill-sized layers, weight streaming + split h
+    for the rest; h_bytes follows the mode."""
+    import synth
+    want = {"toy_fp32": (B.MOE_FFN_STREAM, B.MOE_H_AUTO, 4),
+            "mid_bf16": (B.MOE_FFN_TILED, B.MOE_H_BF16, 2),
+            "mixtral_prefill_bf16": (B.MOE_FFN_TILED, B.MOE_H_BF16, 2),
+            "switch_capacity_bf16": (B.MOE_FFN_STREAM, B.MOE_H_SPLIT, 4),
+            "decode_bf16": (B.MOE_FFN_STREAM, B.MOE_H_SPLIT, 4)}
+    for name, (path, hm, eb) in want.items():
+        s = synth.WORKLOADS[name]
+        d = moe.Desc(s.tokens, s.d_model, s.d_ff, s.n_experts, s.top_k, s.renormalize,
+                     s.capacity, s.dtype, s.expert_bias)
+        p = moe.moe_query_plan(d)
+        assert (p["ffn_path"], p["h_mode"]) == (path, hm), name
+        assert p["h_bytes"] == s.tokens * s.top_k * s.d_ff * eb
+        assert p["workspace_bytes"] == moe.moe_workspace_size(d)
