@@ -47,8 +47,34 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
 }
 // Output layout of both: lane l holds column (l % 16), rows 4*(l/16) + i, i = 0..3.
 
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+// One 32x32 output tile, K = 16 (bf16) per instruction.  Operand lane layout:
+// lane l holds row/column (l % 32) and k-slots 8*(l/32)..+7.  Output: lane l,
+// register i holds row 8*(i/4) + 4*(l/32) + (i%4), column l % 32.  From a
+// single wave per SIMD this shape keeps the matrix pipe ~85% busy, the
+// 16x16x32 shape only ~53% (measured on MI355X), so the MFMA-bound kernel uses it.
+__device__ __forceinline__ f32x16 mfma32_bf16(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// GELU(z) = z * Phi(z) = (z / 2) * (1 + erf(z / sqrt 2)), with erf from
+// Abramowitz & Stegun, Handbook of Mathematical Functions, formula 7.1.26
+// (after Hastings): for a >= 0, erfc(a) ~= P(t) exp(-a^2) with t = 1/(1 + p a)
+// and P a fifth-degree polynomial without constant term; |error| <= 1.5e-7.
+// Using erfc directly for z < 0 (1 + erf(-a) = erfc(a)) avoids cancellation,
+// so GELU's absolute error stays below ~1e-7 |z|.
 __device__ __forceinline__ float gelu_erf(float z) {
-  return 0.5f * z * (1.0f + erff(z * 0.70710678118654752440f));
+  const float a = fabsf(z) * 0.70710678118654752440f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, a, 1.0f));
+  float poly = fmaf(1.061405429f, t, -1.453152027f);
+  poly = fmaf(poly, t, 1.421413741f);
+  poly = fmaf(poly, t, -0.284496736f);
+  poly = fmaf(poly, t, 0.254829592f);
+  poly *= t;
+  const float erfc_a = poly * __builtin_amdgcn_exp2f(-a * a * 1.44269504088896340736f);
+  const float one_plus_erf = z < 0.f ? erfc_a : 2.0f - erfc_a;
+  return 0.5f * z * one_plus_erf;
 }
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }

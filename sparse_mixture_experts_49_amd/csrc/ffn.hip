@@ -9,11 +9,11 @@
 //
 // Two kernels, chosen on the host from a bound on rows per expert (the
 // device-side counts are never read back):
-//   * ffn_tiled_kernel  -- many rows per expert (prefill): 128x128 output
-//     tiles, both operands staged through LDS in 64-wide k-steps, bf16 MFMA
-//     16x16x32 with fp32 accumulation, double-buffered with one barrier per
-//     k-step.  A 1-D grid walks (m-tile, n-tile) with the m-tiles of all
-//     experts laid end to end; each block finds its expert from `offsets`.
+//   * ffn_tiled_kernel  -- many rows per expert (prefill): 256 x 256 output
+//     tiles, both operands loaded straight into LDS in 64-wide k-steps, bf16
+//     MFMA 16x16x32 with fp32 accumulation, double-buffered with one barrier
+//     per k-step, XCD-aware tile order.  Each block finds its expert from
+//     `offsets`.
 //   * ffn_stream_kernel -- few rows per expert (decode, many small experts):
 //     each wave streams its own 16*NWN rows of W_e straight from HBM into
 //     registers in the MFMA operand layout, while the block's (at most
@@ -62,111 +62,279 @@ __device__ __forceinline__ void store_out(void* out, size_t idx, float v) {
 }
 
 // ---------------------------------------------------------------------------
-// LDS-tiled kernel (bf16): 128 x 128 x 64 block tile, 4 waves as 2 x 2, each
-// wave 64 x 64 = 4 x 4 MFMA tiles.
-// LDS tile layout: row-major, 128 B per row (64 bf16), the eight 16-byte chunks
-// of row r stored at chunk position (c ^ (r & 7)) so that both the row-wise
-// stores and the MFMA fragment reads (8 rows x same chunk) are bank-conflict
-// free.
+// LDS-tiled kernel (bf16).  Block tile 256 (rows of one expert) x BN (output
+// columns), k-steps of 64.  NW waves (4 or 8) as 2 x NW/2; each wave computes
+// 128 rows x BN/(NW/2) columns as 32x32 MFMA tiles (v_mfma_f32_32x32x16_bf16).
+// The MFMA computes the transposed tile (W rows as its first operand, A rows
+// as its second), so each lane holds four consecutive output columns of a row.
+// With 8 waves two share each SIMD: while one waits for a load or an LDS read,
+// the other keeps the matrix pipe busy.
+//
+// Memory pipeline.  Operands go from global memory straight into LDS
+// (global_load_lds, 16 B per lane, no register staging), two stages of one
+// k-step, one barrier per k-step placed mid-step: the loads of step k+2 are
+// issued right after it (interleaved with the MFMAs) and land during the next
+// step; each row contributes a whole 128 B line per k-step.
+//
+// LDS layout per stage: rows of 128 B (64 bf16); the eight 16 B chunks of row
+// r sit at chunk position (c ^ ((r >> 1) & 7)).  A load instruction writes 8
+// whole rows (1 KB); a fragment read (16 consecutive rows, same chunk) touches
+// all 64 banks exactly once, the rate at which the LDS serves 16-byte reads.
+//
+// Epilogue.  After the last k-step each wave stages its output sub-tile in
+// LDS (16 B chunks XOR-swizzled by row) and writes whole row segments.
+//
+// Tile order.  The m-tiles of all experts are laid end to end; tiles are
+// walked in bands of 4 m-tiles x all n-tiles, and the blocks of each XCD
+// (workgroups are dealt round-robin to the 8 XCDs) take one contiguous range
+// of that walk, so the tiles running together on an XCD share A and W rows in
+// its L2.
 // ---------------------------------------------------------------------------
-constexpr int kTBM = 128, kTBN = 128, kTBK = 64;
+constexpr int kTBM = 256, kTBK = 64, kBandM = 4, kXcds = 8;
+#ifndef MOE_TILED_WAVES
+#define MOE_TILED_WAVES 8
+#endif
 
-template <bool UP>
-__global__ __launch_bounds__(256, 2) void ffn_tiled_kernel(
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+__device__ __forceinline__ void load_lds16(const void* g, void* l) {
+  __builtin_amdgcn_global_load_lds((glb_void_t*)g, (lds_void_t*)l, 16, 0, 0);
+}
+
+// s_waitcnt immediate (gfx9 encoding) waiting for vmcnt <= vm, other counters untouched.
+constexpr int waitcnt_vm(int vm) { return (vm & 0xF) | ((vm >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+constexpr int kWaitLgkm0 = 0xC07F;   // lgkmcnt(0), others untouched
+
+template <bool UP, int BN, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void ffn_tiled_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets,
     const uint16_t* __restrict__ W, const uint16_t* __restrict__ bias, void* __restrict__ out,
-    int E, int N, int K, int max_mt) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][kTBM * 128];   // [stage][A|B]
+    int E, int N, int K) {
+  constexpr int kWavesN = NW / 2;
+  constexpr int kWN = BN / kWavesN;       // wave tile columns
+  constexpr int kNT = kWN / 32;           // 32-column subtiles per wave
+  constexpr int kMT = 4;                  // 32-row subtiles per wave (128 rows)
+  constexpr int kAStage = kTBM * 128;     // bytes per stage
+  constexpr int kBStage = BN * 128;
+  constexpr int kStage = kAStage + kBStage;
+  constexpr int kAInst = kTBM / 8 / NW;   // 1 KB load instructions per wave per stage
+  constexpr int kBInst = BN / 8 / NW;
+  constexpr int kLoads = kAInst + kBInst;
+  static_assert(kNT >= 1 && kAInst >= 1 && kBInst >= 1, "tile shape");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kStage];
 
-  const int L = blockIdx.x;
-  const int mt = L % max_mt, nt = L / max_mt;
+  // ---- which tile ----
+  int total_mt = 0;
+  for (int e = 0; e < E; ++e) total_mt += (offsets[e + 1] - offsets[e] + kTBM - 1) / kTBM;
+  const int ntn = N / BN;
+  const int total = total_mt * ntn;
+  const int per_xcd = (total + kXcds - 1) / kXcds;
+  const int j = blockIdx.x / kXcds;
+  if (j >= per_xcd) return;
+  const int L = (blockIdx.x % kXcds) * per_xcd + j;
+  if (L >= total) return;
+  const int band = L / (kBandM * ntn);
+  const int rem = L - band * kBandM * ntn;
+  const int band_m = min(kBandM, total_mt - band * kBandM);
+  const int nt = rem / band_m;
+  const int mt = band * kBandM + rem % band_m;
   int e, r0, r1;
   if (!find_mtile(offsets, E, kTBM, mt, e, r0, r1)) return;
-  const int n0 = nt * kTBN;
+  const int n0 = nt * BN;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int fr = lane & 15, fc = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS targets in SGPRs
+  const int wm = wave / kWavesN, wn = wave % kWavesN;
+  const int fr = lane & 31, fc = lane >> 5;
 
-  // Global -> LDS mapping: thread loads rows (tid/8) + 32*i, chunk tid%8.
-  const int lrow = tid >> 3, lch = tid & 7;
-  const uint16_t* a_src[4];
-  const uint16_t* b_src[4];
-  int st_off[4];
+  // Load plan: instruction i of wave w fills LDS rows (i*NW + w)*8 + lane/8,
+  // physical chunk lane%8, i.e. logical chunk (lane%8) ^ ((row >> 1) & 7).
+  const uint16_t* a_src[kAInst];
+  const uint16_t* b_src[kBInst];
   const uint16_t* Wexp = W + (size_t)e * N * K;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = lrow + 32 * i;
-    a_src[i] = A + (size_t)min(r0 + row, r1 - 1) * K + lch * 8;
-    b_src[i] = Wexp + (size_t)(n0 + row) * K + lch * 8;
-    st_off[i] = row * 128 + ((lch ^ (row & 7)) << 4);
+  for (int i = 0; i < kAInst; ++i) {
+    const int row = (i * NW + wave) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ ((row >> 1) & 7);
+    a_src[i] = A + (size_t)min(r0 + row, r1 - 1) * K + c * 8;
   }
-
-  f32x4 acc[4][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  u32x4 ra[4], rb[4];
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ra[i] = ld16(a_src[i] + k0);
-      rb[i] = ld16(b_src[i] + k0);
-    }
-  };
-  auto lstore = [&](int stage) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      st16(&lds[stage][0][st_off[i]], ra[i]);
-      st16(&lds[stage][1][st_off[i]], rb[i]);
-    }
-  };
-
+  for (int i = 0; i < kBInst; ++i) {
+    const int row = (i * NW + wave) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ ((row >> 1) & 7);
+    b_src[i] = Wexp + (size_t)(n0 + row) * K + c * 8;
+  }
   const int nk = K / kTBK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * kTBK);
+  auto issue = [&](int stage, int step) {
+    uint8_t* base = lds + stage * kStage;
+    const int k0 = step * kTBK;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      u32x4 af[4], bfr[4];
+    for (int i = 0; i < kAInst; ++i) load_lds16(a_src[i] + k0, base + (i * NW + wave) * 1024);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = wm * 64 + i * 16 + fr;
-        af[i] = ld16(&lds[cur][0][row * 128 + ((((ks << 2) | fc) ^ (row & 7)) << 4)]);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int row = wn * 64 + j * 16 + fr;
-        bfr[j] = ld16(&lds[cur][1][row * 128 + ((((ks << 2) | fc) ^ (row & 7)) << 4)]);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_bf16(af[i], bfr[j], acc[i][j]);
-    }
-    if (kt + 1 < nk) lstore(cur ^ 1);
-    __syncthreads();
-  }
+    for (int i = 0; i < kBInst; ++i) load_lds16(b_src[i] + k0, base + kAStage + (i * NW + wave) * 1024);
+  };
 
-  // Epilogue: lane holds column fr of each 16x16 tile, rows 4*fc + v.
-  const uint16_t* bexp = bias ? bias + (size_t)e * N : nullptr;
+  f32x16 acc[kNT][kMT];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int col = n0 + wn * 64 + j * 16 + fr;
-    const float bv = bexp ? bf16_to_f32(bexp[col]) : 0.f;
+  for (int jn = 0; jn < kNT; ++jn)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int im = 0; im < kMT; ++im)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int row = r0 + wm * 64 + i * 16 + 4 * fc + v;
-        if (row < r1) store_out<uint16_t, UP>(out, (size_t)row * N + col, acc[i][j][v] + bv);
+      for (int q = 0; q < 16; ++q) acc[jn][im][q] = 0.f;
+
+  // A k-step of 64 is four 16-wide MFMA slices; a half step is two slices.
+  // X holds half 0 of a step, Y half 1.
+  u32x4 xa[2][kMT], xb[2][kNT], ya[2][kMT], yb[2][kNT];
+  auto read_frags = [&](u32x4 (&fa)[2][kMT], u32x4 (&fb)[2][kNT], int stage, int half) {
+    const uint8_t* As = lds + stage * kStage;
+    const uint8_t* Bs = As + kAStage;
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl) {
+      const int ch = (half * 2 + sl) * 2 + fc;     // 16 B chunk: 8 k of this slice
+#pragma unroll
+      for (int im = 0; im < kMT; ++im) {
+        const int row = wm * 128 + im * 32 + fr;
+        fa[sl][im] = ld16(As + row * 128 + ((ch ^ ((row >> 1) & 7)) << 4));
+      }
+#pragma unroll
+      for (int jn = 0; jn < kNT; ++jn) {
+        const int row = wn * kWN + jn * 32 + fr;
+        fb[sl][jn] = ld16(Bs + row * 128 + ((ch ^ ((row >> 1) & 7)) << 4));
       }
     }
+  };
+  auto mfmas = [&](const u32x4 (&fa)[2][kMT], const u32x4 (&fb)[2][kNT]) {
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+      for (int jn = 0; jn < kNT; ++jn)
+#pragma unroll
+        for (int im = 0; im < kMT; ++im) acc[jn][im] = mfma32_bf16(fb[sl][jn], fa[sl][im], acc[jn][im]);
+  };
+  // One LDS read (and in the second half one global->LDS load) between every
+  // few MFMAs, so the wave never issues a run of memory instructions while the
+  // matrix pipe idles.
+  constexpr int kReads = 2 * (kMT + kNT);
+  constexpr int kMfmas = 2 * kMT * kNT;
+  constexpr int kPerRead = kMfmas / kReads;
+  constexpr int kRest = kMfmas - kPerRead * kReads;
+  static_assert(kPerRead >= 1, "at least one MFMA per fragment read");
+  static_assert(kLoads <= kReads, "one load per fragment read at most");
+  auto interleave = [&](bool with_loads) {
+#pragma unroll
+    for (int r = 0; r < kReads; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                               // DS read
+      if (with_loads && r < kLoads) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM
+      __builtin_amdgcn_sched_group_barrier(0x008, kPerRead, 0);                        // MFMA
+    }
+    if constexpr (kRest > 0) __builtin_amdgcn_sched_group_barrier(0x008, kRest, 0);
+  };
+
+  // Pipeline (two LDS stages, step t in stage t & 1):
+  //   X <- half 0 of step t is in registers when step t starts;
+  //   read Y <- half 1 of step t while the X MFMAs run;
+  //   wait for our LDS reads and for step t+1's loads, barrier;
+  //   issue step t+2's loads into stage t & 1 (every wave is done reading it);
+  //   read X <- half 0 of step t+1 while the Y MFMAs run.
+  // In the last iteration there is no step t+2: the final step is reloaded into
+  // the free stage (never read again), which keeps the loop body branch-free.
+  issue(0, 0);
+  if (nk > 1) {
+    issue(1, 1);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(kLoads));
+  } else {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  }
+  __syncthreads();
+  read_frags(xa, xb, 0, 0);
+  for (int kt = 0; kt < nk - 1; ++kt) {
+    const int cur = kt & 1;
+    read_frags(ya, yb, cur, 1);
+    mfmas(xa, xb);
+    interleave(false);
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    __syncthreads();
+    issue(cur, min(kt + 2, nk - 1));
+    read_frags(xa, xb, cur ^ 1, 0);
+    mfmas(ya, yb);
+    interleave(true);
+  }
+  read_frags(ya, yb, (nk - 1) & 1, 1);
+  mfmas(xa, xb);
+  interleave(false);
+  mfmas(ya, yb);
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  __syncthreads();                                   // LDS free for the epilogue
+
+  // Epilogue through LDS.  Lane (fr, fc) holds, for each 32x32 subtile (jn, im)
+  // and g = 0..3, row im*32 + fr and columns jn*32 + 8g + 4fc .. +3 of the
+  // wave's sub-tile.  Each wave stages rows in its own LDS region with 16 B
+  // chunks XOR-swizzled by row, then stores whole row segments.
+  const uint16_t* bexp = bias ? bias + (size_t)e * N : nullptr;
+  auto bias4 = [&](int jn, int g, float (&bv)[4]) {
+    const int col = n0 + wn * kWN + jn * 32 + 8 * g + 4 * fc;
+    if (bexp) {
+      const uint2 braw = *reinterpret_cast<const uint2*>(bexp + col);
+      bv[0] = __uint_as_float(braw.x << 16);
+      bv[1] = __uint_as_float(braw.x & 0xffff0000u);
+      bv[2] = __uint_as_float(braw.y << 16);
+      bv[3] = __uint_as_float(braw.y & 0xffff0000u);
+    } else {
+      bv[0] = bv[1] = bv[2] = bv[3] = 0.f;
+    }
+  };
+  // Rows staged per pass so that NW regions fit in the 2-stage LDS area.
+  constexpr int kElem = UP ? 2 : 4;
+  constexpr int kRowB = kWN * kElem, kChunks = kRowB / 16;
+  constexpr int kPassRows = (2 * kStage / NW) / kRowB >= 128 ? 128 : 64;
+  constexpr int kPasses = 128 / kPassRows;
+  constexpr int kRowsPerInst = 64 / kChunks;
+  uint8_t* my = lds + wave * (kPassRows * kRowB);
+#pragma unroll
+  for (int pass = 0; pass < kPasses; ++pass) {
+#pragma unroll
+    for (int jn = 0; jn < kNT; ++jn)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float bv[4];
+        bias4(jn, g, bv);
+#pragma unroll
+        for (int imp = 0; imp < kPassRows / 32; ++imp) {
+          const int im = pass * (kPassRows / 32) + imp;
+          const int row = imp * 32 + fr;           // row within this pass
+          if constexpr (UP) {
+            const int chunk = jn * 4 + g;           // 16 B = 8 columns; fc picks the half
+            uint32_t p[2];
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+              const uint32_t lo = f32_to_bf16(gelu_erf(acc[jn][im][4 * g + 2 * h2] + bv[2 * h2]));
+              const uint32_t hi = f32_to_bf16(gelu_erf(acc[jn][im][4 * g + 2 * h2 + 1] + bv[2 * h2 + 1]));
+              p[h2] = lo | (hi << 16);
+            }
+            *reinterpret_cast<uint2*>(my + row * kRowB + ((chunk ^ (row & (kChunks - 1))) << 4) + fc * 8) =
+                make_uint2(p[0], p[1]);
+          } else {
+            const int chunk = jn * 8 + 2 * g + fc;  // 16 B = 4 columns
+            f32x4 v;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[q] = acc[jn][im][4 * g + q] + bv[q];
+            *reinterpret_cast<f32x4*>(my + row * kRowB + ((chunk ^ (row & (kChunks - 1))) << 4)) = v;
+          }
+        }
+      }
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);          // our own LDS writes are done
+#pragma unroll 4
+    for (int rb = 0; rb < kPassRows; rb += kRowsPerInst) {
+      const int row = rb + lane / kChunks, chunk = lane % kChunks;
+      const int grow = r0 + wm * 128 + pass * kPassRows + row;
+      const u32x4 v = ld16(my + row * kRowB + ((chunk ^ (row & (kChunks - 1))) << 4));
+      if (grow < r1) {
+        uint8_t* dst = static_cast<uint8_t*>(out) + ((size_t)grow * N + n0 + wn * kWN) * kElem + chunk * 16;
+        st16(dst, v);
+      }
+    }
+    if (kPasses > 1) __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // reads done before the next pass
   }
 }
 
@@ -373,15 +541,22 @@ static void launch_stream(const FfnArgs& a, hipStream_t s) {
 
 hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
   if (a.path == MOE_FFN_TILED) {
+    // Upper bound on tiles: sum_e ceil(count_e/256) <= ceil(R/256) + E; the grid
+    // is a multiple of the XCD count and blocks past the real tile count exit.
     const int max_mt = (a.max_rows + kTBM - 1) / kTBM + a.E;
-    const int grid = max_mt * (a.N / kTBN);
     const uint16_t* A = static_cast<const uint16_t*>(a.a);
     const uint16_t* W = static_cast<const uint16_t*>(a.w);
     const uint16_t* B = static_cast<const uint16_t*>(a.bias);
-    if (a.up)
-      ffn_tiled_kernel<true><<<grid, 256, 0, s>>>(A, a.offsets, W, B, a.out, a.E, a.N, a.K, max_mt);
-    else
-      ffn_tiled_kernel<false><<<grid, 256, 0, s>>>(A, a.offsets, W, B, a.out, a.E, a.N, a.K, max_mt);
+    constexpr int NW = MOE_TILED_WAVES;
+    if (a.N % 256 == 0) {
+      const int grid = ((max_mt * (a.N / 256) + kXcds - 1) / kXcds) * kXcds;
+      if (a.up) ffn_tiled_kernel<true, 256, NW><<<grid, NW * 64, 0, s>>>(A, a.offsets, W, B, a.out, a.E, a.N, a.K);
+      else ffn_tiled_kernel<false, 256, NW><<<grid, NW * 64, 0, s>>>(A, a.offsets, W, B, a.out, a.E, a.N, a.K);
+    } else {
+      const int grid = ((max_mt * (a.N / 128) + kXcds - 1) / kXcds) * kXcds;
+      if (a.up) ffn_tiled_kernel<true, 128, 4><<<grid, 256, 0, s>>>(A, a.offsets, W, B, a.out, a.E, a.N, a.K);
+      else ffn_tiled_kernel<false, 128, 4><<<grid, 256, 0, s>>>(A, a.offsets, W, B, a.out, a.E, a.N, a.K);
+    }
   } else if (a.bf16) {
     if (a.split) {
       if (a.up) launch_stream<uint16_t, true, true>(a, s);

@@ -258,3 +258,25 @@ def test_forward_full_size(name):
         tokens = _sample_tokens(spec, O.route(inp, O.desc_of(spec)))
     err = _check_forward(spec, inp, y, aux, r, tokens)
     print(f"{name}: max|err|/RMS = {err:.3e}")
+
+
+def test_gelu_accuracy_through_first_product():
+    """GELU of the first product's epilogue against math.erf: an fp32 layer with one
+    expert, W1 = identity and no bias, so h = GELU(x) exactly; x spans [-8, 8]."""
+    import math
+    d = F = 128
+    T = 4096
+    z = np.linspace(-8.0, 8.0, T * d).astype(np.float32).reshape(T, d)
+    ref = np.array([0.5 * v * (1.0 + math.erf(v / math.sqrt(2.0))) for v in z.astype(np.float64).ravel()])
+    ref = ref.reshape(T, d)
+    desc = moe.Desc(T, d, F, 1, 1, dtype="f32", has_expert_bias=False)
+    w = moe.Weights(w_router=G.to_dev(np.zeros((1, d), np.float32)),
+                    w1=G.to_dev(np.eye(F, d, dtype=np.float32)[None]),
+                    w2=G.to_dev(np.zeros((1, d, F), np.float32)))
+    offsets = torch.tensor([0, T], dtype=torch.int32, device=G.DEV)
+    h = moe.alloc_h(desc, G.DEV)
+    moe.moe_ffn_up(desc, G.to_dev(z), offsets, w, h)
+    torch.cuda.synchronize()
+    got = h.cpu().numpy().astype(np.float64)
+    # erf to 1.5e-7 (Abramowitz & Stegun 7.1.26) plus fp32 rounding of z/sqrt2 and the products
+    assert np.all(np.abs(got - ref) <= 2e-7 * np.abs(z) + 2e-7 * np.abs(ref) + 1e-12)
