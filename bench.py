@@ -6,12 +6,25 @@ One step = one moe_forward (route -> permute -> grouped FFN -> combine) over one
 batch of synthetic tokens already resident in HBM.  Prints ONE JSON line with
 tokens/s, the roofline of the dominant kernel (timed live with HIP events on
 the stream it runs on) and the fp64 CPU oracle timed on a bounded sample.
+
+    python bench.py --summarize --stats-csv KS.csv --fetch-csv F.csv --write-csv W.csv \
+        --workload NAME --copy-probe-mib N --command "..."
+
+reduces rocprofv3 output (kernel_stats.csv of a --kernel-trace --stats run and
+counter_collection.csv of a FETCH_SIZE run and of a WRITE_SIZE run, all written
+with --output-format csv) to the markdown summary kept beside the results.  The
+counter runs pass --copy-probe-mib so that one plain copy of known size is
+measured by the same counters; its reading scales them to bytes.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -24,6 +37,34 @@ PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3      # MI355X fp32 matrix
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 METRIC = "MoE layer tokens/sec + % of bf16 MFMA peak (prefill) / % HBM BW (decode)"
+COPY_KERNEL_TAG = "neg_kernel"   # torch.neg: reads N bytes, writes N bytes
+
+
+def sources_sha256() -> str:
+    """Hash of the library's sources: a traffic figure measured on other sources is stale."""
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(ROOT, "sparse_mixture_experts_49_amd", "csrc", "*")))
+    files.append(os.path.join(ROOT, "include", "moe_mi355x.h"))
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(entry: str, workload: str):
+    """HBM bytes per launch of `entry` on `workload` from the committed counter summaries,
+    or None if there is none for the current sources."""
+    sha = sources_sha256()
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        for line in open(path):
+            m = re.match(r"<!-- traffic (\{.*\}) -->", line.strip())
+            if not m:
+                continue
+            rec = json.loads(m.group(1))
+            if rec["entry"] == entry and rec["workload"] == workload and rec["sources_sha256"] == sha:
+                return rec["bytes_per_launch"]
+    return None
 
 
 def _to_dev(a, dev):
@@ -35,9 +76,12 @@ def _to_dev(a, dev):
     return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
 
-def _time_events(fn, reps):
-    """Average duration (ms) of fn() over reps launches, HIP events on the current stream."""
+def _time_events(fn, reps, warmup=2):
+    """Average duration (ms) of fn() over reps launches, HIP events on the current stream
+    (the stream the library launches on)."""
     import torch
+    for _ in range(warmup):
+        fn()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
@@ -64,21 +108,19 @@ def cpu_baseline(spec, inp, sample_tokens):
                       f"the sampled tokens), fp64 NumPy/BLAS, {dt:.1f} s"}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="mixtral_prefill_bf16")
-    ap.add_argument("--kernel-reps", type=int, default=10)
-    ap.add_argument("--cpu-sample", type=int, default=256)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the layer is built for a single MI355X; see the sharding notes)", file=sys.stderr)
-        sys.exit(2)
+def kernel_bytes(spec, R, active, h_elem):
+    """Algorithmic HBM bytes of one launch of each expert kernel: the weights (and biases)
+    of the experts that received rows, read once, plus the activations each reads and
+    writes once at their stored widths (o is fp32)."""
+    s = 2 if spec.dtype == "bf16" else 4
+    d, F = spec.d_model, spec.d_ff
+    bias = 1 if spec.expert_bias else 0
+    up = active * (F * d + bias * F) * s + R * d * s + R * F * h_elem
+    down = active * (d * F + bias * d) * s + R * F * h_elem + R * d * 4
+    return up, down
 
+
+def run(args):
     import torch
     import sparse_mixture_experts_49_amd as moe
     import synth
@@ -111,7 +153,7 @@ def main():
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
 
-    # Stage buffers for timing the expert kernels alone (same launch configuration).
+    # The expert kernels alone, same launch configuration as inside moe_forward.
     Tk = spec.tokens * spec.top_k
     el = torch.bfloat16 if spec.dtype == "bf16" else torch.float32
     x_perm = torch.empty(Tk, spec.d_model, dtype=el, device=dev)
@@ -121,30 +163,40 @@ def main():
     moe.moe_permute(desc, x, routing, x_perm, ws)
     torch.cuda.synchronize()
     R = int(routing.offsets[-1].item())
+    active = int((routing.counts > 0).sum().item())
     up_ms = _time_events(lambda: moe.moe_ffn_up(desc, x_perm, routing.offsets, w, h, ws), args.kernel_reps)
     down_ms = _time_events(lambda: moe.moe_ffn_down(desc, h, routing.offsets, w, o, ws), args.kernel_reps)
 
-    flops_up = 2.0 * R * spec.d_ff * spec.d_model
-    flops_down = 2.0 * R * spec.d_model * spec.d_ff
-    ffn_flops = flops_up + flops_down
-    s = 2 if spec.dtype == "bf16" else 4
-    weight_bytes = 2.0 * spec.n_experts * spec.d_ff * spec.d_model * s
-    mean_rows = R / spec.n_experts
+    if args.copy_probe_mib:
+        # One plain copy of known size for scaling the HBM byte counters (see the module doc).
+        n = args.copy_probe_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
+    plan = moe.moe_query_plan(desc)
+    h_elem = h.element_size() * (2 if h.dim() == 3 else 1)
     bf16 = spec.dtype == "bf16"
-    hbm_bound = 2.0 * mean_rows * spec.d_model * spec.d_ff * 2 / (spec.d_model * spec.d_ff * s) < \
-        (PEAK_BF16_TFLOPS if bf16 else PEAK_FP32_TFLOPS) * 1e12 / (PEAK_HBM_GBS * 1e9)
-    dom_name, dom_ms, dom_flops = ("moe_ffn_up", up_ms, flops_up) if up_ms >= down_ms else \
-        ("moe_ffn_down", down_ms, flops_down)
-    if hbm_bound:
-        per_kernel_bytes = weight_bytes / 2 + R * (spec.d_model + spec.d_ff) * s
-        achieved = per_kernel_bytes / (dom_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None, "kernel": dom_name}
+    flops_one = 2.0 * R * spec.d_ff * spec.d_model          # each of the two products
+    up_bytes, down_bytes = kernel_bytes(spec, R, active, h_elem)
+    peak_flops = PEAK_BF16_TFLOPS if bf16 else PEAK_FP32_TFLOPS
+    # The FFN is MFMA-bound when its arithmetic intensity exceeds the ridge point.
+    mfma_bound = 2 * flops_one / (up_bytes + down_bytes) > peak_flops * 1e12 / (PEAK_HBM_GBS * 1e9)
+    dom, dom_ms, dom_bytes = ("moe_ffn_up", up_ms, up_bytes) if up_ms >= down_ms else \
+        ("moe_ffn_down", down_ms, down_bytes)
+    traffic = recorded_traffic(dom, spec.name)
+    if mfma_bound:
+        achieved = flops_one / (dom_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak_flops, "unit": "TFLOP/s",
+                "frac": round(achieved / peak_flops, 4)}
     else:
-        achieved = dom_flops / (dom_ms * 1e-3) / 1e12
-        peak = PEAK_BF16_TFLOPS if bf16 else PEAK_FP32_TFLOPS
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4), "traffic": None, "kernel": dom_name}
+        achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    roof.update({"traffic": traffic, "kernel": dom, "kernel_ms": round(dom_ms, 4),
+                 "algorithmic_bytes": dom_bytes, "algorithmic_flops": flops_one})
 
     out = {
         "metric": METRIC,
@@ -161,17 +213,139 @@ def main():
         "data": "synthetic",
         "config": {"workload": spec.name, "tokens": spec.tokens, "d_model": spec.d_model,
                    "d_ff": spec.d_ff, "n_experts": spec.n_experts, "top_k": spec.top_k,
-                   "capacity": spec.capacity, "kept_rows": R},
+                   "capacity": spec.capacity, "kept_rows": R, "active_experts": active,
+                   "ffn_path": {1: "tiled", 2: "stream"}[plan["ffn_path"]],
+                   "h_mode": {0: "f32", 1: "bf16", 2: "split"}[plan["h_mode"]]},
         "roofline": roof,
-        "layer": {"ffn_tflops": round(ffn_flops / (ms * 1e-3) / 1e12, 1),
-                  "ffn_up_ms": round(up_ms, 4), "ffn_down_ms": round(down_ms, 4),
-                  "ffn_frac_bf16_peak": round(ffn_flops / ((up_ms + down_ms) * 1e-3) / 1e12 /
-                                              PEAK_BF16_TFLOPS, 4) if bf16 else None,
-                  "weight_stream_gbs": round(weight_bytes / ((up_ms + down_ms) * 1e-3) / 1e9, 1)},
+        "layer": {"ffn_up_ms": round(up_ms, 4), "ffn_down_ms": round(down_ms, 4),
+                  "ffn_tflops": round(2 * flops_one / ((up_ms + down_ms) * 1e-3) / 1e12, 1),
+                  "ffn_frac_peak": round(2 * flops_one / ((up_ms + down_ms) * 1e-3) / 1e12 / peak_flops, 4),
+                  "ffn_gbs": round((up_bytes + down_bytes) / ((up_ms + down_ms) * 1e-3) / 1e9, 1),
+                  "step_gbs_weights_and_io": round(
+                      (up_bytes + down_bytes) / (ms * 1e-3) / 1e9, 1)},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(spec, inp, args.cpu_sample)
     print(json.dumps(out), flush=True)
+
+
+# ----------------------------------------------------------------------------------------
+# rocprofv3 output -> markdown summary
+
+def _rows(path):
+    with open(path, newline="") as fh:
+        return list(csv.DictReader(fh))
+
+
+def _entry_of(kernel_name: str):
+    """Entry point that launches a HIP kernel of this library (by kernel name)."""
+    m = re.search(r"moe::(\w+)<(.*)>\(", kernel_name) or re.search(r"moe::(\w+)\(", kernel_name)
+    if not m:
+        return None
+    base = m.group(1)
+    if base.startswith("ffn_"):
+        up = re.search(r"\b(true|false)\b", m.group(2)).group(1) == "true"
+        return "moe_ffn_up" if up else "moe_ffn_down"
+    if base.startswith(("router", "aux")):
+        return "moe_route"
+    if base.startswith("perm"):
+        return "moe_permute"
+    if base.startswith("combine"):
+        return "moe_combine"
+    return None
+
+
+def _short(name: str, n=90):
+    name = re.sub(r"\(.*", "", name)
+    return name if len(name) <= n else name[:n - 3] + "..."
+
+
+def _counter_avgs(path, counter):
+    """Per kernel name: average over dispatches of the counter summed over its instances."""
+    per = {}
+    for r in _rows(path):
+        if r["Counter_Name"] != counter:
+            continue
+        key = r["Kernel_Name"]
+        d = per.setdefault(key, {})
+        d[r["Dispatch_Id"]] = d.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    return {k: (sum(v.values()) / len(v), len(v)) for k, v in per.items()}
+
+
+def summarize(args):
+    lines = [f"# rocprofv3 summary: {args.workload}", ""]
+    if args.command:
+        lines += ["Commands (run from the repository root):", "", "```"] + args.command + ["```", ""]
+    if args.stats_csv:
+        lines += ["## Kernel durations (`--kernel-trace --stats`)", "",
+                  "| kernel | entry point | calls | avg us | min us | max us | share |",
+                  "|---|---|---|---|---|---|---|"]
+        for r in _rows(args.stats_csv):
+            e = _entry_of(r["Name"]) or "-"
+            lines.append(f"| `{_short(r['Name'])}` | {e} | {r['Calls']} | "
+                         f"{float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
+                         f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
+        lines.append("")
+    if args.fetch_csv and args.write_csv:
+        fetch = _counter_avgs(args.fetch_csv, "FETCH_SIZE")
+        write = _counter_avgs(args.write_csv, "WRITE_SIZE")
+        copy_kib = args.copy_probe_mib * 1024.0
+        cf = [v for k, v in fetch.items() if COPY_KERNEL_TAG in k]
+        cw = [v for k, v in write.items() if COPY_KERNEL_TAG in k]
+        if not cf or not cw:
+            raise SystemExit("the copy probe kernel is missing from the counter runs")
+        sf, sw = copy_kib / cf[0][0], copy_kib / cw[0][0]
+        lines += ["## HBM traffic (`--pmc FETCH_SIZE`, then `--pmc WRITE_SIZE`)", "",
+                  f"Scale: a plain copy of {args.copy_probe_mib} MiB (`torch.neg`, reads and writes "
+                  f"{copy_kib:.0f} KiB) reads FETCH_SIZE {cf[0][0]:.0f} KiB and WRITE_SIZE "
+                  f"{cw[0][0]:.0f} KiB, so FETCH_SIZE x {sf:.4f} and WRITE_SIZE x {sw:.4f} give bytes "
+                  "moved to and from memory.", "",
+                  "| kernel | entry point | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | "
+                  "scaled bytes per launch |", "|---|---|---|---|---|---|"]
+        recs = {}
+        for k, (fv, n) in sorted(fetch.items()):
+            e = _entry_of(k)
+            if e is None:
+                continue
+            wv = write.get(k, (0.0, 0))[0]
+            b = (fv * sf + wv * sw) * 1024.0
+            lines.append(f"| `{_short(k)}` | {e} | {n} | {fv:.0f} | {wv:.0f} | {b:.4g} |")
+            if e in ("moe_ffn_up", "moe_ffn_down"):
+                recs[e] = b
+        lines.append("")
+        sha = sources_sha256()
+        for e, b in sorted(recs.items()):
+            lines.append("<!-- traffic " + json.dumps(
+                {"entry": e, "workload": args.workload, "bytes_per_launch": round(b),
+                 "sources_sha256": sha}) + " -->")
+    print("\n".join(lines))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="mixtral_prefill_bf16")
+    ap.add_argument("--kernel-reps", type=int, default=20)
+    ap.add_argument("--cpu-sample", type=int, default=8192)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0)
+    ap.add_argument("--summarize", action="store_true")
+    ap.add_argument("--stats-csv")
+    ap.add_argument("--fetch-csv")
+    ap.add_argument("--write-csv")
+    ap.add_argument("--command", action="append")
+    args = ap.parse_args()
+    if args.summarize:
+        summarize(args)
+        return
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer is built and measured on a single MI355X; sharding across GPUs "
+              "is a design note, not code)", file=sys.stderr)
+        sys.exit(2)
+    run(args)
 
 
 if __name__ == "__main__":

@@ -237,7 +237,7 @@ def test_module_style_forward():
     assert abs(aux.item() - ref["aux"]) <= G.TOL_AUX * ref["aux"]
 
 
-def _sample_tokens(spec, ref_route, n=48, seed=1):
+def _sample_tokens(spec, ref_route, n=256, seed=1):
     rng = np.random.default_rng(seed)
     T = spec.tokens
     pick = set(rng.choice(T, size=min(n, T), replace=False).tolist()) | {0, T - 1}
