@@ -60,21 +60,33 @@ __device__ __forceinline__ f32x16 mfma32_bf16(u32x4 a, u32x4 b, f32x16 c) {
 
 // GELU(z) = z * Phi(z) = (z / 2) * (1 + erf(z / sqrt 2)), with erf from
 // Abramowitz & Stegun, Handbook of Mathematical Functions, formula 7.1.26
-// (after Hastings): for a >= 0, erfc(a) ~= P(t) exp(-a^2) with t = 1/(1 + p a)
-// and P a fifth-degree polynomial without constant term; |error| <= 1.5e-7.
-// Using erfc directly for z < 0 (1 + erf(-a) = erfc(a)) avoids cancellation,
-// so GELU's absolute error stays below ~1e-7 |z|.
+// (after Hastings): for a >= 0, erfc(a) ~= t P(t) exp(-a^2) with t = 1/(1 + p a)
+// and P a fourth-degree polynomial; |error| <= 1.5e-7.  With a = |z| / sqrt 2
+// and m = (z / 2) erfc(a):  GELU(z) = z - m for z >= 0 and m for z < 0
+// (1 + erf(-a) = erfc(a)), so there is no cancellation and GELU's absolute
+// error stays below ~1e-7 |z|.  The 1/sqrt 2 is folded into p, the 1/2 into
+// P's coefficients, and exp(-a^2) = exp2(-z^2 log2(e) / 2).
 __device__ __forceinline__ float gelu_erf(float z) {
-  const float a = fabsf(z) * 0.70710678118654752440f;
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, a, 1.0f));
-  float poly = fmaf(1.061405429f, t, -1.453152027f);
-  poly = fmaf(poly, t, 1.421413741f);
-  poly = fmaf(poly, t, -0.284496736f);
-  poly = fmaf(poly, t, 0.254829592f);
-  poly *= t;
-  const float erfc_a = poly * __builtin_amdgcn_exp2f(-a * a * 1.44269504088896340736f);
-  const float one_plus_erf = z < 0.f ? erfc_a : 2.0f - erfc_a;
-  return 0.5f * z * one_plus_erf;
+  constexpr float kP = 0.3275911f * 0.70710678118654752440f;
+  constexpr float c1 = 0.5f * 0.254829592f, c2 = 0.5f * -0.284496736f, c3 = 0.5f * 1.421413741f,
+                  c4 = 0.5f * -1.453152027f, c5 = 0.5f * 1.061405429f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(kP, fabsf(z), 1.0f));
+  float q = fmaf(c5, t, c4);
+  q = fmaf(q, t, c3);
+  q = fmaf(q, t, c2);
+  q = fmaf(q, t, c1);
+  q *= t;
+  const float e = __builtin_amdgcn_exp2f(z * z * -0.72134752044448170368f);
+  const float m = z * (q * e);
+  return z < 0.f ? m : z - m;
+}
+
+// Two fp32 values rounded to bf16 (nearest, ties to even) and packed, lo in
+// bits 0..15: one v_cvt_pk_bf16_f32 on gfx950.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }

@@ -21,6 +21,8 @@
 //     the four waves.  Weight bytes are read once.
 // The first product applies bias + exact-erf GELU in its epilogue and stores
 // dtype h; the second adds its bias and stores fp32 o.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 #include "../../include/moe_mi355x.h"
@@ -63,18 +65,21 @@ __device__ __forceinline__ void store_out(void* out, size_t idx, float v) {
 
 // ---------------------------------------------------------------------------
 // LDS-tiled kernel (bf16).  Block tile 256 (rows of one expert) x BN (output
-// columns), k-steps of 64.  NW waves (4 or 8) as 2 x NW/2; each wave computes
-// 128 rows x BN/(NW/2) columns as 32x32 MFMA tiles (v_mfma_f32_32x32x16_bf16).
-// The MFMA computes the transposed tile (W rows as its first operand, A rows
-// as its second), so each lane holds four consecutive output columns of a row.
-// With 8 waves two share each SIMD: while one waits for a load or an LDS read,
-// the other keeps the matrix pipe busy.
+// columns), k-steps of 64.  NW = 4 waves, one per SIMD, as 2 x 2; each wave
+// computes 128 rows x BN/2 columns as 32x32 MFMA tiles
+// (v_mfma_f32_32x32x16_bf16, 256 fp32 accumulators per lane in AGPRs).  The
+// MFMA computes the transposed tile (W rows as its first operand, A rows as
+// its second), so each lane holds four consecutive output columns of a row.
+// One wave per SIMD keeps the matrix pipe to itself: measured on MI355X, two
+// waves per SIMD lose more to arbitration and barrier skew than they hide.
 //
 // Memory pipeline.  Operands go from global memory straight into LDS
-// (global_load_lds, 16 B per lane, no register staging), two stages of one
-// k-step, one barrier per k-step placed mid-step: the loads of step k+2 are
-// issued right after it (interleaved with the MFMAs) and land during the next
-// step; each row contributes a whole 128 B line per k-step.
+// (global_load_lds_dwordx4, 16 B per lane, no register staging); A has two
+// LDS stages, W three, one barrier per k-step.  A wave waiting to issue a
+// load cannot issue MFMAs, so each half k-step interleaves its MFMAs, the
+// LDS reads of the next half's fragments and its share of the loads in a
+// fixed order (see half_step).  Each row contributes a whole 128 B line per
+// k-step.
 //
 // LDS layout per stage: rows of 128 B (64 bf16); the eight 16 B chunks of row
 // r sit at chunk position (c ^ ((r >> 1) & 7)).  A load instruction writes 8
@@ -91,20 +96,27 @@ __device__ __forceinline__ void store_out(void* out, size_t idx, float v) {
 // its L2.
 // ---------------------------------------------------------------------------
 constexpr int kTBM = 256, kTBK = 64, kBandM = 4, kXcds = 8;
-#ifndef MOE_TILED_WAVES
-#define MOE_TILED_WAVES 8
-#endif
+
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
 
-__device__ __forceinline__ void load_lds16(const void* g, void* l) {
-  __builtin_amdgcn_global_load_lds((glb_void_t*)g, (lds_void_t*)l, 16, 0, 0);
+// The same load, written so that the compiler does not see an LDS write: it
+// then adds no waits of its own for it (it cannot tell the stages apart and
+// would wait for every load before each LDS read).  The caller waits with
+// explicit s_waitcnt vmcnt before any LDS read of the loaded data.  The load
+// has no register result; M0 (the LDS destination of the wave, uniform) is set
+// in the same statement.
+__device__ __forceinline__ void load_lds16_raw(const void* g, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(g), "s"(lds_addr) : "memory", "m0");
 }
 
 // s_waitcnt immediate (gfx9 encoding) waiting for vmcnt <= vm, other counters untouched.
 constexpr int waitcnt_vm(int vm) { return (vm & 0xF) | ((vm >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 constexpr int kWaitLgkm0 = 0xC07F;   // lgkmcnt(0), others untouched
+// vmcnt <= vm and lgkmcnt(0).
+constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 0xF) | ((vm >> 4) << 14) | (0x7 << 4); }
 
 template <bool UP, int BN, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void ffn_tiled_kernel(
@@ -117,12 +129,13 @@ __global__ __launch_bounds__(NW * 64, 1) void ffn_tiled_kernel(
   constexpr int kMT = 4;                  // 32-row subtiles per wave (128 rows)
   constexpr int kAStage = kTBM * 128;     // bytes per stage
   constexpr int kBStage = BN * 128;
-  constexpr int kStage = kAStage + kBStage;
+  constexpr int kBBase = 2 * kAStage;     // A: 2 stages, then W: 3 stages
+  constexpr int kLds = kBBase + 3 * kBStage;
   constexpr int kAInst = kTBM / 8 / NW;   // 1 KB load instructions per wave per stage
   constexpr int kBInst = BN / 8 / NW;
-  constexpr int kLoads = kAInst + kBInst;
   static_assert(kNT >= 1 && kAInst >= 1 && kBInst >= 1, "tile shape");
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kStage];
+  static_assert(kLds <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kLds];
 
   // ---- which tile ----
   int total_mt = 0;
@@ -166,13 +179,20 @@ __global__ __launch_bounds__(NW * 64, 1) void ffn_tiled_kernel(
     b_src[i] = Wexp + (size_t)(n0 + row) * K + c * 8;
   }
   const int nk = K / kTBK;
-  auto issue = [&](int stage, int step) {
-    uint8_t* base = lds + stage * kStage;
-    const int k0 = step * kTBK;
+  // Steps past the last are clamped to it: those loads refill a free stage and
+  // are never read, which keeps the loop body branch-free.
+  const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
+  auto issue_a = [&](int stage, int step) {
+    const uint32_t base = lds0 + stage * kAStage;
+    const int k0 = min(step, nk - 1) * kTBK;
 #pragma unroll
-    for (int i = 0; i < kAInst; ++i) load_lds16(a_src[i] + k0, base + (i * NW + wave) * 1024);
+    for (int i = 0; i < kAInst; ++i) load_lds16_raw(a_src[i] + k0, base + (i * NW + wave) * 1024);
+  };
+  auto issue_b = [&](int stage, int step) {
+    const uint32_t base = lds0 + kBBase + stage * kBStage;
+    const int k0 = min(step, nk - 1) * kTBK;
 #pragma unroll
-    for (int i = 0; i < kBInst; ++i) load_lds16(b_src[i] + k0, base + kAStage + (i * NW + wave) * 1024);
+    for (int i = 0; i < kBInst; ++i) load_lds16_raw(b_src[i] + k0, base + (i * NW + wave) * 1024);
   };
 
   f32x16 acc[kNT][kMT];
@@ -184,86 +204,94 @@ __global__ __launch_bounds__(NW * 64, 1) void ffn_tiled_kernel(
       for (int q = 0; q < 16; ++q) acc[jn][im][q] = 0.f;
 
   // A k-step of 64 is four 16-wide MFMA slices; a half step is two slices.
-  // X holds half 0 of a step, Y half 1.
-  u32x4 xa[2][kMT], xb[2][kNT], ya[2][kMT], yb[2][kNT];
-  auto read_frags = [&](u32x4 (&fa)[2][kMT], u32x4 (&fb)[2][kNT], int stage, int half) {
-    const uint8_t* As = lds + stage * kStage;
-    const uint8_t* Bs = As + kAStage;
-#pragma unroll
-    for (int sl = 0; sl < 2; ++sl) {
-      const int ch = (half * 2 + sl) * 2 + fc;     // 16 B chunk: 8 k of this slice
-#pragma unroll
-      for (int im = 0; im < kMT; ++im) {
-        const int row = wm * 128 + im * 32 + fr;
-        fa[sl][im] = ld16(As + row * 128 + ((ch ^ ((row >> 1) & 7)) << 4));
-      }
-#pragma unroll
-      for (int jn = 0; jn < kNT; ++jn) {
-        const int row = wn * kWN + jn * 32 + fr;
-        fb[sl][jn] = ld16(Bs + row * 128 + ((ch ^ ((row >> 1) & 7)) << 4));
-      }
-    }
-  };
-  auto mfmas = [&](const u32x4 (&fa)[2][kMT], const u32x4 (&fb)[2][kNT]) {
-#pragma unroll
-    for (int sl = 0; sl < 2; ++sl)
-#pragma unroll
-      for (int jn = 0; jn < kNT; ++jn)
-#pragma unroll
-        for (int im = 0; im < kMT; ++im) acc[jn][im] = mfma32_bf16(fb[sl][jn], fa[sl][im], acc[jn][im]);
-  };
-  // One LDS read (and in the second half one global->LDS load) between every
-  // few MFMAs, so the wave never issues a run of memory instructions while the
-  // matrix pipe idles.
+  // X holds half 0 of a step, Y half 1.  Fragment r of a half (r < kReads) is
+  // slice r / (kMT + kNT) of A subtile q (q < kMT) or of W subtile q - kMT.
   constexpr int kReads = 2 * (kMT + kNT);
   constexpr int kMfmas = 2 * kMT * kNT;
-  constexpr int kPerRead = kMfmas / kReads;
-  constexpr int kRest = kMfmas - kPerRead * kReads;
-  static_assert(kPerRead >= 1, "at least one MFMA per fragment read");
-  static_assert(kLoads <= kReads, "one load per fragment read at most");
-  auto interleave = [&](bool with_loads) {
-#pragma unroll
-    for (int r = 0; r < kReads; ++r) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                               // DS read
-      if (with_loads && r < kLoads) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM
-      __builtin_amdgcn_sched_group_barrier(0x008, kPerRead, 0);                        // MFMA
+  static_assert(kReads % 2 == 0 && kReads / 2 <= kMfmas, "two reads per MFMA");
+  static_assert(kAInst <= kMfmas && kBInst <= kMfmas, "at most one load per MFMA");
+  u32x4 xa[2][kMT], xb[2][kNT], ya[2][kMT], yb[2][kNT];
+  auto read_at = [&](u32x4 (&fa)[2][kMT], u32x4 (&fb)[2][kNT], int sa_, int sb_, int half, int r) {
+    const int sl = r / (kMT + kNT), q = r % (kMT + kNT);
+    const int ch = (half * 2 + sl) * 2 + fc;     // 16 B chunk: 8 k of this slice
+    if (q < kMT) {
+      const int row = wm * 128 + q * 32 + fr;
+      fa[sl][q] = ld16(lds + sa_ * kAStage + row * 128 + ((ch ^ ((row >> 1) & 7)) << 4));
+    } else {
+      const int row = wn * kWN + (q - kMT) * 32 + fr;
+      fb[sl][q - kMT] = ld16(lds + kBBase + sb_ * kBStage + row * 128 + ((ch ^ ((row >> 1) & 7)) << 4));
     }
-    if constexpr (kRest > 0) __builtin_amdgcn_sched_group_barrier(0x008, kRest, 0);
   };
+  auto read_all = [&](u32x4 (&fa)[2][kMT], u32x4 (&fb)[2][kNT], int sa_, int sb_, int half) {
+#pragma unroll
+    for (int r = 0; r < kReads; ++r) read_at(fa, fb, sa_, sb_, half, r);
+  };
+  // MFMA m of a half: slice m / (kNT kMT), W subtile (m / kMT) % kNT, A subtile m % kMT.
+  auto mfma_at = [&](const u32x4 (&fa)[2][kMT], const u32x4 (&fb)[2][kNT], int m) {
+    const int sl = m / (kNT * kMT), jn = (m / kMT) % kNT, im = m % kMT;
+    acc[jn][im] = mfma32_bf16(fb[sl][jn], fa[sl][im], acc[jn][im]);
+  };
+  // One half step in a fixed instruction order: after each MFMA (whose
+  // operands were read in the previous half), up to two LDS reads of the next
+  // half's fragments, front-loaded so they return long before they are needed,
+  // and, evenly spread, this half's L global->LDS loads.  A wave waiting to
+  // issue a load cannot issue MFMAs, so loads are paced rather than burst.
+  auto half_step = [&](const u32x4 (&fa)[2][kMT], const u32x4 (&fb)[2][kNT], u32x4 (&na)[2][kMT],
+                       u32x4 (&nb)[2][kNT], int nsa, int nsb, int nhalf, auto load_fn, auto loads_tag) {
+    constexpr int L = decltype(loads_tag)::value;
+#pragma unroll
+    for (int m = 0; m < kMfmas; ++m) {
+      mfma_at(fa, fb, m);
+      if (2 * m < kReads) {
+        read_at(na, nb, nsa, nsb, nhalf, 2 * m);
+        read_at(na, nb, nsa, nsb, nhalf, 2 * m + 1);
+      }
+      if ((m + 1) * L / kMfmas > m * L / kMfmas) load_fn(m * L / kMfmas);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  using LoadsA = std::integral_constant<int, kAInst>;
+  using LoadsB = std::integral_constant<int, kBInst>;
+  using NoLoads = std::integral_constant<int, 0>;
 
-  // Pipeline (two LDS stages, step t in stage t & 1):
+  // Pipeline.  Step t's A tile sits in A stage t % 2, its W tile in W stage
+  // t % 3.  Per step t:
   //   X <- half 0 of step t is in registers when step t starts;
-  //   read Y <- half 1 of step t while the X MFMAs run;
-  //   wait for our LDS reads and for step t+1's loads, barrier;
-  //   issue step t+2's loads into stage t & 1 (every wave is done reading it);
-  //   read X <- half 0 of step t+1 while the Y MFMAs run.
-  // In the last iteration there is no step t+2: the final step is reloaded into
-  // the free stage (never read again), which keeps the loop body branch-free.
-  issue(0, 0);
-  if (nk > 1) {
-    issue(1, 1);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(kLoads));
-  } else {
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-  }
+  //   first half: X MFMAs, reads of Y <- half 1 of step t, and the loads of W
+  //     for step t+2 into W stage (t+2) % 3, which nobody reads any more (it
+  //     held step t-1, finished before the previous barrier);
+  //   wait for our LDS reads and for A and W of step t+1 (W of step t+2, issued
+  //     after them, may still be in flight), barrier;
+  //   second half: Y MFMAs, reads of X <- half 0 of step t+1, and the loads of
+  //     A for step t+2 into A stage t % 2 (every wave is done reading it).
+  // Loads complete in issue order, so "at most kBInst outstanding" means
+  // everything but the last W group has landed.
+  issue_a(0, 0);
+  issue_b(0, 0);
+  issue_a(1, 1);
+  issue_b(1, 1);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(kAInst + kBInst));
   __syncthreads();
-  read_frags(xa, xb, 0, 0);
+  read_all(xa, xb, 0, 0, 0);
+  int sa = 0, sb = 0;                                // stages of step kt
   for (int kt = 0; kt < nk - 1; ++kt) {
-    const int cur = kt & 1;
-    read_frags(ya, yb, cur, 1);
-    mfmas(xa, xb);
-    interleave(false);
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    const int sa1 = sa ^ 1, sb1 = sb == 2 ? 0 : sb + 1, sb2 = sb1 == 2 ? 0 : sb1 + 1;
+    const int kb = min(kt + 2, nk - 1) * kTBK;
+    half_step(xa, xb, ya, yb, sa, sb, 1,
+              [&](int i) { load_lds16_raw(b_src[i] + kb, lds0 + kBBase + sb2 * kBStage + (i * NW + wave) * 1024); },
+              LoadsB{});
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kBInst));
     __syncthreads();
-    issue(cur, min(kt + 2, nk - 1));
-    read_frags(xa, xb, cur ^ 1, 0);
-    mfmas(ya, yb);
-    interleave(true);
+    half_step(ya, yb, xa, xb, sa1, sb1, 0,
+              [&](int i) { load_lds16_raw(a_src[i] + kb, lds0 + sa * kAStage + (i * NW + wave) * 1024); },
+              LoadsA{});
+    sa = sa1;
+    sb = sb1;
   }
-  read_frags(ya, yb, (nk - 1) & 1, 1);
-  mfmas(xa, xb);
-  interleave(false);
-  mfmas(ya, yb);
+  half_step(xa, xb, ya, yb, sa, sb, 1, [&](int) {}, NoLoads{});
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+#pragma unroll
+  for (int m = 0; m < kMfmas; ++m) mfma_at(ya, yb, m);
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
   __syncthreads();                                   // LDS free for the epilogue
 
@@ -287,7 +315,7 @@ __global__ __launch_bounds__(NW * 64, 1) void ffn_tiled_kernel(
   // Rows staged per pass so that NW regions fit in the 2-stage LDS area.
   constexpr int kElem = UP ? 2 : 4;
   constexpr int kRowB = kWN * kElem, kChunks = kRowB / 16;
-  constexpr int kPassRows = (2 * kStage / NW) / kRowB >= 128 ? 128 : 64;
+  constexpr int kPassRows = (kLds / NW) / kRowB >= 128 ? 128 : 64;
   constexpr int kPasses = 128 / kPassRows;
   constexpr int kRowsPerInst = 64 / kChunks;
   uint8_t* my = lds + wave * (kPassRows * kRowB);
@@ -307,11 +335,9 @@ __global__ __launch_bounds__(NW * 64, 1) void ffn_tiled_kernel(
             const int chunk = jn * 4 + g;           // 16 B = 8 columns; fc picks the half
             uint32_t p[2];
 #pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
-              const uint32_t lo = f32_to_bf16(gelu_erf(acc[jn][im][4 * g + 2 * h2] + bv[2 * h2]));
-              const uint32_t hi = f32_to_bf16(gelu_erf(acc[jn][im][4 * g + 2 * h2 + 1] + bv[2 * h2 + 1]));
-              p[h2] = lo | (hi << 16);
-            }
+            for (int h2 = 0; h2 < 2; ++h2)
+              p[h2] = pack_bf16x2(gelu_erf(acc[jn][im][4 * g + 2 * h2] + bv[2 * h2]),
+                                  gelu_erf(acc[jn][im][4 * g + 2 * h2 + 1] + bv[2 * h2 + 1]));
             *reinterpret_cast<uint2*>(my + row * kRowB + ((chunk ^ (row & (kChunks - 1))) << 4) + fc * 8) =
                 make_uint2(p[0], p[1]);
           } else {
@@ -547,7 +573,7 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
     const uint16_t* A = static_cast<const uint16_t*>(a.a);
     const uint16_t* W = static_cast<const uint16_t*>(a.w);
     const uint16_t* B = static_cast<const uint16_t*>(a.bias);
-    constexpr int NW = MOE_TILED_WAVES;
+    constexpr int NW = 4;
     if (a.N % 256 == 0) {
       const int grid = ((max_mt * (a.N / 256) + kXcds - 1) / kXcds) * kXcds;
       if (a.up) ffn_tiled_kernel<true, 256, NW><<<grid, NW * 64, 0, s>>>(A, a.offsets, W, B, a.out, a.E, a.N, a.K);
