@@ -89,11 +89,8 @@ __device__ __forceinline__ void store_out(void* out, size_t idx, float v) {
 // Epilogue.  After the last k-step each wave stages its output sub-tile in
 // LDS (16 B chunks XOR-swizzled by row) and writes whole row segments.
 //
-// Tile order.  The m-tiles of all experts are laid end to end; tiles are
-// walked in bands of 4 m-tiles x all n-tiles, and the blocks of each XCD
-// (workgroups are dealt round-robin to the 8 XCDs) take one contiguous range
-// of that walk, so the tiles running together on an XCD share A and W rows in
-// its L2.
+// Tile order.  The m-tiles of all experts are laid end to end; see the
+// mapping at the top of the kernel.
 // ---------------------------------------------------------------------------
 constexpr int kTBM = 256, kTBK = 64, kBandM = 4, kXcds = 8;
 
@@ -141,17 +138,30 @@ __global__ __launch_bounds__(NW * 64, 1) void ffn_tiled_kernel(
   int total_mt = 0;
   for (int e = 0; e < E; ++e) total_mt += (offsets[e + 1] - offsets[e] + kTBM - 1) / kTBM;
   const int ntn = N / BN;
-  const int total = total_mt * ntn;
-  const int per_xcd = (total + kXcds - 1) / kXcds;
-  const int j = blockIdx.x / kXcds;
-  if (j >= per_xcd) return;
-  const int L = (blockIdx.x % kXcds) * per_xcd + j;
-  if (L >= total) return;
-  const int band = L / (kBandM * ntn);
-  const int rem = L - band * kBandM * ntn;
-  const int band_m = min(kBandM, total_mt - band * kBandM);
-  const int nt = rem / band_m;
-  const int mt = band * kBandM + rem % band_m;
+  // Block b runs on XCD x = b % 8 (workgroups are dealt round-robin) and takes
+  // entry i = b / 8 of that XCD's list.  m-tiles come in groups of 32; in
+  // group g, XCD x owns m-tiles 32g + 4x .. +3 and walks them n-tile by
+  // n-tile (4 m-tiles fastest).  The 32 blocks an XCD runs at once thus cover
+  // 4 m-tiles x 8 n-tiles (their A and W rows shared in its L2), and all XCDs
+  // sweep the same n-tiles at the same time, so each W slice is fetched from
+  // HBM once and served to the other XCDs from the last-level cache.  The
+  // m-tiles past the last full group are dealt round-robin over the XCDs.
+  constexpr int kGroupM = kXcds * kBandM;
+  const int x = blockIdx.x % kXcds, i = blockIdx.x / kXcds;
+  const int G = total_mt / kGroupM;
+  const int full = G * kBandM * ntn;                 // entries from full groups, per XCD
+  int mt, nt;
+  if (i < full) {
+    const int g = i / (kBandM * ntn), rem = i - g * kBandM * ntn;
+    nt = rem / kBandM;
+    mt = g * kGroupM + x * kBandM + rem % kBandM;
+  } else {
+    const int lm = total_mt - G * kGroupM;           // leftover m-tiles (< 32)
+    const int u = (i - full) * kXcds + x;
+    if (u >= lm * ntn) return;
+    nt = u / lm;
+    mt = G * kGroupM + u % lm;
+  }
   int e, r0, r1;
   if (!find_mtile(offsets, E, kTBM, mt, e, r0, r1)) return;
   const int n0 = nt * BN;
@@ -575,11 +585,11 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
     const uint16_t* B = static_cast<const uint16_t*>(a.bias);
     constexpr int NW = 4;
     if (a.N % 256 == 0) {
-      const int grid = ((max_mt * (a.N / 256) + kXcds - 1) / kXcds) * kXcds;
+      const int grid = ((max_mt * (a.N / 256) + kXcds - 1) / kXcds + 1) * kXcds;
       if (a.up) ffn_tiled_kernel<true, 256, NW><<<grid, NW * 64, 0, s>>>(A, a.offsets, W, B, a.out, a.E, a.N, a.K);
       else ffn_tiled_kernel<false, 256, NW><<<grid, NW * 64, 0, s>>>(A, a.offsets, W, B, a.out, a.E, a.N, a.K);
     } else {
-      const int grid = ((max_mt * (a.N / 128) + kXcds - 1) / kXcds) * kXcds;
+      const int grid = ((max_mt * (a.N / 128) + kXcds - 1) / kXcds + 1) * kXcds;
       if (a.up) ffn_tiled_kernel<true, 128, 4><<<grid, 256, 0, s>>>(A, a.offsets, W, B, a.out, a.E, a.N, a.K);
       else ffn_tiled_kernel<false, 128, 4><<<grid, 256, 0, s>>>(A, a.offsets, W, B, a.out, a.E, a.N, a.K);
     }
