@@ -378,16 +378,21 @@ __global__ __launch_bounds__(NW * 64, 1) void ffn_tiled_kernel(
 // Weight-streaming kernel.  Block = 4 waves; wave w owns the 16*NWN output
 // columns n0 + w*16*NWN + [0, 16*NWN); the block owns rows
 // [offsets[e] + g*16*NMT, ...) of expert e = blockIdx.y, g = blockIdx.z.
-// Per k-chunk:
-//   - the block stages its A rows into LDS (16 B per thread per m-tile); each
-//     row's chunk is 256 B (two 128 B planes when the second product reads a
-//     split h = hi + lo), its 16 B pieces stored at (piece ^ (row & mask)) so
-//     the fragment reads (16 rows x same piece) are conflict free;
-//   - each wave loads its W rows for the next chunk into registers: lane l
-//     reads row (l % 16) of its n-tile and KQ consecutive 16 B pieces starting
-//     at piece (l / 16) * KQ;
-//   - MFMA q of the chunk uses the lane's q-th piece of A (and of A's low
-//     term when h is split) and of W.
+// The k range is cut into chunks; each chunk of a row is 256 B of A (two 128 B
+// planes when the second product reads a split h = hi + lo).
+//   - W goes straight into registers: lane l reads row (l % 16) of its n-tile
+//     and pieces 4q + l / 16, q < KQ, so one load instruction reads 64
+//     contiguous bytes of each of 16 rows (measured on MI355X: ~6% more HBM
+//     bandwidth than KQ adjacent pieces per lane).  A ring of kDepth register
+//     buffers keeps kDepth - 1 chunks of W loading while one is consumed.
+//   - A goes global -> LDS by DMA (global_load_lds_dwordx4, 1 KB per wave
+//     instruction) into a ring of kDepth LDS stages, kDepth - 1 chunks ahead,
+//     so neither operand's load latency sits on the per-chunk path; one
+//     barrier per chunk publishes a stage and frees the one consumed before.
+//     Pieces of a row sit at (piece ^ swz(row)) so the fragment reads (16
+//     rows, same piece) are conflict free.
+//   - MFMA q of the chunk uses the lane's piece 4q + l / 16 of A (and of A's
+//     low term when h is split) and of W.
 // m-tiles past the block's last row issue no MFMA, so padding costs nothing.
 // ---------------------------------------------------------------------------
 template <typename T, bool UP, bool SPLIT, int NMT, int NWN>
@@ -400,10 +405,16 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(
   constexpr int kPerVec = 16 / sizeof(T);
   constexpr int kChunk = 4 * kQ * kPerVec;         // 128 bf16, 64 (split) or 64 fp32
   constexpr int kPieces = 4 * kQ;                  // pieces per row per plane
-  constexpr int kRowBytes = kPieces * 16;
+  constexpr int kRowBytes = kPieces * 16;          // 256 B, or 128 B per plane
   constexpr int kMR = 16 * NMT;
   constexpr int kPlaneBytes = kMR * kRowBytes;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][kMR * 256];
+  constexpr int kStageBytes = kMR * 256;           // all planes of one chunk
+  constexpr int kDepth = NMT <= 4 ? 4 : 2;
+  constexpr int kAInst = NMT;                      // 1 KB DMA instructions per wave per chunk
+  constexpr int kWInst = NWN * kQ;                 // W load instructions per wave per chunk
+  static_assert(kStageBytes == 4 * 1024 * kAInst && kPlaneBytes % 1024 == 0, "DMA plan");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kDepth * kStageBytes];
+  auto swz = [](int row) { return kPieces == 16 ? (row & 15) : ((row >> 1) & 7); };
 
   const int e = blockIdx.y;
   const int seg0 = offsets[e], seg1 = offsets[e + 1];
@@ -412,30 +423,30 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(
   const int r1 = min(seg1, r0 + kMR);
   const int mt_active = (r1 - r0 + 15) >> 4;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int fr = lane & 15, fc = lane >> 4;
   const int n0 = blockIdx.x * (64 * NWN) + wave * 16 * NWN;
 
-  // A staging: vector v = tid + 256*i covers row v/16 and 16 B piece v%16
-  // (plane (v%16)/8 when A is split).
-  const T* a_src[NMT];
-  int a_st[NMT];
-  bool a_on[NMT];
+  // DMA plan: instruction i of wave w fills bytes [g*1KB, (g+1)*1KB) of a
+  // stage, g = 4i + w: plane g*1KB / kPlaneBytes, rows from there on; lane L
+  // writes physical piece L % kPieces of its row, i.e. logical piece
+  // (L % kPieces) ^ swz(row).  Rows past the block's last are clamped (their
+  // data is never used).
+  const T* a_src[kAInst];
 #pragma unroll
-  for (int i = 0; i < NMT; ++i) {
-    const int v = tid + 256 * i;
-    const int row = v >> 4, within = v & 15;
-    const int plane = kTwoA ? (within >> 3) : 0;
-    const int pc = kTwoA ? (within & 7) : within;
+  for (int i = 0; i < kAInst; ++i) {
+    const int byte = (i * 4 + wave) * 1024 + lane * 16;
+    const int plane = byte / kPlaneBytes;
+    const int row = (byte % kPlaneBytes) / kRowBytes;
+    const int logical = ((byte % kRowBytes) / 16) ^ swz(row);
     const T* base = (kTwoA && plane) ? A_lo : A;
-    a_src[i] = base + (size_t)min(r0 + row, r1 - 1) * K + pc * kPerVec;
-    a_st[i] = plane * kPlaneBytes + row * kRowBytes + ((pc ^ (row & (kPieces - 1))) << 4);
-    a_on[i] = (row >> 4) < mt_active;
+    a_src[i] = base + (size_t)min(r0 + row, r1 - 1) * K + logical * kPerVec;
   }
   const T* w_src[NWN];
   const T* Wexp = W + (size_t)e * N * K;
 #pragma unroll
-  for (int j = 0; j < NWN; ++j) w_src[j] = Wexp + (size_t)(n0 + j * 16 + fr) * K + fc * kQ * kPerVec;
+  for (int j = 0; j < NWN; ++j) w_src[j] = Wexp + (size_t)(n0 + j * 16 + fr) * K + fc * kPerVec;
 
   f32x4 acc[NMT][NWN];
 #pragma unroll
@@ -443,37 +454,22 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(
 #pragma unroll
     for (int j = 0; j < NWN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 ra[NMT];
-  u32x4 wcur[NWN][kQ], wnext[NWN][kQ];
-  auto aload = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < NMT; ++i)
-      if (a_on[i]) ra[i] = ld16(a_src[i] + k0);
-  };
-  auto astore = [&](int stage) {
-#pragma unroll
-    for (int i = 0; i < NMT; ++i)
-      if (a_on[i]) st16(&lds[stage][a_st[i]], ra[i]);
-  };
-  auto wload = [&](u32x4 (&dst)[NWN][kQ], int k0) {
+  const int nch = K / kChunk;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
+  u32x4 wbuf[kDepth][NWN][kQ];
+  // Issue chunk ch: W into register slot `slot`, A into LDS stage `slot`.
+  auto issue = [&](u32x4 (&wdst)[NWN][kQ], int slot, int ch) {
+    const int k0 = ch * kChunk;
 #pragma unroll
     for (int j = 0; j < NWN; ++j)
 #pragma unroll
-      for (int q = 0; q < kQ; ++q) dst[j][q] = ld16(w_src[j] + k0 + q * kPerVec);
+      for (int q = 0; q < kQ; ++q) wdst[j][q] = ld16(w_src[j] + k0 + q * 4 * kPerVec);
+#pragma unroll
+    for (int i = 0; i < kAInst; ++i)
+      load_lds16_raw(a_src[i] + k0, lds0 + slot * kStageBytes + (i * 4 + wave) * 1024);
   };
-
-  const int nch = K / kChunk;
-  aload(0);
-  wload(wcur, 0);
-  astore(0);
-  __syncthreads();
-  for (int ch = 0; ch < nch; ++ch) {
-    const int cur = ch & 1;
-    const bool more = ch + 1 < nch;
-    if (more) {
-      aload((ch + 1) * kChunk);
-      wload(wnext, (ch + 1) * kChunk);
-    }
+  auto compute = [&](const u32x4 (&wc)[NWN][kQ], int slot) {
+    const uint8_t* st = lds + slot * kStageBytes;
 #pragma unroll
     for (int i = 0; i < NMT; ++i) {
       if (i < mt_active) {
@@ -481,36 +477,54 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(
         u32x4 af[kQ], al[kQ];
 #pragma unroll
         for (int q = 0; q < kQ; ++q) {
-          const int off = row * kRowBytes + ((((fc * kQ) + q) ^ (row & (kPieces - 1))) << 4);
-          af[q] = ld16(&lds[cur][off]);
-          if constexpr (kTwoA) al[q] = ld16(&lds[cur][kPlaneBytes + off]);
+          const int off = row * kRowBytes + (((q * 4 + fc) ^ swz(row)) << 4);
+          af[q] = ld16(st + off);
+          if constexpr (kTwoA) al[q] = ld16(st + kPlaneBytes + off);
         }
 #pragma unroll
         for (int j = 0; j < NWN; ++j) {
           if constexpr (sizeof(T) == 2) {
 #pragma unroll
             for (int q = 0; q < kQ; ++q) {
-              acc[i][j] = mfma_bf16(af[q], wcur[j][q], acc[i][j]);
-              if constexpr (kTwoA) acc[i][j] = mfma_bf16(al[q], wcur[j][q], acc[i][j]);
+              acc[i][j] = mfma_bf16(af[q], wc[j][q], acc[i][j]);
+              if constexpr (kTwoA) acc[i][j] = mfma_bf16(al[q], wc[j][q], acc[i][j]);
             }
           } else {
 #pragma unroll
             for (int q = 0; q < kQ; ++q)
 #pragma unroll
               for (int u = 0; u < 4; ++u)
-                acc[i][j] = mfma_f32(__uint_as_float(af[q][u]), __uint_as_float(wcur[j][q][u]),
+                acc[i][j] = mfma_f32(__uint_as_float(af[q][u]), __uint_as_float(wc[j][q][u]),
                                      acc[i][j]);
           }
         }
       }
     }
-    if (more) astore(cur ^ 1);
-    __syncthreads();
-    if (more) {
+  };
+
+  // Loads complete in issue order.  In steady state kDepth - 2 chunks' loads
+  // were issued after A of the next chunk, so waiting for at most that many
+  // outstanding lands it; near the end (fewer loads issued) wait for all.
+  constexpr int kSteadyWait = (kDepth - 2) * (kWInst + kAInst);
 #pragma unroll
-      for (int j = 0; j < NWN; ++j)
+  for (int d = 0; d < kDepth - 1; ++d)
+    if (d < nch) issue(wbuf[d], d, d);
+  if (nch >= kDepth - 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kSteadyWait));
+  else __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+  __syncthreads();
+  for (int ch0 = 0; ch0 < nch; ch0 += kDepth) {
 #pragma unroll
-        for (int q = 0; q < kQ; ++q) wcur[j][q] = wnext[j][q];
+    for (int d = 0; d < kDepth; ++d) {
+      const int ch = ch0 + d;
+      if (ch < nch) {
+        const int dn = (d + kDepth - 1) % kDepth;       // slot of chunk ch + kDepth - 1 (constant once unrolled)
+        const bool steady = ch + kDepth - 1 < nch;
+        if (steady) issue(wbuf[dn], dn, ch + kDepth - 1);
+        compute(wbuf[d], d);
+        if (steady) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kSteadyWait));
+        else __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+        __syncthreads();
+      }
     }
   }
 
