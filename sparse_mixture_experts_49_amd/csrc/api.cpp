@@ -147,7 +147,7 @@ size_t elem_bytes(const moe_desc* d) { return d->dtype == MOE_DTYPE_BF16 ? 2 : 4
 struct Layout {
   size_t part_psum, part_top1, blk_hist, blk_base;
   size_t topk_idx, topk_w, counts, offsets, dest, src, top1, prob_mean;
-  size_t x_perm, h, o;
+  size_t x_perm, h, o, partial;
   size_t total;
 };
 
@@ -177,6 +177,18 @@ Layout layout_of(const moe_desc* d) {
   resolve(d, plan);
   L.h = take(A * d->d_ff * plan.h_elem);
   L.o = take(A * d->d_model * sizeof(float));
+  // Split-k partial sums of the weight-streaming path (one product at a time).
+  size_t part = 0;
+  if (plan.path == MOE_FFN_STREAM) {
+    const bool bf16 = d->dtype == MOE_DTYPE_BF16, split = plan.h_mode == MOE_H_SPLIT;
+    for (int up = 0; up < 2; ++up) {
+      const size_t b = moe::ffn_partial_bytes(bf16, up, split, d->n_experts,
+                                              up ? d->d_ff : d->d_model, up ? d->d_model : d->d_ff,
+                                              row_bound(d), max_rows(d));
+      if (b > part) part = b;
+    }
+  }
+  L.partial = take(part);
   L.total = p;
   return L;
 }
@@ -247,7 +259,7 @@ int launch_perm(const moe_desc* d, const void* x, const int32_t* idx, int32_t* c
 }
 
 int launch_one_ffn(const moe_desc* d, bool up, const void* in, const int32_t* offsets,
-                   const moe_weights* w, void* out, hipStream_t s) {
+                   const moe_weights* w, void* out, void* ws, const Layout& L, hipStream_t s) {
   Plan plan{};
   if (int st = resolve(d, plan)) return st;
   moe::FfnArgs a{};
@@ -266,6 +278,7 @@ int launch_one_ffn(const moe_desc* d, bool up, const void* in, const int32_t* of
   a.max_rows_per_expert = row_bound(d);
   a.max_rows = max_rows(d);
   a.path = plan.path;
+  a.partial = at<float>(ws, L.partial);
   return hip_status(moe::launch_ffn(a, s), up ? "ffn up launch" : "ffn down launch");
 }
 
@@ -355,7 +368,7 @@ int moe_ffn_up(const moe_desc* desc, const void* x_perm, const int32_t* offsets,
   if (int st = validate_weights(desc, w, false, true)) return st;
   Layout L;
   if (int st = check_ws(desc, ws, ws_bytes, L)) return st;
-  return launch_one_ffn(desc, true, x_perm, offsets, w, h, static_cast<hipStream_t>(stream));
+  return launch_one_ffn(desc, true, x_perm, offsets, w, h, ws, L, static_cast<hipStream_t>(stream));
 }
 
 int moe_ffn_down(const moe_desc* desc, const void* h, const int32_t* offsets,
@@ -367,7 +380,7 @@ int moe_ffn_down(const moe_desc* desc, const void* h, const int32_t* offsets,
   if (int st = validate_weights(desc, w, false, true)) return st;
   Layout L;
   if (int st = check_ws(desc, ws, ws_bytes, L)) return st;
-  return launch_one_ffn(desc, false, h, offsets, w, o, static_cast<hipStream_t>(stream));
+  return launch_one_ffn(desc, false, h, offsets, w, o, ws, L, static_cast<hipStream_t>(stream));
 }
 
 int moe_grouped_ffn(const moe_desc* desc, const void* x_perm, const int32_t* offsets,
@@ -382,8 +395,8 @@ int moe_grouped_ffn(const moe_desc* desc, const void* x_perm, const int32_t* off
   Layout L;
   if (int st = check_ws(desc, ws, ws_bytes, L)) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (int st = launch_one_ffn(desc, true, x_perm, offsets, w, h, s)) return st;
-  return launch_one_ffn(desc, false, h, offsets, w, o, s);
+  if (int st = launch_one_ffn(desc, true, x_perm, offsets, w, h, ws, L, s)) return st;
+  return launch_one_ffn(desc, false, h, offsets, w, o, ws, L, s);
 }
 
 int moe_combine(const moe_desc* desc, const float* o, const int32_t* dest, const float* topk_w,
@@ -432,8 +445,8 @@ int moe_forward(const moe_desc* desc, const void* x, const moe_weights* w, float
   if (int st = launch_perm(desc, x, r.topk_idx, r.counts, r.offsets, r.dest, r.src, x_perm, L, ws,
                            s))
     return st;
-  if (int st = launch_one_ffn(desc, true, x_perm, r.offsets, w, h, s)) return st;
-  if (int st = launch_one_ffn(desc, false, h, r.offsets, w, o, s)) return st;
+  if (int st = launch_one_ffn(desc, true, x_perm, r.offsets, w, h, ws, L, s)) return st;
+  if (int st = launch_one_ffn(desc, false, h, r.offsets, w, o, ws, L, s)) return st;
   return launch_comb(desc, o, r.dest, r.topk_w, y, s);
 }
 

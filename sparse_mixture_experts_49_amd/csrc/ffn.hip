@@ -21,6 +21,7 @@
 //     the four waves.  Weight bytes are read once.
 // The first product applies bias + exact-erf GELU in its epilogue and stores
 // dtype h; the second adds its bias and stores fp32 o.
+#include <algorithm>
 #include <type_traits>
 
 #include "device_common.h"
@@ -63,6 +64,22 @@ __device__ __forceinline__ void store_out(void* out, size_t idx, float v) {
   }
 }
 
+// One finished pre-activation (bias included) of the stream path: the first
+// product stores GELU of it (as dtype, or as bf16 hi + lo planes when h is
+// split), the second stores it as fp32.
+template <typename T, bool UP, bool SPLIT>
+__device__ __forceinline__ void emit(void* out, size_t out_plane, size_t idx, float v) {
+  if constexpr (UP && SPLIT) {
+    const float g = gelu_erf(v);
+    const uint16_t hi = f32_to_bf16(g);
+    const uint16_t lo = f32_to_bf16(g - bf16_to_f32(hi));
+    static_cast<uint16_t*>(out)[idx] = hi;
+    static_cast<uint16_t*>(out)[out_plane + idx] = lo;
+  } else {
+    store_out<T, UP>(out, idx, v);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // LDS-tiled kernel (bf16).  Block tile 256 (rows of one expert) x BN (output
 // columns), k-steps of 64.  NW = 4 waves, one per SIMD, as 2 x 2; each wave
@@ -93,6 +110,9 @@ __device__ __forceinline__ void store_out(void* out, size_t idx, float v) {
 // mapping at the top of the kernel.
 // ---------------------------------------------------------------------------
 constexpr int kTBM = 256, kTBK = 64, kBandM = 4, kXcds = 8;
+// Weight-streaming launches aim for at least this many blocks (8 per CU on a
+// 256-CU MI355X) before they split the k range.
+constexpr long kStreamMinBlocks = 2048;
 
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -399,7 +419,7 @@ template <typename T, bool UP, bool SPLIT, int NMT, int NWN>
 __global__ __launch_bounds__(256) void ffn_stream_kernel(
     const T* __restrict__ A, const T* __restrict__ A_lo, const int32_t* __restrict__ offsets,
     const T* __restrict__ W, const T* __restrict__ bias, void* __restrict__ out,
-    size_t out_plane, int E, int N, int K) {
+    size_t out_plane, int E, int N, int K, int splits, float* __restrict__ partial, int rows_cap) {
   constexpr bool kTwoA = SPLIT && !UP;             // A operand is split h
   constexpr int kQ = kTwoA ? 2 : 4;                // 16 B pieces per lane per chunk
   constexpr int kPerVec = 16 / sizeof(T);
@@ -417,8 +437,9 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(
   auto swz = [](int row) { return kPieces == 16 ? (row & 15) : ((row >> 1) & 7); };
 
   const int e = blockIdx.y;
+  const int split = blockIdx.z % splits;             // k range [c0, c1) of the chunks
   const int seg0 = offsets[e], seg1 = offsets[e + 1];
-  const int r0 = seg0 + blockIdx.z * kMR;
+  const int r0 = seg0 + (blockIdx.z / splits) * kMR;
   if (r0 >= seg1) return;
   const int r1 = min(seg1, r0 + kMR);
   const int mt_active = (r1 - r0 + 15) >> 4;
@@ -454,12 +475,14 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(
 #pragma unroll
     for (int j = 0; j < NWN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nch = K / kChunk;
+  const int nch_all = K / kChunk;
+  const int c0 = (int)((long)split * nch_all / splits);
+  const int nch = (int)((long)(split + 1) * nch_all / splits) - c0;
   const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
   u32x4 wbuf[kDepth][NWN][kQ];
   // Issue chunk ch: W into register slot `slot`, A into LDS stage `slot`.
   auto issue = [&](u32x4 (&wdst)[NWN][kQ], int slot, int ch) {
-    const int k0 = ch * kChunk;
+    const int k0 = (c0 + ch) * kChunk;
 #pragma unroll
     for (int j = 0; j < NWN; ++j)
 #pragma unroll
@@ -528,11 +551,14 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(
     }
   }
 
+  // Epilogue.  Lane (fr, fc) holds column n0 + 16j + fr of rows 4fc + v.  With
+  // a split k range each split stores its fp32 partial sums (split 0 adds the
+  // bias) and ffn_splitk_reduce finishes the product.
   const T* bexp = bias ? bias + (size_t)e * N : nullptr;
 #pragma unroll
   for (int j = 0; j < NWN; ++j) {
     const int col = n0 + j * 16 + fr;
-    const float bv = bexp ? Elem<T>::to_f32(bexp[col]) : 0.f;
+    const float bv = (bexp && split == 0) ? Elem<T>::to_f32(bexp[col]) : 0.f;
 #pragma unroll
     for (int i = 0; i < NMT; ++i) {
 #pragma unroll
@@ -540,52 +566,101 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(
         const int row = r0 + i * 16 + 4 * fc + v;
         if (row < r1) {
           const size_t idx = (size_t)row * N + col;
-          if constexpr (UP && SPLIT) {
-            const float g = gelu_erf(acc[i][j][v] + bv);
-            const uint16_t hi = f32_to_bf16(g);
-            const uint16_t lo = f32_to_bf16(g - bf16_to_f32(hi));
-            static_cast<uint16_t*>(out)[idx] = hi;
-            static_cast<uint16_t*>(out)[out_plane + idx] = lo;
-          } else {
-            store_out<T, UP>(out, idx, acc[i][j][v] + bv);
-          }
+          if (splits > 1)
+            partial[((size_t)split * rows_cap + row) * N + col] = acc[i][j][v] + bv;
+          else
+            emit<T, UP, SPLIT>(out, out_plane, idx, acc[i][j][v] + bv);
         }
       }
     }
   }
 }
 
+// Finish a split-k product: out[r][c] = epilogue(sum over splits s of
+// partial[s][r][c]), summed in split order; rows r < offsets[E] only.  Each
+// thread handles four consecutive columns.
+template <typename T, bool UP, bool SPLIT>
+__global__ __launch_bounds__(256) void ffn_splitk_reduce(
+    const float* __restrict__ partial, const int32_t* __restrict__ offsets, int E, int N,
+    int splits, int rows_cap, void* __restrict__ out, size_t out_plane) {
+  const int R = offsets[E];
+  const size_t q = (size_t)blockIdx.x * 256 + threadIdx.x;   // quad index
+  const int quads = N / 4;
+  const int row = (int)(q / quads), c = (int)(q % quads) * 4;
+  if (row >= R) return;
+  f32x4 v = *reinterpret_cast<const f32x4*>(partial + (size_t)row * N + c);
+  for (int sp = 1; sp < splits; ++sp)
+    v += *reinterpret_cast<const f32x4*>(partial + ((size_t)sp * rows_cap + row) * N + c);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) emit<T, UP, SPLIT>(out, out_plane, (size_t)row * N + c + u, v[u]);
+}
+
+// Launch shape of the weight-streaming kernel, decided on the host from the
+// descriptor alone (never from device data).
+struct StreamShape {
+  int nmt, nwn, groups, splits;
+};
+static StreamShape stream_shape(bool bf16, bool up, bool split, int E, int N, int K,
+                                int max_rows_per_expert) {
+  // Rows per block: 16/32/64/160, the smallest covering the host's bound on
+  // any expert's rows (capped at 160); more row groups (grid z) cover the rest.
+  // Empty m-tiles issue no MFMA, so a generous block costs registers only.
+  StreamShape sh{};
+  const int bound = max_rows_per_expert;
+  sh.nmt = bound <= 16 ? 1 : bound <= 32 ? 2 : bound <= 64 ? 4 : 10;
+  sh.groups = (bound + 16 * sh.nmt - 1) / (16 * sh.nmt);
+  sh.nwn = (sh.nmt < 10 && (long)E * (N / 128) >= 1024) ? 2 : 1;
+  // Split the k range when the grid is too small to keep enough weight loads
+  // in flight (fewer than kStreamMinBlocks / 2 blocks), up to about
+  // kStreamMinBlocks blocks and keeping >= 8 chunks per split; the partial sums
+  // cost rows x N x 4 B per split plus a reduce launch, which does not pay for
+  // grids already above that (measured on MI355X).
+  const int chunk = !bf16 ? 64 : (split && !up) ? 64 : 128;
+  const long blocks = (long)(N / (64 * sh.nwn)) * E * sh.groups;
+  const int max_splits = std::max(1, std::min(8, K / chunk / 8));
+  sh.splits = 1;
+  if (blocks < kStreamMinBlocks / 2)
+    while (sh.splits < max_splits && blocks * sh.splits < kStreamMinBlocks) ++sh.splits;
+  return sh;
+}
+
+size_t ffn_partial_bytes(bool bf16, bool up, bool split, int E, int N, int K,
+                         int max_rows_per_expert, int max_rows) {
+  const StreamShape sh = stream_shape(bf16, up, split, E, N, K, max_rows_per_expert);
+  return sh.splits > 1 ? (size_t)sh.splits * max_rows * N * sizeof(float) : 0;
+}
+
 template <typename T, bool UP, bool SPLIT, int NMT>
-static void launch_stream_nwn(const FfnArgs& a, int nwn, int groups, hipStream_t s) {
+static void launch_stream_nmt(const FfnArgs& a, const StreamShape& sh, hipStream_t s) {
   const T* A = static_cast<const T*>(a.a);
   const T* A_lo = SPLIT && !UP ? A + a.plane : nullptr;
   const T* W = static_cast<const T*>(a.w);
   const T* B = static_cast<const T*>(a.bias);
-  if (nwn == 2) {
-    dim3 grid(a.N / 128, a.E, groups);
-    ffn_stream_kernel<T, UP, SPLIT, NMT, 2><<<grid, 256, 0, s>>>(A, A_lo, a.offsets, W, B, a.out,
-                                                                 a.plane, a.E, a.N, a.K);
+  const int z = sh.groups * sh.splits;
+  if (sh.nwn == 2) {
+    dim3 grid(a.N / 128, a.E, z);
+    ffn_stream_kernel<T, UP, SPLIT, NMT, 2><<<grid, 256, 0, s>>>(
+        A, A_lo, a.offsets, W, B, a.out, a.plane, a.E, a.N, a.K, sh.splits, a.partial, a.max_rows);
   } else {
-    dim3 grid(a.N / 64, a.E, groups);
-    ffn_stream_kernel<T, UP, SPLIT, NMT, 1><<<grid, 256, 0, s>>>(A, A_lo, a.offsets, W, B, a.out,
-                                                                 a.plane, a.E, a.N, a.K);
+    dim3 grid(a.N / 64, a.E, z);
+    ffn_stream_kernel<T, UP, SPLIT, NMT, 1><<<grid, 256, 0, s>>>(
+        A, A_lo, a.offsets, W, B, a.out, a.plane, a.E, a.N, a.K, sh.splits, a.partial, a.max_rows);
+  }
+  if (sh.splits > 1) {
+    const size_t quads = (size_t)a.max_rows * (a.N / 4);
+    ffn_splitk_reduce<T, UP, SPLIT><<<(unsigned)((quads + 255) / 256), 256, 0, s>>>(
+        a.partial, a.offsets, a.E, a.N, sh.splits, a.max_rows, a.out, a.plane);
   }
 }
 
 template <typename T, bool UP, bool SPLIT>
 static void launch_stream(const FfnArgs& a, hipStream_t s) {
-  // Rows per block: 16/32/64/160, the smallest covering the host's bound on
-  // any expert's rows (capped at 160); more row groups (grid z) cover the rest.
-  // Empty m-tiles issue no MFMA, so a generous block costs registers only.
-  const int bound = a.max_rows_per_expert;
-  const int nmt = bound <= 16 ? 1 : bound <= 32 ? 2 : bound <= 64 ? 4 : 10;
-  const int groups = (bound + 16 * nmt - 1) / (16 * nmt);
-  const int nwn = (nmt < 10 && (long)a.E * (a.N / 128) >= 1024) ? 2 : 1;
-  switch (nmt) {
-    case 1: launch_stream_nwn<T, UP, SPLIT, 1>(a, nwn, groups, s); break;
-    case 2: launch_stream_nwn<T, UP, SPLIT, 2>(a, nwn, groups, s); break;
-    case 4: launch_stream_nwn<T, UP, SPLIT, 4>(a, nwn, groups, s); break;
-    default: launch_stream_nwn<T, UP, SPLIT, 10>(a, nwn, groups, s); break;
+  const StreamShape sh = stream_shape(a.bf16, UP, SPLIT, a.E, a.N, a.K, a.max_rows_per_expert);
+  switch (sh.nmt) {
+    case 1: launch_stream_nmt<T, UP, SPLIT, 1>(a, sh, s); break;
+    case 2: launch_stream_nmt<T, UP, SPLIT, 2>(a, sh, s); break;
+    case 4: launch_stream_nmt<T, UP, SPLIT, 4>(a, sh, s); break;
+    default: launch_stream_nmt<T, UP, SPLIT, 10>(a, sh, s); break;
   }
 }
 
