@@ -15,6 +15,7 @@
 namespace moe {
 
 constexpr int kRouterTokens = 16;   // tokens per block (one MFMA row tile)
+constexpr int kAuxThreads = 512;    // threads of the single aux-reduction block
 constexpr int kRouterWaves = 4;     // the block's waves split d between them
 
 // One block = 16 tokens x all experts.  Wave w accumulates the k-chunks
@@ -186,47 +187,50 @@ __global__ __launch_bounds__(256) void router_kernel(
   }
 }
 
-// Fixed-order reduction of the router partials: f, P and aux.
-// 256 threads: thread (e = tid % 64, g = tid / 64) sums blocks g, g+4, ...;
-// the four group sums are then added in group order.
-__global__ __launch_bounds__(256) void aux_finalize_kernel(
+// Fixed-order reduction of the router partials: f, P and aux (web page
+// "Mixture of Experts: Scaling Parameters Without Scaling Compute", section
+// "The central problem: load balancing").
+__global__ __launch_bounds__(kAuxThreads) void aux_finalize_kernel(
     const double* __restrict__ part_psum, const int32_t* __restrict__ part_top1, int nblk,
     int T_, int E, int32_t* __restrict__ top1_count, float* __restrict__ prob_mean,
     float* __restrict__ aux) {
-  __shared__ double ps[4][64];
-  __shared__ long long pc[4][64];
+  // The partials are [nblk][E] laid out flat.  Thread t < stride (a multiple of
+  // E) sums entries t, t + stride, ... (all of expert t % E, coalesced across
+  // the block); expert e's per-thread sums are then added in thread order.
+  // The grouping depends only on (nblk, E), so the result is deterministic.
+  __shared__ double ps[kAuxThreads];
+  __shared__ long long pc[kAuxThreads];
   __shared__ double fP[64];
-  const int e = threadIdx.x & 63, g = threadIdx.x >> 6;
-  double s = 0.0;
+  const int t = threadIdx.x;
+  const int stride = (kAuxThreads / E) * E;
+  const long n = (long)nblk * E;
+  double sum = 0.0;
   long long cnt = 0;
-  if (e < E) {
-    for (int b = g; b < nblk; b += 4) {
-      s += part_psum[(size_t)b * E + e];
-      cnt += part_top1[(size_t)b * E + e];
+  if (t < stride)
+    for (long i = t; i < n; i += stride) {
+      sum += part_psum[i];
+      cnt += part_top1[i];
     }
-  }
-  ps[g][e] = s;
-  pc[g][e] = cnt;
+  ps[t] = sum;
+  pc[t] = cnt;
   __syncthreads();
-  if (g == 0) {
+  if (t < E) {
     double S = 0.0;
     long long C = 0;
-    if (e < E) {
-      S = ((ps[0][e] + ps[1][e]) + ps[2][e]) + ps[3][e];
-      C = pc[0][e] + pc[1][e] + pc[2][e] + pc[3][e];
+    for (int u = t; u < stride; u += E) {
+      S += ps[u];
+      C += pc[u];
     }
     const double P = S / (double)T_, f = (double)C / (double)T_;
-    fP[e] = (e < E) ? f * P : 0.0;
-    if (e < E) {
-      if (top1_count) top1_count[e] = (int32_t)C;
-      if (prob_mean) prob_mean[e] = (float)P;
-    }
+    fP[t] = f * P;
+    if (top1_count) top1_count[t] = (int32_t)C;
+    if (prob_mean) prob_mean[t] = (float)P;
   }
   __syncthreads();
-  if (threadIdx.x == 0 && aux) {
-    double a = 0.0;
-    for (int i = 0; i < E; ++i) a += fP[i];
-    *aux = (float)((double)E * a);
+  if (t == 0 && aux) {
+    double acc = 0.0;
+    for (int i = 0; i < E; ++i) acc += fP[i];
+    *aux = (float)((double)E * acc);
   }
 }
 
@@ -252,7 +256,7 @@ static hipError_t launch_router_t(const RouterArgs& a, hipStream_t s) {
 #undef MOE_ROUTER_CASE
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  aux_finalize_kernel<<<1, 256, 0, s>>>(a.part_psum, a.part_top1, nblk, a.T, a.E, a.top1_count,
+  aux_finalize_kernel<<<1, kAuxThreads, 0, s>>>(a.part_psum, a.part_top1, nblk, a.T, a.E, a.top1_count,
                                         a.prob_mean, a.aux);
   return hipGetLastError();
 }
