@@ -177,12 +177,12 @@ Layout layout_of(const moe_desc* d) {
   resolve(d, plan);
   L.h = take(A * d->d_ff * plan.h_elem);
   L.o = take(A * d->d_model * sizeof(float));
-  // Split-k partial sums of the weight-streaming path (one product at a time).
+  // Split-k partial sums of the expert products (one product at a time).
   size_t part = 0;
-  if (plan.path == MOE_FFN_STREAM) {
+  {
     const bool bf16 = d->dtype == MOE_DTYPE_BF16, split = plan.h_mode == MOE_H_SPLIT;
     for (int up = 0; up < 2; ++up) {
-      const size_t b = moe::ffn_partial_bytes(bf16, up, split, d->n_experts,
+      const size_t b = moe::ffn_partial_bytes(plan.path, bf16, up, split, d->n_experts,
                                               up ? d->d_ff : d->d_model, up ? d->d_model : d->d_ff,
                                               row_bound(d), max_rows(d));
       if (b > part) part = b;

@@ -135,11 +135,87 @@ constexpr int kWaitLgkm0 = 0xC07F;   // lgkmcnt(0), others untouched
 // vmcnt <= vm and lgkmcnt(0).
 constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 0xF) | ((vm >> 4) << 14) | (0x7 << 4); }
 
+// Which tile (and which part of its k range) block b of the tiled kernel
+// computes.  Block b runs on XCD x = b % 8 (workgroups are dealt round-robin)
+// and takes entry i = b / 8 of that XCD's list.  m-tiles come in groups of 32;
+// in group g, XCD x owns m-tiles 32g + 4x .. +3 and walks them n-tile by
+// n-tile (4 m-tiles fastest).  The 32 blocks an XCD runs at once thus cover 4
+// m-tiles x 8 n-tiles (their A and W rows shared in its L2), and all XCDs
+// sweep the same n-tiles at the same time, so each W slice is fetched from HBM
+// once and served to the other XCDs from the last-level cache.  The m-tiles
+// past the last full group are dealt round-robin over the XCDs.
+//
+// Tail.  An XCD's list is cut into rounds of kCusPerXcd tiles.  If the last,
+// partial round has at most half a round of tiles, each of them is split into
+// S = min(kMaxSplit, kCusPerXcd / tail) parts of its k range, run by S blocks
+// that store fp32 partial tiles into workspace slot x * kCusPerXcd + j; the
+// reduce kernel then sums the parts in order.  Otherwise the last round's
+// tiles stay whole.
+constexpr int kCusPerXcd = 32;
+constexpr int kMaxSplit = 8;
+constexpr int kPartialSlots = kXcds * kCusPerXcd;
+constexpr size_t kPartialTileFloats = (size_t)kTBM * 256;
+
+struct TileJob {
+  int mt, nt;      // m-tile (over all experts, end to end) and n-tile
+  int part, parts; // part of the k range, of `parts` (1: the whole range)
+  int slot;        // partial-tile slot when parts > 1
+};
+
+__device__ __forceinline__ bool tile_job(const int32_t* __restrict__ offsets, int E, int ntn, int nk,
+                                         int b, TileJob& job) {
+  int total_mt = 0;
+  for (int e = 0; e < E; ++e) total_mt += (offsets[e + 1] - offsets[e] + kTBM - 1) / kTBM;
+  constexpr int kGroupM = kXcds * kBandM;
+  const int x = b % kXcds, i = b / kXcds;
+  const int G = total_mt / kGroupM;
+  const int full = G * kBandM * ntn;                 // entries from full groups, per XCD
+  const int lm = total_mt - G * kGroupM;             // leftover m-tiles (< 32)
+  const int left = lm * ntn;                         // leftover tiles, dealt round-robin
+  const int cnt = full + (left > x ? (left - x + kXcds - 1) / kXcds : 0);
+  const int rounds = cnt / kCusPerXcd, tail = cnt - rounds * kCusPerXcd;
+  const int S = (tail > 0 && 2 * tail <= kCusPerXcd) ? min(min(kMaxSplit, nk), kCusPerXcd / tail) : 1;
+  int entry = i;
+  job.part = 0;
+  job.parts = 1;
+  job.slot = 0;
+  if (S > 1 && i >= rounds * kCusPerXcd) {
+    const int j = i - rounds * kCusPerXcd;
+    if (j >= tail * S) return false;
+    entry = rounds * kCusPerXcd + j / S;
+    job.part = j % S;
+    job.parts = S;
+    job.slot = x * kCusPerXcd + j;
+  }
+  if (entry >= cnt) return false;
+  if (entry < full) {
+    const int g = entry / (kBandM * ntn), rem = entry - g * kBandM * ntn;
+    job.nt = rem / kBandM;
+    job.mt = g * kGroupM + x * kBandM + rem % kBandM;
+  } else {
+    const int u = (entry - full) * kXcds + x;
+    job.nt = u / lm;
+    job.mt = G * kGroupM + u % lm;
+  }
+  return true;
+}
+
+// First entry of XCD x's tail (its last, partial round) in tile_job's order.
+__device__ __forceinline__ int tail_start(const int32_t* __restrict__ offsets, int E, int ntn, int x) {
+  int total_mt = 0;
+  for (int e = 0; e < E; ++e) total_mt += (offsets[e + 1] - offsets[e] + kTBM - 1) / kTBM;
+  constexpr int kGroupM = kXcds * kBandM;
+  const int G = total_mt / kGroupM;
+  const int left = (total_mt - G * kGroupM) * ntn;
+  const int cnt = G * kBandM * ntn + (left > x ? (left - x + kXcds - 1) / kXcds : 0);
+  return cnt / kCusPerXcd * kCusPerXcd;
+}
+
 template <bool UP, int BN, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void ffn_tiled_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets,
     const uint16_t* __restrict__ W, const uint16_t* __restrict__ bias, void* __restrict__ out,
-    int E, int N, int K) {
+    int E, int N, int K, float* __restrict__ partial) {
   constexpr int kWavesN = NW / 2;
   constexpr int kWN = BN / kWavesN;       // wave tile columns
   constexpr int kNT = kWN / 32;           // 32-column subtiles per wave
@@ -155,33 +231,10 @@ __global__ __launch_bounds__(NW * 64, 1) void ffn_tiled_kernel(
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kLds];
 
   // ---- which tile ----
-  int total_mt = 0;
-  for (int e = 0; e < E; ++e) total_mt += (offsets[e + 1] - offsets[e] + kTBM - 1) / kTBM;
   const int ntn = N / BN;
-  // Block b runs on XCD x = b % 8 (workgroups are dealt round-robin) and takes
-  // entry i = b / 8 of that XCD's list.  m-tiles come in groups of 32; in
-  // group g, XCD x owns m-tiles 32g + 4x .. +3 and walks them n-tile by
-  // n-tile (4 m-tiles fastest).  The 32 blocks an XCD runs at once thus cover
-  // 4 m-tiles x 8 n-tiles (their A and W rows shared in its L2), and all XCDs
-  // sweep the same n-tiles at the same time, so each W slice is fetched from
-  // HBM once and served to the other XCDs from the last-level cache.  The
-  // m-tiles past the last full group are dealt round-robin over the XCDs.
-  constexpr int kGroupM = kXcds * kBandM;
-  const int x = blockIdx.x % kXcds, i = blockIdx.x / kXcds;
-  const int G = total_mt / kGroupM;
-  const int full = G * kBandM * ntn;                 // entries from full groups, per XCD
-  int mt, nt;
-  if (i < full) {
-    const int g = i / (kBandM * ntn), rem = i - g * kBandM * ntn;
-    nt = rem / kBandM;
-    mt = g * kGroupM + x * kBandM + rem % kBandM;
-  } else {
-    const int lm = total_mt - G * kGroupM;           // leftover m-tiles (< 32)
-    const int u = (i - full) * kXcds + x;
-    if (u >= lm * ntn) return;
-    nt = u / lm;
-    mt = G * kGroupM + u % lm;
-  }
+  TileJob job;
+  if (!tile_job(offsets, E, ntn, K / kTBK, blockIdx.x, job)) return;
+  const int mt = job.mt, nt = job.nt;
   int e, r0, r1;
   if (!find_mtile(offsets, E, kTBM, mt, e, r0, r1)) return;
   const int n0 = nt * BN;
@@ -208,7 +261,13 @@ __global__ __launch_bounds__(NW * 64, 1) void ffn_tiled_kernel(
     const int c = (lane & 7) ^ ((row >> 1) & 7);
     b_src[i] = Wexp + (size_t)(n0 + row) * K + c * 8;
   }
-  const int nk = K / kTBK;
+  const int nk_all = K / kTBK;
+  const int ks0 = (int)((long)job.part * nk_all / job.parts);
+  const int nk = (int)((long)(job.part + 1) * nk_all / job.parts) - ks0;
+#pragma unroll
+  for (int i = 0; i < kAInst; ++i) a_src[i] += ks0 * kTBK;
+#pragma unroll
+  for (int i = 0; i < kBInst; ++i) b_src[i] += ks0 * kTBK;
   // Steps past the last are clamped to it: those loads refill a free stage and
   // are never read, which keeps the loop body branch-free.
   const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
@@ -328,69 +387,121 @@ __global__ __launch_bounds__(NW * 64, 1) void ffn_tiled_kernel(
   // Epilogue through LDS.  Lane (fr, fc) holds, for each 32x32 subtile (jn, im)
   // and g = 0..3, row im*32 + fr and columns jn*32 + 8g + 4fc .. +3 of the
   // wave's sub-tile.  Each wave stages rows in its own LDS region with 16 B
-  // chunks XOR-swizzled by row, then stores whole row segments.
+  // chunks XOR-swizzled by row, then stores whole row segments of the rows
+  // below row_lim to dst (row stride in elements).  F32: fp32 values (the
+  // second product's output, or a partial tile); otherwise GELU, rounded to
+  // bf16 (the first product's output).
   const uint16_t* bexp = bias ? bias + (size_t)e * N : nullptr;
   auto bias4 = [&](int jn, int g, float (&bv)[4]) {
     const int col = n0 + wn * kWN + jn * 32 + 8 * g + 4 * fc;
-    if (bexp) {
-      const uint2 braw = *reinterpret_cast<const uint2*>(bexp + col);
-      bv[0] = __uint_as_float(braw.x << 16);
-      bv[1] = __uint_as_float(braw.x & 0xffff0000u);
-      bv[2] = __uint_as_float(braw.y << 16);
-      bv[3] = __uint_as_float(braw.y & 0xffff0000u);
-    } else {
-      bv[0] = bv[1] = bv[2] = bv[3] = 0.f;
-    }
+    const uint2 braw = *reinterpret_cast<const uint2*>(bexp + col);
+    bv[0] = __uint_as_float(braw.x << 16);
+    bv[1] = __uint_as_float(braw.x & 0xffff0000u);
+    bv[2] = __uint_as_float(braw.y << 16);
+    bv[3] = __uint_as_float(braw.y & 0xffff0000u);
   };
-  // Rows staged per pass so that NW regions fit in the 2-stage LDS area.
-  constexpr int kElem = UP ? 2 : 4;
-  constexpr int kRowB = kWN * kElem, kChunks = kRowB / 16;
-  constexpr int kPassRows = (kLds / NW) / kRowB >= 128 ? 128 : 64;
-  constexpr int kPasses = 128 / kPassRows;
-  constexpr int kRowsPerInst = 64 / kChunks;
-  uint8_t* my = lds + wave * (kPassRows * kRowB);
+  auto store_tile = [&](auto f32_tag, uint8_t* dst, size_t row_stride, int row_lim, bool with_bias) {
+    constexpr bool F32 = decltype(f32_tag)::value;
+    constexpr int kElem = F32 ? 4 : 2;
+    constexpr int kRowB = kWN * kElem, kChunks = kRowB / 16;
+    // Rows staged per pass so that NW regions fit in the LDS.
+    constexpr int kPassRows = (kLds / NW) / kRowB >= 128 ? 128 : 64;
+    constexpr int kPasses = 128 / kPassRows;
+    constexpr int kRowsPerInst = 64 / kChunks;
+    uint8_t* my = lds + wave * (kPassRows * kRowB);
 #pragma unroll
-  for (int pass = 0; pass < kPasses; ++pass) {
+    for (int pass = 0; pass < kPasses; ++pass) {
 #pragma unroll
-    for (int jn = 0; jn < kNT; ++jn)
+      for (int jn = 0; jn < kNT; ++jn)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        float bv[4];
-        bias4(jn, g, bv);
+        for (int g = 0; g < 4; ++g) {
+          float bv[4] = {0.f, 0.f, 0.f, 0.f};
+          if (with_bias) bias4(jn, g, bv);
 #pragma unroll
-        for (int imp = 0; imp < kPassRows / 32; ++imp) {
-          const int im = pass * (kPassRows / 32) + imp;
-          const int row = imp * 32 + fr;           // row within this pass
-          if constexpr (UP) {
-            const int chunk = jn * 4 + g;           // 16 B = 8 columns; fc picks the half
-            uint32_t p[2];
+          for (int imp = 0; imp < kPassRows / 32; ++imp) {
+            const int im = pass * (kPassRows / 32) + imp;
+            const int row = imp * 32 + fr;           // row within this pass
+            if constexpr (!F32) {
+              const int chunk = jn * 4 + g;           // 16 B = 8 columns; fc picks the half
+              uint32_t p[2];
 #pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2)
-              p[h2] = pack_bf16x2(gelu_erf(acc[jn][im][4 * g + 2 * h2] + bv[2 * h2]),
-                                  gelu_erf(acc[jn][im][4 * g + 2 * h2 + 1] + bv[2 * h2 + 1]));
-            *reinterpret_cast<uint2*>(my + row * kRowB + ((chunk ^ (row & (kChunks - 1))) << 4) + fc * 8) =
-                make_uint2(p[0], p[1]);
-          } else {
-            const int chunk = jn * 8 + 2 * g + fc;  // 16 B = 4 columns
-            f32x4 v;
+              for (int h2 = 0; h2 < 2; ++h2)
+                p[h2] = pack_bf16x2(gelu_erf(acc[jn][im][4 * g + 2 * h2] + bv[2 * h2]),
+                                    gelu_erf(acc[jn][im][4 * g + 2 * h2 + 1] + bv[2 * h2 + 1]));
+              *reinterpret_cast<uint2*>(my + row * kRowB + ((chunk ^ (row & (kChunks - 1))) << 4) + fc * 8) =
+                  make_uint2(p[0], p[1]);
+            } else {
+              const int chunk = jn * 8 + 2 * g + fc;  // 16 B = 4 columns
+              f32x4 v;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) v[q] = acc[jn][im][4 * g + q] + bv[q];
-            *reinterpret_cast<f32x4*>(my + row * kRowB + ((chunk ^ (row & (kChunks - 1))) << 4)) = v;
+              for (int q = 0; q < 4; ++q) v[q] = acc[jn][im][4 * g + q] + bv[q];
+              *reinterpret_cast<f32x4*>(my + row * kRowB + ((chunk ^ (row & (kChunks - 1))) << 4)) = v;
+            }
           }
         }
-      }
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);          // our own LDS writes are done
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);        // our own LDS writes are done
 #pragma unroll 4
-    for (int rb = 0; rb < kPassRows; rb += kRowsPerInst) {
-      const int row = rb + lane / kChunks, chunk = lane % kChunks;
-      const int grow = r0 + wm * 128 + pass * kPassRows + row;
-      const u32x4 v = ld16(my + row * kRowB + ((chunk ^ (row & (kChunks - 1))) << 4));
-      if (grow < r1) {
-        uint8_t* dst = static_cast<uint8_t*>(out) + ((size_t)grow * N + n0 + wn * kWN) * kElem + chunk * 16;
-        st16(dst, v);
+      for (int rb = 0; rb < kPassRows; rb += kRowsPerInst) {
+        const int row = rb + lane / kChunks, chunk = lane % kChunks;
+        const int lrow = wm * 128 + pass * kPassRows + row;
+        const u32x4 v = ld16(my + row * kRowB + ((chunk ^ (row & (kChunks - 1))) << 4));
+        if (lrow < row_lim) st16(dst + ((size_t)lrow * row_stride + wn * kWN) * kElem + chunk * 16, v);
       }
+      if (kPasses > 1) __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // reads done before the next pass
     }
-    if (kPasses > 1) __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // reads done before the next pass
+  };
+  if (job.parts > 1) {
+    store_tile(std::true_type{}, reinterpret_cast<uint8_t*>(partial + job.slot * kPartialTileFloats),
+               BN, r1 - r0, false);
+  } else if constexpr (UP) {
+    store_tile(std::false_type{}, static_cast<uint8_t*>(out) + ((size_t)r0 * N + n0) * 2, N, r1 - r0,
+               bexp != nullptr);
+  } else {
+    store_tile(std::true_type{}, static_cast<uint8_t*>(out) + ((size_t)r0 * N + n0) * 4, N, r1 - r0,
+               bexp != nullptr);
+  }
+}
+
+// Finish the tiles the tiled kernel split along k: block (x = b % 8, j = b / 8)
+// takes the j-th block of XCD x's tail round, i.e. part p of a split tile,
+// and completes rows [p * 256 / S, (p + 1) * 256 / S) of it: the S partial
+// tiles summed in part order, plus the bias, then the product's epilogue.
+template <bool UP, int BN>
+__global__ __launch_bounds__(256) void ffn_tile_reduce(
+    const int32_t* __restrict__ offsets, const uint16_t* __restrict__ bias, void* __restrict__ out,
+    int E, int N, int K, const float* __restrict__ partial) {
+  const int ntn = N / BN, x = blockIdx.x % kXcds, j = blockIdx.x / kXcds;
+  TileJob job;
+  if (!tile_job(offsets, E, ntn, K / kTBK, x + kXcds * (tail_start(offsets, E, ntn, x) + j), job) ||
+      job.parts == 1)
+    return;
+  int e, r0, r1;
+  if (!find_mtile(offsets, E, kTBM, job.mt, e, r0, r1)) return;
+  const int n0 = job.nt * BN;
+  const int ra = job.part * kTBM / job.parts;
+  const int rb = min(r1 - r0, (job.part + 1) * kTBM / job.parts);
+  const float* p0 = partial + (size_t)(job.slot - job.part) * kPartialTileFloats;
+  const uint16_t* bexp = bias ? bias + (size_t)e * N + n0 : nullptr;
+  constexpr int kQuads = BN / 4;
+  for (int q = ra * kQuads + threadIdx.x; q < rb * kQuads; q += 256) {
+    const int r = q / kQuads, c = (q % kQuads) * 4;
+    f32x4 v = *reinterpret_cast<const f32x4*>(p0 + (size_t)r * BN + c);
+    for (int sp = 1; sp < job.parts; ++sp)
+      v += *reinterpret_cast<const f32x4*>(p0 + sp * kPartialTileFloats + (size_t)r * BN + c);
+    if (bexp) {
+      const uint2 braw = *reinterpret_cast<const uint2*>(bexp + c);
+      v[0] += __uint_as_float(braw.x << 16);
+      v[1] += __uint_as_float(braw.x & 0xffff0000u);
+      v[2] += __uint_as_float(braw.y << 16);
+      v[3] += __uint_as_float(braw.y & 0xffff0000u);
+    }
+    const size_t idx = (size_t)(r0 + r) * N + n0 + c;
+    if constexpr (UP) {
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + idx) =
+          make_uint2(pack_bf16x2(gelu_erf(v[0]), gelu_erf(v[1])), pack_bf16x2(gelu_erf(v[2]), gelu_erf(v[3])));
+    } else {
+      *reinterpret_cast<f32x4*>(static_cast<float*>(out) + idx) = v;
+    }
   }
 }
 
@@ -624,8 +735,9 @@ static StreamShape stream_shape(bool bf16, bool up, bool split, int E, int N, in
   return sh;
 }
 
-size_t ffn_partial_bytes(bool bf16, bool up, bool split, int E, int N, int K,
+size_t ffn_partial_bytes(int path, bool bf16, bool up, bool split, int E, int N, int K,
                          int max_rows_per_expert, int max_rows) {
+  if (path == MOE_FFN_TILED) return (size_t)kPartialSlots * kPartialTileFloats * sizeof(float);
   const StreamShape sh = stream_shape(bf16, up, split, E, N, K, max_rows_per_expert);
   return sh.splits > 1 ? (size_t)sh.splits * max_rows * N * sizeof(float) : 0;
 }
@@ -672,15 +784,28 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
     const uint16_t* A = static_cast<const uint16_t*>(a.a);
     const uint16_t* W = static_cast<const uint16_t*>(a.w);
     const uint16_t* B = static_cast<const uint16_t*>(a.bias);
+    // Per XCD at most ceil(max_mt * ntn / 8) entries, plus at most one round of
+    // tail-split blocks; blocks without a job exit at once.
     constexpr int NW = 4;
-    if (a.N % 256 == 0) {
-      const int grid = ((max_mt * (a.N / 256) + kXcds - 1) / kXcds + 1) * kXcds;
-      if (a.up) ffn_tiled_kernel<true, 256, NW><<<grid, NW * 64, 0, s>>>(A, a.offsets, W, B, a.out, a.E, a.N, a.K);
-      else ffn_tiled_kernel<false, 256, NW><<<grid, NW * 64, 0, s>>>(A, a.offsets, W, B, a.out, a.E, a.N, a.K);
+    const int bn = a.N % 256 == 0 ? 256 : 128;
+    const int per_xcd = (max_mt * (a.N / bn) + kXcds - 1) / kXcds + 1 + kCusPerXcd;
+    const int grid = per_xcd * kXcds;
+    if (bn == 256) {
+      if (a.up) {
+        ffn_tiled_kernel<true, 256, NW><<<grid, NW * 64, 0, s>>>(A, a.offsets, W, B, a.out, a.E, a.N, a.K, a.partial);
+        ffn_tile_reduce<true, 256><<<kPartialSlots, 256, 0, s>>>(a.offsets, B, a.out, a.E, a.N, a.K, a.partial);
+      } else {
+        ffn_tiled_kernel<false, 256, NW><<<grid, NW * 64, 0, s>>>(A, a.offsets, W, B, a.out, a.E, a.N, a.K, a.partial);
+        ffn_tile_reduce<false, 256><<<kPartialSlots, 256, 0, s>>>(a.offsets, B, a.out, a.E, a.N, a.K, a.partial);
+      }
     } else {
-      const int grid = ((max_mt * (a.N / 128) + kXcds - 1) / kXcds + 1) * kXcds;
-      if (a.up) ffn_tiled_kernel<true, 128, 4><<<grid, 256, 0, s>>>(A, a.offsets, W, B, a.out, a.E, a.N, a.K);
-      else ffn_tiled_kernel<false, 128, 4><<<grid, 256, 0, s>>>(A, a.offsets, W, B, a.out, a.E, a.N, a.K);
+      if (a.up) {
+        ffn_tiled_kernel<true, 128, 4><<<grid, 256, 0, s>>>(A, a.offsets, W, B, a.out, a.E, a.N, a.K, a.partial);
+        ffn_tile_reduce<true, 128><<<kPartialSlots, 256, 0, s>>>(a.offsets, B, a.out, a.E, a.N, a.K, a.partial);
+      } else {
+        ffn_tiled_kernel<false, 128, 4><<<grid, 256, 0, s>>>(A, a.offsets, W, B, a.out, a.E, a.N, a.K, a.partial);
+        ffn_tile_reduce<false, 128><<<kPartialSlots, 256, 0, s>>>(a.offsets, B, a.out, a.E, a.N, a.K, a.partial);
+      }
     }
   } else if (a.bf16) {
     if (a.split) {

@@ -53,11 +53,12 @@ struct FfnArgs {
   int path;                // resolved MOE_FFN_TILED or MOE_FFN_STREAM
   bool split;              // bf16 h kept as hi + lo planes (MOE_H_SPLIT)
   size_t plane;            // elements per h plane (T*k*F) when split
-  float* partial;          // workspace for split-k partial sums (ffn_partial_bytes)
+  float* partial;          // workspace for split-k partial sums (ffn_partial_bytes bytes)
 };
 hipError_t launch_ffn(const FfnArgs& a, hipStream_t s);
-// Workspace bytes the product needs for split-k partial sums (0 if unsplit).
-size_t ffn_partial_bytes(bool bf16, bool up, bool split, int E, int N, int K,
+// Workspace bytes the product needs for split-k partial sums on `path`
+// (MOE_FFN_TILED or MOE_FFN_STREAM; 0 if it never splits).
+size_t ffn_partial_bytes(int path, bool bf16, bool up, bool split, int E, int N, int K,
                          int max_rows_per_expert, int max_rows);
 
 struct CombineArgs {
