@@ -25,6 +25,10 @@ Readings where the pages are silent or garbled (all listed in the design notes):
   * the router has no bias unless a workload supplies an fp32 logit bias;
   * top-k ranks experts by logit, descending, equal logits -> lower index
     first; softmax is monotone, so this is the same order as by probability;
+  * an optional per-expert selection bias is added to the logits for ranking
+    only; the routing weights stay softmax(logits) of the chosen experts;
+  * the router z-loss is the mean over tokens of the squared log-sum-exp of
+    the logits (router bias included, selection bias not);
   * renormalisation divides the chosen probabilities by their sum;
   * y sums the weighted expert outputs (each expert's output bias included)
     in slot order; no residual is added inside the layer;
@@ -96,6 +100,23 @@ def topk_by_logit(g, k):
     else:
         margin = np.full(g.shape[0], np.inf)
     return idx, margin
+
+
+def selection_scores(g, b_select64=None):
+    """Scores the experts are ranked by: the logits, plus a per-expert bias when
+    one is given.  The bias only decides which experts are chosen; the routing
+    weights still come from softmax(g).  [LH "The central problem: load
+    balancing", auxiliary-loss-free balancing: per-expert bias terms]"""
+    return g if b_select64 is None else g + b_select64[None, :]
+
+
+def router_z_loss(g):
+    """z = mean over tokens of (log sum_e exp g_te)^2, the squared log-partition
+    of the router logits.  [LH "The central problem: load balancing", router
+    z-loss: a penalty on large router logits]"""
+    m = g.max(axis=-1, keepdims=True)
+    lse = (m + np.log(np.exp(g - m).sum(axis=-1, keepdims=True)))[:, 0]
+    return float(np.mean(lse * lse))
 
 
 def routing_weights(p, idx, renormalize):
@@ -197,14 +218,15 @@ def route(inputs, desc):
     x64 = widen(inputs["x"])
     g = router_logits(x64, widen(inputs["w_router"]), widen(inputs.get("b_router")))
     p = softmax(g)
-    idx, margin = topk_by_logit(g, desc["top_k"])
+    idx, margin = topk_by_logit(selection_scores(g, widen(inputs.get("b_select"))), desc["top_k"])
     w = routing_weights(p, idx, desc["renormalize"])
     keep = capacity_keep(idx, desc["n_experts"], desc.get("capacity", 0))
     counts, offsets, dest, src = dispatch_layout(idx, keep, desc["n_experts"])
     aux, f, P, top1 = aux_loss(idx, p, desc["n_experts"])
     return {"logits": g, "probs": p, "topk_idx": idx, "topk_w": w, "margin": margin,
             "keep": keep, "counts": counts, "offsets": offsets, "dest": dest, "src": src,
-            "aux": aux, "f": f, "P": P, "top1_count": top1, "x64": x64}
+            "aux": aux, "f": f, "P": P, "top1_count": top1, "z_loss": router_z_loss(g),
+            "x64": x64}
 
 
 def forward(inputs, desc, tokens=None, chunk_rows=4096, check_margin=True):

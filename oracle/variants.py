@@ -12,7 +12,8 @@ bench's CPU baseline leg only).
 
 Neither calls the oracle module.  Both follow the same readings of the pages as
 the oracle (see its header): lower index wins ties, slot-order combination,
-exact-erf GELU, top-1 fractions before capacity for the aux loss.
+exact-erf GELU, top-1 fractions before capacity for the aux loss, a selection
+bias that only ranks, z-loss as the mean squared log-sum-exp of the logits.
 """
 from __future__ import annotations
 
@@ -41,9 +42,12 @@ def dense_masked(inputs, desc):
     gmax = g.max(axis=1, keepdims=True)
     ex = np.exp(g - gmax)
     p = ex / ex.sum(axis=1, keepdims=True)
-    # rank[t,e] = #experts strictly better than e (higher logit, or equal logit and lower index)
-    better = (g[:, None, :] > g[:, :, None]) | \
-             ((g[:, None, :] == g[:, :, None]) & (np.arange(E)[None, None, :] < np.arange(E)[None, :, None]))
+    lse = gmax[:, 0] + np.log(ex.sum(axis=1))
+    z_loss = float(np.mean(lse ** 2))
+    sc = g if inputs.get("b_select") is None else g + _wide(inputs["b_select"])[None, :]
+    # rank[t,e] = #experts strictly better than e (higher score, or equal score and lower index)
+    better = (sc[:, None, :] > sc[:, :, None]) | \
+             ((sc[:, None, :] == sc[:, :, None]) & (np.arange(E)[None, None, :] < np.arange(E)[None, :, None]))
     rank = better.sum(axis=2)                              # [T,E]
     mask = rank < k
     wsel = np.where(mask, p, 0.0)
@@ -69,7 +73,7 @@ def dense_masked(inputs, desc):
     f = np.bincount(top1, minlength=E) / T
     P = p.mean(axis=0)
     aux = E * float(np.sum(f * P))
-    return {"y": y, "aux": aux, "mask": mask, "rank": rank}
+    return {"y": y, "aux": aux, "mask": mask, "rank": rank, "z_loss": z_loss}
 
 
 def _erf_py(z):
@@ -86,12 +90,13 @@ def loops(inputs, desc):
     X = wide_list(inputs["x"])
     WR = wide_list(inputs["w_router"])
     BR = wide_list(inputs.get("b_router"))
+    BS = wide_list(inputs.get("b_select"))
     W1, W2 = wide_list(inputs["w1"]), wide_list(inputs["w2"])
     B1, B2 = wide_list(inputs.get("b1")), wide_list(inputs.get("b2"))
     E, k, C = desc["n_experts"], desc["top_k"], desc.get("capacity", 0)
     d, F = desc["d_model"], desc["d_ff"]
     T = len(X)
-    ys, top1s, probs_all = [], [], []
+    ys, top1s, probs_all, lses = [], [], [], []
     taken = [0] * E
     for t in range(T):
         g = []
@@ -107,13 +112,15 @@ def loops(inputs, desc):
         tot = sum(ex)
         p = [v / tot for v in ex]
         probs_all.append(p)
+        lses.append(m + math.log(tot))
+        sc = [g[e] + (BS[e] if BS is not None else 0.0) for e in range(E)]
         chosen = []
         for _ in range(k):                      # repeated argmax, first (lowest) index wins ties
             best = None
             for e in range(E):
                 if e in chosen:
                     continue
-                if best is None or g[e] > g[best]:
+                if best is None or sc[e] > sc[best]:
                     best = e
             chosen.append(best)
         top1s.append(chosen[0])
@@ -139,4 +146,5 @@ def loops(inputs, desc):
     f_frac = [sum(1 for t in range(T) if top1s[t] == e) / T for e in range(E)]
     P = [sum(probs_all[t][e] for t in range(T)) / T for e in range(E)]
     aux = E * sum(f_frac[e] * P[e] for e in range(E))
-    return {"y": np.array(ys), "aux": aux, "top1": top1s}
+    z_loss = sum(v * v for v in lses) / T
+    return {"y": np.array(ys), "aux": aux, "top1": top1s, "z_loss": z_loss}

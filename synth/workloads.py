@@ -13,6 +13,7 @@ Layouts (row-major, nn.Linear ``[out][in]`` for weights):
   x          [T][d]                  f32 or bf16
   w_router   [E][d]                  f32 or bf16
   b_router   [E]                     f32 (only for the skewed workloads) or None
+  b_select   [E]                     f32 selection-only bias (workloads that ask for it) or None
   w1         [E][d_ff][d]            f32 or bf16
   b1         [E][d_ff]               f32 or bf16, or None
   w2         [E][d][d_ff]            f32 or bf16
@@ -42,6 +43,7 @@ from concurrent.futures import ThreadPoolExecutor
 import numpy as np
 
 STREAM_X, STREAM_WR, STREAM_W1, STREAM_B1, STREAM_W2, STREAM_B2, STREAM_REDRAW = range(7)
+STREAM_BSEL = 8             # per-expert selection bias (stream 7 is the calibration sample)
 
 _PARAMS_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "input_params.json")
 
@@ -62,6 +64,7 @@ class Workload:
     dtype: str             # "f32" or "bf16"
     router_bias: bool = False  # fp32 logit bias drawn by calibration (skewed workloads)
     seed: int = 0
+    selection_bias: bool = False  # fp32 per-expert bias added to the scores used to pick experts
 
     def with_(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -131,6 +134,13 @@ def draw_x_rows(spec: Workload, redraw: dict | None) -> np.ndarray:
     return x
 
 
+def make_selection_bias(spec: Workload) -> np.ndarray:
+    """Per-expert selection bias, U(-1, 1) in fp32 (router logits are ~N(0, 1),
+    so it changes a fair share of the choices)."""
+    u = _rng(spec.seed, STREAM_BSEL).random(spec.n_experts, dtype=np.float32)
+    return u * np.float32(2.0) - np.float32(1.0)
+
+
 def make_router(spec: Workload) -> np.ndarray:
     return _store(_normal((spec.seed, STREAM_WR), (spec.n_experts, spec.d_model),
                           1.0 / np.sqrt(spec.d_model)), spec.dtype)
@@ -181,6 +191,7 @@ def make_inputs(spec: Workload, redraw: dict | None = None, router_bias=None,
         "x": make_x(spec, redraw),
         "w_router": make_router(spec),
         "b_router": None if router_bias is None else np.asarray(router_bias, np.float32),
+        "b_select": make_selection_bias(spec) if spec.selection_bias else None,
     }
     if with_experts:
         out.update(make_expert_bank(spec))

@@ -30,6 +30,11 @@ SMALL = {
     "topk_eq_e_bf16": Workload("topk_eq_e_bf16", 70, 256, 256, 4, 4, True, 0, True, "bf16"),
     "single_token_bf16": Workload("single_token_bf16", 1, 256, 512, 8, 2, True, 0, True, "bf16"),
     "capacity_one_bf16": Workload("capacity_one_bf16", 64, 128, 256, 8, 1, True, 1, True, "bf16"),
+    # selection-only per-expert bias (and the z-loss, computed for every shape)
+    "select_bias_bf16": Workload("select_bias_bf16", 300, 256, 512, 16, 4, True, 0, True, "bf16",
+                                 selection_bias=True),
+    "select_bias_top1_fp32": Workload("select_bias_top1_fp32", 90, 128, 256, 8, 1, False, 0, True,
+                                      "f32", selection_bias=True),
 }
 
 
@@ -44,13 +49,14 @@ def small_router_bias(spec):
 
 
 def repair(spec, router_bias=None, max_rounds=50):
-    """Redraw token rows until every top-k logit margin exceeds 1e-3."""
+    """Redraw token rows until every top-k margin of the selection scores exceeds 1e-3."""
     wr64 = O.widen(W.make_router(spec))
     b64 = None if router_bias is None else np.asarray(router_bias, np.float32).astype(np.float64)
+    bs64 = O.widen(W.make_selection_bias(spec)) if spec.selection_bias else None
     redraw = {}
     for _ in range(max_rounds):
         g = O.router_logits(O.widen(W.make_x(spec, redraw)), wr64, b64)
-        _, margin = O.topk_by_logit(g, spec.top_k)
+        _, margin = O.topk_by_logit(O.selection_scores(g, bs64), spec.top_k)
         bad = np.flatnonzero(margin <= O.MARGIN_MIN)
         if bad.size == 0:
             return redraw

@@ -6,11 +6,14 @@ least one of them.
 """
 from __future__ import annotations
 
+import functools
+
 import numpy as np
 import pytest
 
 from oracle import moe_oracle as O
 from tests import test_oracle_pins as P
+from tests import test_oracle_router_extras as RX
 
 
 def _tanh_gelu(z):
@@ -66,6 +69,19 @@ def _ffn_transposed(rows64, w1e, b1e, w2e, b2e):
     return o + (b2e[None, :] if b2e is not None else 0)
 
 
+def _z_no_square(g):
+    m = g.max(axis=-1, keepdims=True)
+    return float(np.mean(m[:, 0] + np.log(np.exp(g - m).sum(axis=-1))))
+
+
+def _selection_ignores_bias(g, b_select64=None):
+    return g
+
+
+def _selection_subtracts_bias(g, b_select64=None):
+    return g if b_select64 is None else g - b_select64[None, :]
+
+
 MUTATIONS = [
     ("gelu_erf", _tanh_gelu, [P.test_gelu_against_math_erf_and_identities,
                               P.test_single_expert_reduces_to_dense_mlp]),
@@ -75,6 +91,12 @@ MUTATIONS = [
     ("aux_loss", _aux_all_slots, [P.test_oracle_matches_listing_structure_toy]),
     ("expert_ffn", _ffn_no_out_bias, [P.test_single_expert_reduces_to_dense_mlp]),
     ("expert_ffn", _ffn_transposed, [P.test_oracle_matches_listing_structure_toy]),
+    ("router_z_loss", _z_no_square, [functools.partial(RX.test_z_loss_of_equal_logits_is_log_E_squared, 8),
+                                     RX.test_z_loss_of_one_hot_logits]),
+    ("selection_scores", _selection_ignores_bias,
+     [RX.test_dominant_selection_bias_picks_expert_with_unbiased_weights]),
+    ("selection_scores", _selection_subtracts_bias,
+     [RX.test_dominant_selection_bias_picks_expert_with_unbiased_weights]),
 ]
 
 
