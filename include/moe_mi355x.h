@@ -110,6 +110,11 @@ typedef struct moe_weights {
   const void* b1;          /* [E][F]    dtype, NULL iff !has_expert_bias */
   const void* w2;          /* [E][d][F] dtype */
   const void* b2;          /* [E][d]    dtype, NULL iff !has_expert_bias */
+  const float* b_select;   /* [E]       fp32 selection-only bias, or NULL: experts are ranked by
+                              logit + b_select, the routing weights stay softmax(logits)
+                              (web page "Mixture of Experts: Scaling Parameters Without Scaling
+                              Compute", section "The central problem: load balancing",
+                              auxiliary-loss-free balancing) */
 } moe_weights;
 
 /* Routing results (device pointers).  Which fields a call reads or writes is
@@ -124,6 +129,9 @@ typedef struct moe_routing {
   int32_t* src;            /* [T*k]  rows < R hold the assignment id t*k+s; rows >= R are not written */
   int32_t* top1_count;     /* [E]    tokens whose first choice is e, before capacity (defines f_e) */
   float* prob_mean;        /* [E]    P_e = mean over tokens of p_e */
+  float* z_loss;           /* [1]    router z-loss: mean over tokens of (log sum_e exp logit_e)^2
+                              (same page and section, router z-loss); logits include b_router,
+                              not b_select */
 } moe_routing;
 
 /* Status code -> static string. */
@@ -139,11 +147,11 @@ int moe_workspace_size(const moe_desc* desc, size_t* bytes);
 /* Resolve the descriptor's AUTO choices (host output). */
 int moe_query_plan(const moe_desc* desc, moe_plan* plan);
 
-/* Router: logits = x W_r^T (+ b_router), softmax, top-k by logit, routing
- * weights, and the aux loss.
+/* Router: logits = x W_r^T (+ b_router), softmax, top-k by logit (+ b_select
+ * when given), routing weights, the aux loss and the router z-loss.
  *   x [T][d] dtype.  Writes out->topk_idx and out->topk_w (both required),
- *   out->top1_count and out->prob_mean (each optional), and *aux (device fp32
- *   scalar, optional): aux = E * sum_e (top1_count_e / T) * P_e. */
+ *   out->top1_count, out->prob_mean and out->z_loss (each optional), and *aux
+ *   (device fp32 scalar, optional): aux = E * sum_e (top1_count_e / T) * P_e. */
 int moe_route(const moe_desc* desc, const void* x, const moe_weights* w, moe_routing* out,
               float* aux, void* workspace, size_t workspace_bytes, void* stream);
 

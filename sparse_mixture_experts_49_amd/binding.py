@@ -43,13 +43,14 @@ class CPlan(ctypes.Structure):
 
 
 class CWeights(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in ("w_router", "b_router", "w1", "b1", "w2", "b2")]
+    _fields_ = [(n, ctypes.c_void_p) for n in ("w_router", "b_router", "w1", "b1", "w2", "b2",
+                                               "b_select")]
 
 
 class CRouting(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("topk_idx", "topk_w", "counts", "offsets", "dest", "src", "top1_count",
-                 "prob_mean")]
+                 "prob_mean", "z_loss")]
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -119,9 +120,10 @@ class Weights:
     b_router: Optional[torch.Tensor] = None
     b1: Optional[torch.Tensor] = None
     b2: Optional[torch.Tensor] = None
+    b_select: Optional[torch.Tensor] = None
 
     def to_c(self) -> CWeights:
-        return CWeights(*(_ptr(getattr(self, n)) for n in ("w_router", "b_router", "w1", "b1", "w2", "b2")))
+        return CWeights(*(_ptr(getattr(self, n)) for n, _ in CWeights._fields_))
 
 
 @dataclasses.dataclass
@@ -134,6 +136,7 @@ class Routing:
     src: Optional[torch.Tensor] = None
     top1_count: Optional[torch.Tensor] = None
     prob_mean: Optional[torch.Tensor] = None
+    z_loss: Optional[torch.Tensor] = None
 
     @classmethod
     def allocate(cls, desc: Desc, device) -> "Routing":
@@ -144,7 +147,8 @@ class Routing:
                    counts=torch.empty(E, **i32), offsets=torch.empty(E + 1, **i32),
                    dest=torch.empty(T, k, **i32), src=torch.empty(T * k, **i32),
                    top1_count=torch.empty(E, **i32),
-                   prob_mean=torch.empty(E, dtype=torch.float32, device=device))
+                   prob_mean=torch.empty(E, dtype=torch.float32, device=device),
+                   z_loss=torch.empty(1, dtype=torch.float32, device=device))
 
     def to_c(self) -> CRouting:
         return CRouting(*(_ptr(getattr(self, f.name)) for f in dataclasses.fields(self)))

@@ -127,6 +127,7 @@ int validate_weights(const moe_desc* d, const moe_weights* w, bool router, bool 
   if (router) {
     MOE_REQUIRE_PTR(w->w_router, "w_router");
     MOE_OPTIONAL_PTR(w->b_router, "b_router");
+    MOE_OPTIONAL_PTR(w->b_select, "b_select");
   }
   if (experts) {
     MOE_REQUIRE_PTR(w->w1, "w1");
@@ -145,7 +146,7 @@ size_t elem_bytes(const moe_desc* d) { return d->dtype == MOE_DTYPE_BF16 ? 2 : 4
 
 // Workspace carving: every region starts on a 256-byte boundary.
 struct Layout {
-  size_t part_psum, part_top1, blk_hist, blk_base;
+  size_t part_psum, part_top1, part_z, blk_hist, blk_base;
   size_t topk_idx, topk_w, counts, offsets, dest, src, top1, prob_mean;
   size_t x_perm, h, o, partial;
   size_t total;
@@ -162,6 +163,7 @@ Layout layout_of(const moe_desc* d) {
   auto take = [&](size_t bytes) { size_t at = p; p += up256(bytes); return at; };
   L.part_psum = take(rb * E * sizeof(double));
   L.part_top1 = take(rb * E * sizeof(int32_t));
+  L.part_z = take(rb * sizeof(double));
   L.blk_hist = take(pb * E * sizeof(int32_t));
   L.blk_base = take(pb * E * sizeof(int32_t));
   L.topk_idx = take(A * 4);
@@ -214,13 +216,14 @@ int hip_status(hipError_t e, const char* what) {
 }
 
 int launch_route(const moe_desc* d, const void* x, const moe_weights* w, int32_t* idx, float* wt,
-                 int32_t* top1, float* pmean, float* aux, const Layout& L, void* ws,
+                 int32_t* top1, float* pmean, float* aux, float* zl, const Layout& L, void* ws,
                  hipStream_t s) {
   moe::RouterArgs a{};
   a.bf16 = d->dtype == MOE_DTYPE_BF16;
   a.x = x;
   a.w_router = w->w_router;
   a.b_router = w->b_router;
+  a.b_select = w->b_select;
   a.T = d->tokens;
   a.d = d->d_model;
   a.E = d->n_experts;
@@ -230,9 +233,11 @@ int launch_route(const moe_desc* d, const void* x, const moe_weights* w, int32_t
   a.topk_w = wt;
   a.part_psum = at<double>(ws, L.part_psum);
   a.part_top1 = at<int32_t>(ws, L.part_top1);
+  a.part_z = at<double>(ws, L.part_z);
   a.top1_count = top1;
   a.prob_mean = pmean;
   a.aux = aux;
+  a.z_loss = zl;
   return hip_status(moe::launch_router(a, s), "router launch");
 }
 
@@ -336,10 +341,11 @@ int moe_route(const moe_desc* desc, const void* x, const moe_weights* w, moe_rou
   MOE_REQUIRE_PTR(out->topk_w, "out->topk_w");
   MOE_OPTIONAL_PTR(out->top1_count, "out->top1_count");
   MOE_OPTIONAL_PTR(out->prob_mean, "out->prob_mean");
+  MOE_OPTIONAL_PTR(out->z_loss, "out->z_loss");
   Layout L;
   if (int st = check_ws(desc, ws, ws_bytes, L)) return st;
   return launch_route(desc, x, w, out->topk_idx, out->topk_w, out->top1_count, out->prob_mean,
-                      aux, L, ws, static_cast<hipStream_t>(stream));
+                      aux, out->z_loss, L, ws, static_cast<hipStream_t>(stream));
 }
 
 int moe_permute(const moe_desc* desc, const void* x, moe_routing* r, void* x_perm, void* ws,
@@ -426,6 +432,7 @@ int moe_forward(const moe_desc* desc, const void* x, const moe_weights* w, float
     MOE_OPTIONAL_PTR(r.src, "routing->src");
     MOE_OPTIONAL_PTR(r.top1_count, "routing->top1_count");
     MOE_OPTIONAL_PTR(r.prob_mean, "routing->prob_mean");
+    MOE_OPTIONAL_PTR(r.z_loss, "routing->z_loss");
   }
   Layout L;
   if (int st = check_ws(desc, ws, ws_bytes, L)) return st;
@@ -439,8 +446,8 @@ int moe_forward(const moe_desc* desc, const void* x, const moe_weights* w, float
   void* x_perm = at<void>(ws, L.x_perm);
   void* h = at<void>(ws, L.h);
   float* o = at<float>(ws, L.o);
-  if (int st = launch_route(desc, x, w, r.topk_idx, r.topk_w, r.top1_count, r.prob_mean, aux, L,
-                            ws, s))
+  if (int st = launch_route(desc, x, w, r.topk_idx, r.topk_w, r.top1_count, r.prob_mean, aux,
+                            r.z_loss, L, ws, s))
     return st;
   if (int st = launch_perm(desc, x, r.topk_idx, r.counts, r.offsets, r.dest, r.src, x_perm, L, ws,
                            s))

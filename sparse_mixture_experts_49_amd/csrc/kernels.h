@@ -11,14 +11,17 @@ struct RouterArgs {
   const void* x;
   const void* w_router;
   const float* b_router;
+  const float* b_select;   // selection-only bias or null
   int T, d, E, k, renorm;
   int32_t* topk_idx;
   float* topk_w;
   double* part_psum;       // [router_blocks(T)][E]
   int32_t* part_top1;      // [router_blocks(T)][E]
+  double* part_z;          // [router_blocks(T)]
   int32_t* top1_count;     // optional
   float* prob_mean;        // optional
   float* aux;              // optional
+  float* z_loss;           // optional
 };
 int router_blocks(int T);
 hipError_t launch_router(const RouterArgs& a, hipStream_t s);

@@ -8,7 +8,11 @@
 // tokens whose first choice is i and P_i the mean router probability.
 //
 // Ranking is by logit (softmax is monotone), descending; equal logits go to
-// the lower expert index, the order a stable descending sort gives.
+// the lower expert index, the order a stable descending sort gives.  An
+// optional per-expert selection bias is added to the ranking scores only
+// (same page and section: auxiliary-loss-free balancing); the weights stay the
+// unbiased probabilities.  The router z-loss is the mean over tokens of the
+// squared log-sum-exp of the logits (same section: router z-loss).
 #include "device_common.h"
 #include "kernels.h"
 
@@ -30,9 +34,9 @@ constexpr int kRouterWaves = 4;     // the block's waves split d between them
 template <typename T, int NT>
 __global__ __launch_bounds__(256) void router_kernel(
     const T* __restrict__ x, const T* __restrict__ wr, const float* __restrict__ br,
-    int T_, int d, int E, int k, int renorm,
+    const float* __restrict__ bsel, int T_, int d, int E, int k, int renorm,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
-    double* __restrict__ part_psum, int32_t* __restrict__ part_top1) {
+    double* __restrict__ part_psum, int32_t* __restrict__ part_top1, double* __restrict__ part_z) {
   constexpr int kPerLane = 64 / sizeof(T);          // elements per lane per chunk
   constexpr int kChunk = 4 * kPerLane;              // 128 bf16 or 64 fp32
   constexpr int kPerVec = 16 / sizeof(T);
@@ -40,6 +44,7 @@ __global__ __launch_bounds__(256) void router_kernel(
   __shared__ float red[kRouterWaves][kRouterTokens][65];
   __shared__ float prob[kRouterTokens][64];
   __shared__ int top1[kRouterTokens];
+  __shared__ float lse[kRouterTokens];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, c = lane >> 4;
@@ -87,7 +92,7 @@ __global__ __launch_bounds__(256) void router_kernel(
     const int tq = lane >> 2, q = lane & 3;
     const int t = t0 + tq;
     constexpr int kMaxPer = 16;
-    float g[kMaxPer], p[kMaxPer];
+    float g[kMaxPer], p[kMaxPer], sc[kMaxPer];
     float m = -INFINITY;
 #pragma unroll
     for (int j = 0; j < kMaxPer; ++j) {
@@ -111,7 +116,12 @@ __global__ __launch_bounds__(256) void router_kernel(
     s += __shfl_xor(s, 2);
     const float inv = 1.0f / s;
 #pragma unroll
-    for (int j = 0; j < kMaxPer; ++j) p[j] *= inv;
+    for (int j = 0; j < kMaxPer; ++j) {
+      p[j] *= inv;
+      const int e = q + 4 * j;
+      sc[j] = (bsel && e < E) ? g[j] + bsel[e] : g[j];   // ranking scores
+    }
+    if (q == 0) lse[tq] = m + logf(s);
 
     // top-k: k rounds of a quad-wide argmax over the unselected logits.
     uint32_t taken = 0;
@@ -127,8 +137,8 @@ __global__ __launch_bounds__(256) void router_kernel(
 #pragma unroll
         for (int j = 0; j < kMaxPer; ++j) {
           const int e = q + 4 * j;
-          if (e < E && !((taken >> j) & 1u) && (g[j] > bv || be == 0x7fffffff)) {
-            bv = g[j];
+          if (e < E && !((taken >> j) & 1u) && (sc[j] > bv || be == 0x7fffffff)) {
+            bv = sc[j];
             be = e;
             bp = p[j];
           }
@@ -185,21 +195,27 @@ __global__ __launch_bounds__(256) void router_kernel(
     part_psum[(size_t)blockIdx.x * E + e] = ps;
     part_top1[(size_t)blockIdx.x * E + e] = cnt;
   }
+  if (threadIdx.x == 64) {                           // z-loss partial, token order
+    double z = 0.0;
+    for (int i = 0; i < kRouterTokens && t0 + i < T_; ++i) z += (double)lse[i] * (double)lse[i];
+    part_z[blockIdx.x] = z;
+  }
 }
 
 // Fixed-order reduction of the router partials: f, P and aux (web page
 // "Mixture of Experts: Scaling Parameters Without Scaling Compute", section
 // "The central problem: load balancing").
 __global__ __launch_bounds__(kAuxThreads) void aux_finalize_kernel(
-    const double* __restrict__ part_psum, const int32_t* __restrict__ part_top1, int nblk,
-    int T_, int E, int32_t* __restrict__ top1_count, float* __restrict__ prob_mean,
-    float* __restrict__ aux) {
+    const double* __restrict__ part_psum, const int32_t* __restrict__ part_top1,
+    const double* __restrict__ part_z, int nblk, int T_, int E, int32_t* __restrict__ top1_count,
+    float* __restrict__ prob_mean, float* __restrict__ aux, float* __restrict__ z_loss) {
   // The partials are [nblk][E] laid out flat.  Thread t < stride (a multiple of
   // E) sums entries t, t + stride, ... (all of expert t % E, coalesced across
   // the block); expert e's per-thread sums are then added in thread order.
   // The grouping depends only on (nblk, E), so the result is deterministic.
   __shared__ double ps[kAuxThreads];
   __shared__ long long pc[kAuxThreads];
+  __shared__ double pz[kAuxThreads];
   __shared__ double fP[64];
   const int t = threadIdx.x;
   const int stride = (kAuxThreads / E) * E;
@@ -213,6 +229,9 @@ __global__ __launch_bounds__(kAuxThreads) void aux_finalize_kernel(
     }
   ps[t] = sum;
   pc[t] = cnt;
+  double zs = 0.0;                                   // z-loss: block partials t, t + threads, ...
+  for (int b = t; b < nblk; b += kAuxThreads) zs += part_z[b];
+  pz[t] = zs;
   __syncthreads();
   if (t < E) {
     double S = 0.0;
@@ -232,6 +251,11 @@ __global__ __launch_bounds__(kAuxThreads) void aux_finalize_kernel(
     for (int i = 0; i < E; ++i) acc += fP[i];
     *aux = (float)((double)E * acc);
   }
+  if (t == 64 && z_loss) {
+    double zt = 0.0;
+    for (int u = 0; u < kAuxThreads; ++u) zt += pz[u];
+    *z_loss = (float)(zt / (double)T_);
+  }
 }
 
 template <typename T>
@@ -242,9 +266,9 @@ static hipError_t launch_router_t(const RouterArgs& a, hipStream_t s) {
   const T* wr = static_cast<const T*>(a.w_router);
 #define MOE_ROUTER_CASE(NT)                                                                   \
   case NT:                                                                                  \
-    router_kernel<T, NT><<<nblk, 256, 0, s>>>(x, wr, a.b_router, a.T, a.d, a.E, a.k,       \
-                                               a.renorm, a.topk_idx, a.topk_w, a.part_psum, \
-                                               a.part_top1);                                \
+    router_kernel<T, NT><<<nblk, 256, 0, s>>>(x, wr, a.b_router, a.b_select, a.T, a.d, a.E, \
+                                               a.k, a.renorm, a.topk_idx, a.topk_w,         \
+                                               a.part_psum, a.part_top1, a.part_z);         \
     break;
   switch (nt) {
     MOE_ROUTER_CASE(1)
@@ -256,8 +280,8 @@ static hipError_t launch_router_t(const RouterArgs& a, hipStream_t s) {
 #undef MOE_ROUTER_CASE
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  aux_finalize_kernel<<<1, kAuxThreads, 0, s>>>(a.part_psum, a.part_top1, nblk, a.T, a.E, a.top1_count,
-                                        a.prob_mean, a.aux);
+  aux_finalize_kernel<<<1, kAuxThreads, 0, s>>>(a.part_psum, a.part_top1, a.part_z, nblk, a.T, a.E,
+                                                a.top1_count, a.prob_mean, a.aux, a.z_loss);
   return hipGetLastError();
 }
 

@@ -31,7 +31,8 @@ def desc_for(spec, path=moe.MOE_FFN_AUTO, h_mode=moe.MOE_H_AUTO):
 def weights_for(inp, dev=DEV):
     return moe.Weights(w_router=to_dev(inp["w_router"], dev), w1=to_dev(inp["w1"], dev),
                        w2=to_dev(inp["w2"], dev), b_router=to_dev(inp.get("b_router"), dev),
-                       b1=to_dev(inp.get("b1"), dev), b2=to_dev(inp.get("b2"), dev))
+                       b1=to_dev(inp.get("b1"), dev), b2=to_dev(inp.get("b2"), dev),
+                       b_select=to_dev(inp.get("b_select"), dev))
 
 
 def tol_for(spec):

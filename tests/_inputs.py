@@ -35,6 +35,9 @@ SMALL = {
                                  selection_bias=True),
     "select_bias_top1_fp32": Workload("select_bias_top1_fp32", 90, 128, 256, 8, 1, False, 0, True,
                                       "f32", selection_bias=True),
+    # the mid-size layer's shapes (4096 tokens, 16 experts) with a selection bias
+    "mid_select_bias_bf16": Workload("mid_select_bias_bf16", 4096, 1024, 4096, 16, 2, True, 0, True,
+                                     "bf16", selection_bias=True),
 }
 
 

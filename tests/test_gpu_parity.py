@@ -52,6 +52,7 @@ def test_route(name):
     assert np.array_equal(r.top1_count.cpu().numpy(), ref["top1_count"])
     assert G.rel_err(r.prob_mean.cpu().numpy(), ref["P"]) <= G.TOL_W
     assert abs(aux.item() - ref["aux"]) <= G.TOL_AUX * abs(ref["aux"])
+    assert abs(r.z_loss.item() - ref["z_loss"]) <= G.TOL_AUX * abs(ref["z_loss"])
 
 
 def test_route_eight_expert_example():
@@ -195,6 +196,7 @@ def _check_forward(spec, inp, y, aux, r, tokens=None):
     assert np.array_equal(r.dest.cpu().numpy(), ref["dest"])
     assert G.rel_err(r.topk_w.cpu().numpy(), ref["topk_w"]) <= G.TOL_W
     assert abs(aux.item() - ref["aux"]) <= G.TOL_AUX * abs(ref["aux"])
+    assert abs(r.z_loss.item() - ref["z_loss"]) <= G.TOL_AUX * abs(ref["z_loss"])
     err = G.err_over_rms(y.cpu().numpy()[sel], ref["y"])
     assert err <= G.tol_for(spec), err
     return err
@@ -280,3 +282,19 @@ def test_gelu_accuracy_through_first_product():
     got = h.cpu().numpy().astype(np.float64)
     # erf to 1.5e-7 (Abramowitz & Stegun 7.1.26) plus fp32 rounding of z/sqrt2 and the products
     assert np.all(np.abs(got - ref) <= 2e-7 * np.abs(z) + 2e-7 * np.abs(ref) + 1e-12)
+
+
+def test_selection_bias_changes_choices_not_weights():
+    """With a selection bias the GPU ranks by logit + bias but weights by the
+    unbiased softmax: compared with the same layer without the bias, some
+    choices differ, and every weight equals the oracle's unbiased probability
+    of the expert chosen (renormalised)."""
+    spec, inp = inputs_for("select_bias_bf16")
+    ref = O.route(inp, O.desc_of(spec))
+    _, _, _, r, _, _ = _route_gpu(spec, inp)
+    unbiased = O.route(dict(inp, b_select=None), O.desc_of(spec))
+    idx = r.topk_idx.cpu().numpy()
+    assert np.array_equal(idx, ref["topk_idx"])
+    assert not np.array_equal(idx, unbiased["topk_idx"])
+    p = np.take_along_axis(ref["probs"], idx, axis=1)
+    assert G.rel_err(r.topk_w.cpu().numpy(), p / p.sum(axis=1, keepdims=True)) <= G.TOL_W
