@@ -37,7 +37,9 @@ Readings where the pages are silent or garbled (all listed in the design notes):
     P_i averages the full softmax over all tokens, aux = E * sum_i f_i P_i;
   * capacity (top-1 only) keeps, per expert, the C lowest-index tokens that
     chose it; a dropped token's layer output is 0;
-  * rows of one expert's segment are ordered by token index.
+  * rows of one expert's segment are ordered by token index;
+  * a shared expert (optional) runs on every token, dropped ones included, and
+    its output is added to y after the routed sum, with weight 1.
 """
 from __future__ import annotations
 
@@ -261,9 +263,24 @@ def forward(inputs, desc, tokens=None, chunk_rows=4096, check_margin=True):
     w = r["topk_w"][sel]
     for s in range(k):                    # slot order
         y += np.where(r["keep"][sel][:, s:s + 1], w[:, s:s + 1] * contrib[:, s], 0.0)
+    shared = shared_expert(inputs, x64[sel])
+    if shared is not None:                # added after the routed sum, to every token
+        y += shared
     r["y"] = y
     r["tokens"] = sel
     return r
+
+
+def shared_expert(inputs, x64_rows):
+    """The always-active shared expert on the given token rows: the same
+    Linear-GELU-Linear as a routed expert, with no routing weight.  [LH "Design
+    variations": shared experts, always active]  Several shared experts equal
+    one whose hidden layer is their hidden layers side by side, so one FFN of
+    width d_ff_shared covers them."""
+    if inputs.get("w1_shared") is None:
+        return None
+    return expert_ffn(x64_rows, widen(inputs["w1_shared"]), widen(inputs.get("b1_shared")),
+                      widen(inputs["w2_shared"]), widen(inputs.get("b2_shared")))
 
 
 def expert_outputs(inputs, desc, rows=None):

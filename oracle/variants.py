@@ -13,7 +13,8 @@ bench's CPU baseline leg only).
 Neither calls the oracle module.  Both follow the same readings of the pages as
 the oracle (see its header): lower index wins ties, slot-order combination,
 exact-erf GELU, top-1 fractions before capacity for the aux loss, a selection
-bias that only ranks, z-loss as the mean squared log-sum-exp of the logits.
+bias that only ranks, z-loss as the mean squared log-sum-exp of the logits, a
+shared expert added to every token after the routed sum.
 """
 from __future__ import annotations
 
@@ -70,6 +71,15 @@ def dense_masked(inputs, desc):
         if b2 is not None:
             o = o + _wide(b2[e])[None, :]
         y += np.where(mask[:, e:e + 1], wsel[:, e:e + 1] * o, 0.0)
+    if inputs.get("w1_shared") is not None:
+        hs = x @ _wide(inputs["w1_shared"]).T
+        if inputs.get("b1_shared") is not None:
+            hs = hs + _wide(inputs["b1_shared"])[None, :]
+        hs = hs * 0.5 * (1.0 + _erf_py(hs / math.sqrt(2.0)))
+        os_ = hs @ _wide(inputs["w2_shared"]).T
+        if inputs.get("b2_shared") is not None:
+            os_ = os_ + _wide(inputs["b2_shared"])[None, :]
+        y = y + os_
     f = np.bincount(top1, minlength=E) / T
     P = p.mean(axis=0)
     aux = E * float(np.sum(f * P))
@@ -91,6 +101,8 @@ def loops(inputs, desc):
     WR = wide_list(inputs["w_router"])
     BR = wide_list(inputs.get("b_router"))
     BS = wide_list(inputs.get("b_select"))
+    W1S, W2S = wide_list(inputs.get("w1_shared")), wide_list(inputs.get("w2_shared"))
+    B1S, B2S = wide_list(inputs.get("b1_shared")), wide_list(inputs.get("b2_shared"))
     W1, W2 = wide_list(inputs["w1"]), wide_list(inputs["w2"])
     B1, B2 = wide_list(inputs.get("b1")), wide_list(inputs.get("b2"))
     E, k, C = desc["n_experts"], desc["top_k"], desc.get("capacity", 0)
@@ -142,6 +154,14 @@ def loops(inputs, desc):
             for i in range(d):
                 o = sum(W2[e][i][f] * h[f] for f in range(F)) + (B2[e][i] if B2 else 0.0)
                 y[i] += w[s] * o
+        if W1S is not None:
+            Fs = len(W1S)
+            hs = []
+            for f in range(Fs):
+                a = sum(W1S[f][j] * X[t][j] for j in range(d)) + (B1S[f] if B1S else 0.0)
+                hs.append(0.5 * a * (1.0 + math.erf(a / math.sqrt(2.0))))
+            for i in range(d):
+                y[i] += sum(W2S[i][f] * hs[f] for f in range(Fs)) + (B2S[i] if B2S else 0.0)
         ys.append(y)
     f_frac = [sum(1 for t in range(T) if top1s[t] == e) / T for e in range(E)]
     P = [sum(probs_all[t][e] for t in range(T)) / T for e in range(E)]

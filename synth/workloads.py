@@ -14,6 +14,8 @@ Layouts (row-major, nn.Linear ``[out][in]`` for weights):
   w_router   [E][d]                  f32 or bf16
   b_router   [E]                     f32 (only for the skewed workloads) or None
   b_select   [E]                     f32 selection-only bias (workloads that ask for it) or None
+  w1_shared  [Fs][d], b1_shared [Fs], w2_shared [d][Fs], b2_shared [d]
+                                     the shared expert (workloads with d_ff_shared > 0)
   w1         [E][d_ff][d]            f32 or bf16
   b1         [E][d_ff]               f32 or bf16, or None
   w2         [E][d][d_ff]            f32 or bf16
@@ -44,6 +46,7 @@ import numpy as np
 
 STREAM_X, STREAM_WR, STREAM_W1, STREAM_B1, STREAM_W2, STREAM_B2, STREAM_REDRAW = range(7)
 STREAM_BSEL = 8             # per-expert selection bias (stream 7 is the calibration sample)
+STREAM_W1S, STREAM_B1S, STREAM_W2S, STREAM_B2S = 9, 10, 11, 12   # shared expert
 
 _PARAMS_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "input_params.json")
 
@@ -65,6 +68,7 @@ class Workload:
     router_bias: bool = False  # fp32 logit bias drawn by calibration (skewed workloads)
     seed: int = 0
     selection_bias: bool = False  # fp32 per-expert bias added to the scores used to pick experts
+    d_ff_shared: int = 0          # hidden width of the always-active shared expert (0: none)
 
     def with_(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -87,6 +91,10 @@ WORKLOADS = {
     "switch_capacity_bf16": Workload("switch_capacity_bf16", 8192, 2048, 8192, 64, 1, False,
                                      capacity_for(8192, 64), True, "bf16", router_bias=True),
     "decode_bf16": Workload("decode_bf16", 32, 4096, 14336, 8, 2, True, 0, True, "bf16"),
+    # fine-grained experts (64 experts of width 1408, top-6) plus a shared expert of
+    # width 2816 (two of width 1408 side by side); no router skew
+    "finegrained_shared_bf16": Workload("finegrained_shared_bf16", 8192, 2048, 1408, 64, 6, True, 0,
+                                        False, "bf16", d_ff_shared=2816),
 }
 
 
@@ -173,6 +181,19 @@ def make_expert_bank(spec: Workload, threads: int | None = None) -> dict:
     return {"w1": w1, "b1": b1, "w2": w2, "b2": b2}
 
 
+def make_shared_expert(spec: Workload) -> dict:
+    """The shared expert's weights (same laws as the routed experts; biases iff
+    the routed experts have them)."""
+    d, Fs = spec.d_model, spec.d_ff_shared
+    out = {"w1_shared": _store(_normal((spec.seed, STREAM_W1S), (Fs, d), 1.0 / np.sqrt(d)), spec.dtype),
+           "w2_shared": _store(_normal((spec.seed, STREAM_W2S), (d, Fs), 1.0 / np.sqrt(Fs)), spec.dtype),
+           "b1_shared": None, "b2_shared": None}
+    if spec.expert_bias:
+        out["b1_shared"] = _store(_uniform_bias((spec.seed, STREAM_B1S), (Fs,)), spec.dtype)
+        out["b2_shared"] = _store(_uniform_bias((spec.seed, STREAM_B2S), (d,)), spec.dtype)
+    return out
+
+
 def make_inputs(spec: Workload, redraw: dict | None = None, router_bias=None,
                 with_experts: bool = True, params: dict | None = None) -> dict:
     """All inputs of one layer call.
@@ -195,4 +216,6 @@ def make_inputs(spec: Workload, redraw: dict | None = None, router_bias=None,
     }
     if with_experts:
         out.update(make_expert_bank(spec))
+        if spec.d_ff_shared:
+            out.update(make_shared_expert(spec))
     return out

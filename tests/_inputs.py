@@ -35,6 +35,14 @@ SMALL = {
                                  selection_bias=True),
     "select_bias_top1_fp32": Workload("select_bias_top1_fp32", 90, 128, 256, 8, 1, False, 0, True,
                                       "f32", selection_bias=True),
+    # fine-grained routing (32 experts, top-6) plus a shared expert
+    "shared_fine_bf16": Workload("shared_fine_bf16", 500, 256, 256, 32, 6, True, 0, True, "bf16",
+                                 d_ff_shared=512),
+    # top-1 with capacity: dropped tokens still get the shared expert
+    "shared_capacity_bf16": Workload("shared_capacity_bf16", 300, 256, 512, 16, 1, True,
+                                     W.capacity_for(300, 16), True, "bf16", router_bias=True,
+                                     d_ff_shared=256),
+    "shared_fp32": Workload("shared_fp32", 60, 128, 256, 8, 2, True, 0, True, "f32", d_ff_shared=384),
     # the mid-size layer's shapes (4096 tokens, 16 experts) with a selection bias
     "mid_select_bias_bf16": Workload("mid_select_bias_bf16", 4096, 1024, 4096, 16, 2, True, 0, True,
                                      "bf16", selection_bias=True),

@@ -14,6 +14,7 @@ import pytest
 from oracle import moe_oracle as O
 from tests import test_oracle_pins as P
 from tests import test_oracle_router_extras as RX
+from tests import test_oracle_shared_experts as SX
 
 
 def _tanh_gelu(z):
@@ -82,6 +83,13 @@ def _selection_subtracts_bias(g, b_select64=None):
     return g if b_select64 is None else g - b_select64[None, :]
 
 
+def _shared_half(inputs, x64_rows):
+    r = O.expert_ffn(x64_rows, O.widen(inputs["w1_shared"]), O.widen(inputs.get("b1_shared")),
+                     O.widen(inputs["w2_shared"]), O.widen(inputs.get("b2_shared"))) \
+        if inputs.get("w1_shared") is not None else None
+    return None if r is None else 0.5 * r
+
+
 MUTATIONS = [
     ("gelu_erf", _tanh_gelu, [P.test_gelu_against_math_erf_and_identities,
                               P.test_single_expert_reduces_to_dense_mlp]),
@@ -97,6 +105,8 @@ MUTATIONS = [
      [RX.test_dominant_selection_bias_picks_expert_with_unbiased_weights]),
     ("selection_scores", _selection_subtracts_bias,
      [RX.test_dominant_selection_bias_picks_expert_with_unbiased_weights]),
+    ("shared_expert", _shared_half, [SX.test_shared_expert_is_added_with_weight_one,
+                                     SX.test_dropped_token_keeps_the_shared_expert]),
 ]
 
 
