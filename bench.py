@@ -129,11 +129,12 @@ def run(args):
     dev = "cuda:0"
     inp = synth.make_inputs(spec)
     desc = moe.Desc(spec.tokens, spec.d_model, spec.d_ff, spec.n_experts, spec.top_k,
-                    spec.renormalize, spec.capacity, spec.dtype, spec.expert_bias)
+                    spec.renormalize, spec.capacity, spec.dtype, spec.expert_bias,
+                    d_ff_shared=spec.d_ff_shared)
     x = _to_dev(inp["x"], dev)
-    w = moe.Weights(w_router=_to_dev(inp["w_router"], dev), w1=_to_dev(inp["w1"], dev),
-                    w2=_to_dev(inp["w2"], dev), b_router=_to_dev(inp["b_router"], dev),
-                    b1=_to_dev(inp["b1"], dev), b2=_to_dev(inp["b2"], dev))
+    w = moe.Weights(**{name: _to_dev(inp.get(name), dev) for name in (
+        "w_router", "w1", "w2", "b_router", "b1", "b2", "b_select", "w1_shared", "b1_shared",
+        "w2_shared", "b2_shared")})
     ws = moe.alloc_workspace(desc, dev)
     y = torch.empty(spec.tokens, spec.d_model, dtype=torch.float32, device=dev)
     aux = torch.empty((), dtype=torch.float32, device=dev)
@@ -166,6 +167,10 @@ def run(args):
     active = int((routing.counts > 0).sum().item())
     up_ms = _time_events(lambda: moe.moe_ffn_up(desc, x_perm, routing.offsets, w, h, ws), args.kernel_reps)
     down_ms = _time_events(lambda: moe.moe_ffn_down(desc, h, routing.offsets, w, o, ws), args.kernel_reps)
+    shared_ms = None
+    if spec.d_ff_shared:
+        o_sh = torch.empty(spec.tokens, spec.d_model, dtype=torch.float32, device=dev)
+        shared_ms = _time_events(lambda: moe.moe_shared_ffn(desc, x, w, o_sh, ws), args.kernel_reps)
 
     if args.copy_probe_mib:
         # One plain copy of known size for scaling the HBM byte counters (see the module doc).
@@ -224,6 +229,10 @@ def run(args):
                   "step_gbs_weights_and_io": round(
                       (up_bytes + down_bytes) / (ms * 1e-3) / 1e9, 1)},
     }
+    if shared_ms is not None:
+        sh_flops = 4.0 * spec.tokens * spec.d_model * spec.d_ff_shared
+        out["layer"].update({"shared_ffn_ms": round(shared_ms, 4),
+                             "shared_ffn_tflops": round(sh_flops / (shared_ms * 1e-3) / 1e12, 1)})
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(spec, inp, args.cpu_sample)
     print(json.dumps(out), flush=True)

@@ -39,8 +39,9 @@
  * Determinism.  No call uses floating-point atomics; repeated calls on the
  * same inputs give bitwise-identical results.
  * Limits.  1 <= tokens; 1 <= n_experts <= 64; 1 <= top_k <= min(8, n_experts);
- * d_model and d_ff are multiples of 128; tokens * top_k * max(d_model, d_ff)
- * must fit in int32 (else MOE_ERR_UNSUPPORTED).
+ * d_model, d_ff and d_ff_shared are multiples of 128; tokens * top_k *
+ * max(d_model, d_ff) and tokens * d_ff_shared must fit in int32 (else
+ * MOE_ERR_UNSUPPORTED).
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
@@ -92,6 +93,13 @@ typedef struct moe_desc {
   int32_t has_expert_bias; /* 1: b1 and b2 are given; 0: both absent */
   int32_t ffn_path;        /* MOE_FFN_*: AUTO picks by rows per expert; the others force a kernel */
   int32_t h_mode;          /* MOE_H_*: storage of the post-GELU activations h */
+  int32_t d_ff_shared;     /* Fs: hidden width of the shared expert, a multiple of 128; 0 = none.
+                              The shared expert (web page "Mixture of Experts: Scaling Parameters
+                              Without Scaling Compute", section "Design variations": shared
+                              experts, always active) runs on every token and its output is added
+                              to y with weight 1.  Several shared experts are one of their joint
+                              width: W1s stacked along the hidden axis, W2s side by side, b2s
+                              summed. */
 } moe_desc;
 
 /* What the library will run for a descriptor (host struct, filled by moe_query_plan). */
@@ -115,6 +123,10 @@ typedef struct moe_weights {
                               (web page "Mixture of Experts: Scaling Parameters Without Scaling
                               Compute", section "The central problem: load balancing",
                               auxiliary-loss-free balancing) */
+  const void* w1_shared;   /* [Fs][d] dtype, NULL iff d_ff_shared == 0 */
+  const void* b1_shared;   /* [Fs]    dtype, NULL iff d_ff_shared == 0 or !has_expert_bias */
+  const void* w2_shared;   /* [d][Fs] dtype, NULL iff d_ff_shared == 0 */
+  const void* b2_shared;   /* [d]     dtype, NULL iff d_ff_shared == 0 or !has_expert_bias */
 } moe_weights;
 
 /* Routing results (device pointers).  Which fields a call reads or writes is
@@ -184,15 +196,24 @@ int moe_grouped_ffn(const moe_desc* desc, const void* x_perm, const int32_t* off
                     const moe_weights* w, void* h, float* o, void* workspace,
                     size_t workspace_bytes, void* stream);
 
+/* The shared expert on every token (desc->d_ff_shared > 0):
+ *   o_shared[t] = W2s GELU(W1s x[t] + b1s) + b2s.  x [T][d] dtype, o_shared [T][d]
+ *   fp32.  Its hidden activations live in the workspace. */
+int moe_shared_ffn(const moe_desc* desc, const void* x, const moe_weights* w, float* o_shared,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
 /* Combine (web page "Mixture of Experts: Scaling Parameters Without Scaling
  * Compute", section "The MoE layer", step 3): y[t] = sum over slots s = 0..k-1
  * with dest[t][s] >= 0 of topk_w[t][s] * o[dest[t][s]], accumulated in fp32
- * in slot order (no atomics); y[t] = 0 when every slot was dropped.
- *   o [T*k][d] fp32, dest [T][k], topk_w [T][k] fp32, y [T][d] fp32. */
+ * in slot order (no atomics), plus o_shared[t] when o_shared is not NULL;
+ * without a shared expert y[t] = 0 when every slot was dropped.
+ *   o [T*k][d] fp32, dest [T][k], topk_w [T][k] fp32, o_shared [T][d] fp32 or
+ *   NULL, y [T][d] fp32. */
 int moe_combine(const moe_desc* desc, const float* o, const int32_t* dest, const float* topk_w,
-                float* y, void* stream);
+                const float* o_shared, float* y, void* stream);
 
-/* The whole layer: route, permute, grouped FFN, combine.
+/* The whole layer: route, permute, grouped FFN, the shared expert (if any),
+ * combine.
  *   x [T][d] dtype -> y [T][d] fp32 and *aux (device fp32 scalar, optional).
  *   routing may be NULL; any non-NULL field of it receives that result. */
 int moe_forward(const moe_desc* desc, const void* x, const moe_weights* w, float* y, float* aux,

@@ -20,9 +20,8 @@ MOE_FFN_AUTO, MOE_FFN_TILED, MOE_FFN_STREAM = 0, 1, 2
 MOE_H_AUTO, MOE_H_BF16, MOE_H_SPLIT = 0, 1, 2
 
 ENTRY_POINTS = ("moe_status_string", "moe_last_error", "moe_workspace_size", "moe_query_plan",
-                "moe_route",
-                "moe_permute", "moe_ffn_up", "moe_ffn_down", "moe_grouped_ffn", "moe_combine",
-                "moe_forward")
+                "moe_route", "moe_permute", "moe_ffn_up", "moe_ffn_down", "moe_grouped_ffn",
+                "moe_shared_ffn", "moe_combine", "moe_forward")
 
 
 class MoeError(RuntimeError):
@@ -34,7 +33,7 @@ class MoeError(RuntimeError):
 class CDesc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("tokens", "d_model", "d_ff", "n_experts", "top_k", "renormalize", "capacity",
-                 "dtype", "has_expert_bias", "ffn_path", "h_mode")]
+                 "dtype", "has_expert_bias", "ffn_path", "h_mode", "d_ff_shared")]
 
 
 class CPlan(ctypes.Structure):
@@ -44,7 +43,8 @@ class CPlan(ctypes.Structure):
 
 class CWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("w_router", "b_router", "w1", "b1", "w2", "b2",
-                                               "b_select")]
+                                               "b_select", "w1_shared", "b1_shared", "w2_shared",
+                                               "b2_shared")]
 
 
 class CRouting(ctypes.Structure):
@@ -77,7 +77,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "moe_ffn_up": (I, [pd, P, P, pw, P, P, S, P]),
         "moe_ffn_down": (I, [pd, P, P, pw, P, P, S, P]),
         "moe_grouped_ffn": (I, [pd, P, P, pw, P, P, P, S, P]),
-        "moe_combine": (I, [pd, P, P, P, P, P]),
+        "moe_shared_ffn": (I, [pd, P, pw, P, P, S, P]),
+        "moe_combine": (I, [pd, P, P, P, P, P, P]),
         "moe_forward": (I, [pd, P, pw, P, P, pr, P, S, P]),
     }
     for name, (res, args) in sig.items():
@@ -100,12 +101,13 @@ class Desc:
     has_expert_bias: bool = True
     ffn_path: int = MOE_FFN_AUTO
     h_mode: int = MOE_H_AUTO
+    d_ff_shared: int = 0          # shared expert width, 0 = none
 
     def to_c(self) -> CDesc:
         return CDesc(self.tokens, self.d_model, self.d_ff, self.n_experts, self.top_k,
                      int(bool(self.renormalize)), self.capacity,
                      MOE_DTYPE_BF16 if self.dtype == "bf16" else MOE_DTYPE_F32,
-                     int(bool(self.has_expert_bias)), self.ffn_path, self.h_mode)
+                     int(bool(self.has_expert_bias)), self.ffn_path, self.h_mode, self.d_ff_shared)
 
     @property
     def torch_dtype(self):
@@ -121,6 +123,10 @@ class Weights:
     b1: Optional[torch.Tensor] = None
     b2: Optional[torch.Tensor] = None
     b_select: Optional[torch.Tensor] = None
+    w1_shared: Optional[torch.Tensor] = None
+    b1_shared: Optional[torch.Tensor] = None
+    w2_shared: Optional[torch.Tensor] = None
+    b2_shared: Optional[torch.Tensor] = None
 
     def to_c(self) -> CWeights:
         return CWeights(*(_ptr(getattr(self, n)) for n, _ in CWeights._fields_))
@@ -239,9 +245,15 @@ def moe_grouped_ffn(desc, x_perm, offsets, weights, h, o, workspace=None, stream
                                           ws.numel(), _stream(stream)))
 
 
-def moe_combine(desc, o, dest, topk_w, y, stream=None):
+def moe_shared_ffn(desc, x, weights, o_shared, workspace=None, stream=None):
+    ws = workspace if workspace is not None else alloc_workspace(desc, x.device)
+    _check(load_library().moe_shared_ffn(ctypes.byref(desc.to_c()), _ptr(x), ctypes.byref(weights.to_c()),
+                                         _ptr(o_shared), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def moe_combine(desc, o, dest, topk_w, y, o_shared=None, stream=None):
     _check(load_library().moe_combine(ctypes.byref(desc.to_c()), _ptr(o), _ptr(dest), _ptr(topk_w),
-                                      _ptr(y), _stream(stream)))
+                                      _ptr(o_shared), _ptr(y), _stream(stream)))
 
 
 def moe_forward(desc, x, weights, y, aux=None, routing=None, workspace=None, stream=None):

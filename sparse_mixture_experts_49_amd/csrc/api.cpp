@@ -77,6 +77,11 @@ int validate_desc(const moe_desc* d) {
   const long long widest = d->d_model > d->d_ff ? d->d_model : d->d_ff;
   if (rows * widest > std::numeric_limits<int32_t>::max())
     return fail(MOE_ERR_UNSUPPORTED, "tokens * top_k * max(d_model, d_ff) exceeds int32");
+  if (d->d_ff_shared < 0) return fail(MOE_ERR_INVALID, "d_ff_shared must be >= 0");
+  if (d->d_ff_shared % 128)
+    return fail(MOE_ERR_UNSUPPORTED, "d_ff_shared (%d) must be a multiple of 128", d->d_ff_shared);
+  if ((long long)d->tokens * d->d_ff_shared > std::numeric_limits<int32_t>::max())
+    return fail(MOE_ERR_UNSUPPORTED, "tokens * d_ff_shared exceeds int32");
   return MOE_OK;
 }
 
@@ -122,6 +127,16 @@ int resolve(const moe_desc* d, Plan& p) {
   return MOE_OK;
 }
 
+// The shared expert is one dense product over all T tokens: the LDS-tiled
+// kernel with bf16 h when T >= 256 rows (bf16), else weight streaming with
+// split h (bf16) or fp32 h.
+void resolve_shared(const moe_desc* d, Plan& p) {
+  const bool bf16 = d->dtype == MOE_DTYPE_BF16;
+  p.path = (bf16 && d->tokens >= 256) ? MOE_FFN_TILED : MOE_FFN_STREAM;
+  p.h_mode = !bf16 ? MOE_H_AUTO : p.path == MOE_FFN_TILED ? MOE_H_BF16 : MOE_H_SPLIT;
+  p.h_elem = (!bf16 || p.h_mode == MOE_H_SPLIT) ? 4 : 2;
+}
+
 int validate_weights(const moe_desc* d, const moe_weights* w, bool router, bool experts) {
   if (!w) return fail(MOE_ERR_INVALID, "weights must not be NULL");
   if (router) {
@@ -138,6 +153,18 @@ int validate_weights(const moe_desc* d, const moe_weights* w, bool router, bool 
     } else if (w->b1 || w->b2) {
       return fail(MOE_ERR_INVALID, "b1/b2 given but has_expert_bias == 0");
     }
+    if (d->d_ff_shared > 0) {
+      MOE_REQUIRE_PTR(w->w1_shared, "w1_shared");
+      MOE_REQUIRE_PTR(w->w2_shared, "w2_shared");
+      if (d->has_expert_bias) {
+        MOE_REQUIRE_PTR(w->b1_shared, "b1_shared");
+        MOE_REQUIRE_PTR(w->b2_shared, "b2_shared");
+      } else if (w->b1_shared || w->b2_shared) {
+        return fail(MOE_ERR_INVALID, "b1_shared/b2_shared given but has_expert_bias == 0");
+      }
+    } else if (w->w1_shared || w->b1_shared || w->w2_shared || w->b2_shared) {
+      return fail(MOE_ERR_INVALID, "shared expert weights given but d_ff_shared == 0");
+    }
   }
   return MOE_OK;
 }
@@ -149,6 +176,7 @@ struct Layout {
   size_t part_psum, part_top1, part_z, blk_hist, blk_base;
   size_t topk_idx, topk_w, counts, offsets, dest, src, top1, prob_mean;
   size_t x_perm, h, o, partial;
+  size_t sh_offsets, h_sh, o_sh;   // shared expert (d_ff_shared > 0)
   size_t total;
 };
 
@@ -179,14 +207,26 @@ Layout layout_of(const moe_desc* d) {
   resolve(d, plan);
   L.h = take(A * d->d_ff * plan.h_elem);
   L.o = take(A * d->d_model * sizeof(float));
+  const size_t Fs = d->d_ff_shared;
+  Plan sh{};
+  resolve_shared(d, sh);
+  if (Fs) {
+    L.sh_offsets = take(2 * sizeof(int32_t));
+    L.h_sh = take(T * Fs * sh.h_elem);
+    L.o_sh = take(T * d->d_model * sizeof(float));
+  }
   // Split-k partial sums of the expert products (one product at a time).
   size_t part = 0;
-  {
-    const bool bf16 = d->dtype == MOE_DTYPE_BF16, split = plan.h_mode == MOE_H_SPLIT;
-    for (int up = 0; up < 2; ++up) {
-      const size_t b = moe::ffn_partial_bytes(plan.path, bf16, up, split, d->n_experts,
-                                              up ? d->d_ff : d->d_model, up ? d->d_model : d->d_ff,
-                                              row_bound(d), max_rows(d));
+  const bool bf16 = d->dtype == MOE_DTYPE_BF16;
+  for (int up = 0; up < 2; ++up) {
+    size_t b = moe::ffn_partial_bytes(plan.path, bf16, up, plan.h_mode == MOE_H_SPLIT, d->n_experts,
+                                      up ? d->d_ff : d->d_model, up ? d->d_model : d->d_ff,
+                                      row_bound(d), max_rows(d));
+    if (b > part) part = b;
+    if (Fs) {
+      b = moe::ffn_partial_bytes(sh.path, bf16, up, sh.h_mode == MOE_H_SPLIT, 1,
+                                 up ? (int)Fs : d->d_model, up ? d->d_model : (int)Fs, d->tokens,
+                                 d->tokens);
       if (b > part) part = b;
     }
   }
@@ -287,9 +327,46 @@ int launch_one_ffn(const moe_desc* d, bool up, const void* in, const int32_t* of
   return hip_status(moe::launch_ffn(a, s), up ? "ffn up launch" : "ffn down launch");
 }
 
-int launch_comb(const moe_desc* d, const float* o, const int32_t* dest, const float* wt, float* y,
-                hipStream_t s) {
-  moe::CombineArgs a{o, dest, wt, y, d->tokens, d->d_model, d->top_k};
+// The shared expert: one dense product pair over all T tokens of x.
+int launch_shared(const moe_desc* d, const void* x, const moe_weights* w, float* o_sh, void* ws,
+                  const Layout& L, hipStream_t s) {
+  Plan sh{};
+  resolve_shared(d, sh);
+  int32_t* offs = at<int32_t>(ws, L.sh_offsets);
+  if (int st = hip_status(moe::launch_dense_offsets(offs, d->tokens, s), "shared offsets launch"))
+    return st;
+  moe::FfnArgs a{};
+  a.split = sh.h_mode == MOE_H_SPLIT;
+  a.plane = (size_t)d->tokens * d->d_ff_shared;
+  a.bf16 = d->dtype == MOE_DTYPE_BF16;
+  a.offsets = offs;
+  a.E = 1;
+  a.max_rows_per_expert = d->tokens;
+  a.max_rows = d->tokens;
+  a.path = sh.path;
+  a.partial = at<float>(ws, L.partial);
+  void* h = at<void>(ws, L.h_sh);
+  a.up = true;
+  a.a = x;
+  a.w = w->w1_shared;
+  a.bias = d->has_expert_bias ? w->b1_shared : nullptr;
+  a.out = h;
+  a.N = d->d_ff_shared;
+  a.K = d->d_model;
+  if (int st = hip_status(moe::launch_ffn(a, s), "shared ffn up launch")) return st;
+  a.up = false;
+  a.a = h;
+  a.w = w->w2_shared;
+  a.bias = d->has_expert_bias ? w->b2_shared : nullptr;
+  a.out = o_sh;
+  a.N = d->d_model;
+  a.K = d->d_ff_shared;
+  return hip_status(moe::launch_ffn(a, s), "shared ffn down launch");
+}
+
+int launch_comb(const moe_desc* d, const float* o, const int32_t* dest, const float* wt,
+                const float* o_sh, float* y, hipStream_t s) {
+  moe::CombineArgs a{o, dest, wt, y, d->tokens, d->d_model, d->top_k, o_sh};
   return hip_status(moe::launch_combine(a, s), "combine launch");
 }
 
@@ -406,13 +483,26 @@ int moe_grouped_ffn(const moe_desc* desc, const void* x_perm, const int32_t* off
 }
 
 int moe_combine(const moe_desc* desc, const float* o, const int32_t* dest, const float* topk_w,
-                float* y, void* stream) {
+                const float* o_shared, float* y, void* stream) {
   if (int st = validate_desc(desc)) return st;
   MOE_REQUIRE_PTR(o, "o");
   MOE_REQUIRE_PTR(dest, "dest");
   MOE_REQUIRE_PTR(topk_w, "topk_w");
+  MOE_OPTIONAL_PTR(o_shared, "o_shared");
   MOE_REQUIRE_PTR(y, "y");
-  return launch_comb(desc, o, dest, topk_w, y, static_cast<hipStream_t>(stream));
+  return launch_comb(desc, o, dest, topk_w, o_shared, y, static_cast<hipStream_t>(stream));
+}
+
+int moe_shared_ffn(const moe_desc* desc, const void* x, const moe_weights* w, float* o_shared,
+                   void* ws, size_t ws_bytes, void* stream) {
+  if (int st = validate_desc(desc)) return st;
+  if (desc->d_ff_shared == 0) return fail(MOE_ERR_INVALID, "the layer has no shared expert");
+  MOE_REQUIRE_PTR(x, "x");
+  MOE_REQUIRE_PTR(o_shared, "o_shared");
+  if (int st = validate_weights(desc, w, false, true)) return st;
+  Layout L;
+  if (int st = check_ws(desc, ws, ws_bytes, L)) return st;
+  return launch_shared(desc, x, w, o_shared, ws, L, static_cast<hipStream_t>(stream));
 }
 
 int moe_forward(const moe_desc* desc, const void* x, const moe_weights* w, float* y, float* aux,
@@ -454,7 +544,12 @@ int moe_forward(const moe_desc* desc, const void* x, const moe_weights* w, float
     return st;
   if (int st = launch_one_ffn(desc, true, x_perm, r.offsets, w, h, ws, L, s)) return st;
   if (int st = launch_one_ffn(desc, false, h, r.offsets, w, o, ws, L, s)) return st;
-  return launch_comb(desc, o, r.dest, r.topk_w, y, s);
+  float* o_sh = nullptr;
+  if (desc->d_ff_shared > 0) {
+    o_sh = at<float>(ws, L.o_sh);
+    if (int st = launch_shared(desc, x, w, o_sh, ws, L, s)) return st;
+  }
+  return launch_comb(desc, o, r.dest, r.topk_w, o_sh, y, s);
 }
 
 }  // extern "C"

@@ -6,7 +6,9 @@
 // sums them in slot order (fp32 fma), so no two threads ever write the same
 // output and no atomics are needed; the result is bitwise repeatable.  A token
 // whose every slot was dropped by the capacity limit gets 0 (the residual
-// connection outside the layer carries x).
+// connection outside the layer carries x).  A shared expert's output, when
+// given, is added after the slot sum (same page, section "Design variations":
+// shared experts are always active), also for tokens whose slots were dropped.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -14,7 +16,8 @@ namespace moe {
 
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ o,
                                                       const int32_t* __restrict__ dest,
-                                                      const float* __restrict__ topk_w, int T,
+                                                      const float* __restrict__ topk_w,
+                                                      const float* __restrict__ shared, int T,
                                                       int d, int k, float* __restrict__ y) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + wave;
@@ -39,12 +42,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
         for (int i = 0; i < 4; ++i) acc[i] = fmaf(w[s], ov[i], acc[i]);
       }
     }
+    if (shared) acc += *reinterpret_cast<const f32x4*>(shared + (size_t)t * d + (size_t)v * 4);
     *reinterpret_cast<f32x4*>(yr + (size_t)v * 4) = acc;
   }
 }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
-  combine_kernel<<<(a.T + 3) / 4, 256, 0, s>>>(a.o, a.dest, a.topk_w, a.T, a.d, a.k, a.y);
+  combine_kernel<<<(a.T + 3) / 4, 256, 0, s>>>(a.o, a.dest, a.topk_w, a.shared, a.T, a.d, a.k, a.y);
   return hipGetLastError();
 }
 

@@ -776,6 +776,18 @@ static void launch_stream(const FfnArgs& a, hipStream_t s) {
   }
 }
 
+__global__ void dense_offsets_kernel(int32_t* __restrict__ offsets, int rows) {
+  if (threadIdx.x == 0) {
+    offsets[0] = 0;
+    offsets[1] = rows;
+  }
+}
+
+hipError_t launch_dense_offsets(int32_t* offsets, int rows, hipStream_t s) {
+  dense_offsets_kernel<<<1, 64, 0, s>>>(offsets, rows);
+  return hipGetLastError();
+}
+
 hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
   if (a.path == MOE_FFN_TILED) {
     // Upper bound on tiles: sum_e ceil(count_e/256) <= ceil(R/256) + E; the grid

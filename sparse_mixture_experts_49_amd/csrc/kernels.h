@@ -59,6 +59,9 @@ struct FfnArgs {
   float* partial;          // workspace for split-k partial sums (ffn_partial_bytes bytes)
 };
 hipError_t launch_ffn(const FfnArgs& a, hipStream_t s);
+// Writes offsets = {0, rows}: the segment table of a dense product (one
+// "expert" owning every row), e.g. the shared expert over all tokens.
+hipError_t launch_dense_offsets(int32_t* offsets, int rows, hipStream_t s);
 // Workspace bytes the product needs for split-k partial sums on `path`
 // (MOE_FFN_TILED or MOE_FFN_STREAM; 0 if it never splits).
 size_t ffn_partial_bytes(int path, bool bf16, bool up, bool split, int E, int N, int K,
@@ -70,6 +73,7 @@ struct CombineArgs {
   const float* topk_w;
   float* y;
   int T, d, k;
+  const float* shared;     // [T][d] shared expert output added after the slot sum, or null
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 

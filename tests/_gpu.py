@@ -25,14 +25,17 @@ def desc_for(spec, path=moe.MOE_FFN_AUTO, h_mode=moe.MOE_H_AUTO):
     if spec.dtype == "f32":
         h_mode = moe.MOE_H_AUTO
     return moe.Desc(spec.tokens, spec.d_model, spec.d_ff, spec.n_experts, spec.top_k,
-                    spec.renormalize, spec.capacity, spec.dtype, spec.expert_bias, path, h_mode)
+                    spec.renormalize, spec.capacity, spec.dtype, spec.expert_bias, path, h_mode,
+                    spec.d_ff_shared)
 
 
 def weights_for(inp, dev=DEV):
     return moe.Weights(w_router=to_dev(inp["w_router"], dev), w1=to_dev(inp["w1"], dev),
                        w2=to_dev(inp["w2"], dev), b_router=to_dev(inp.get("b_router"), dev),
                        b1=to_dev(inp.get("b1"), dev), b2=to_dev(inp.get("b2"), dev),
-                       b_select=to_dev(inp.get("b_select"), dev))
+                       b_select=to_dev(inp.get("b_select"), dev),
+                       w1_shared=to_dev(inp.get("w1_shared"), dev), b1_shared=to_dev(inp.get("b1_shared"), dev),
+                       w2_shared=to_dev(inp.get("w2_shared"), dev), b2_shared=to_dev(inp.get("b2_shared"), dev))
 
 
 def tol_for(spec):

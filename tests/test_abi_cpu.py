@@ -75,6 +75,9 @@ def test_workspace_size_grows_with_shape():
     (dict(h_mode=3), B.MOE_ERR_INVALID),
     (dict(h_mode=B.MOE_H_SPLIT, dtype="f32"), B.MOE_ERR_INVALID),
     (dict(h_mode=B.MOE_H_SPLIT, ffn_path=B.MOE_FFN_TILED), B.MOE_ERR_UNSUPPORTED),
+    (dict(d_ff_shared=-128), B.MOE_ERR_INVALID),
+    (dict(d_ff_shared=100), B.MOE_ERR_UNSUPPORTED),
+    (dict(tokens=1 << 20, d_ff_shared=4096, top_k=1), B.MOE_ERR_UNSUPPORTED),
 ])
 def test_invalid_descriptors(kw, status):
     base = dict(tokens=64, d_model=256, d_ff=512, n_experts=8, top_k=2)
@@ -151,3 +154,27 @@ def test_plan_resolution_of_the_named_workloads():
         assert (p["ffn_path"], p["h_mode"]) == (path, hm), name
         assert p["h_bytes"] == s.tokens * s.top_k * s.d_ff * eb
         assert p["workspace_bytes"] == moe.moe_workspace_size(d)
+
+
+def test_shared_expert_flag_must_match_pointers():
+    lib = moe.load_library()
+    d = moe.Desc(64, 256, 512, 8, 2, has_expert_bias=False)
+    w = B.CWeights(0x1000, None, 0x2000, None, 0x4000, None, None, 0x5000, None, 0x6000, None)
+    st = lib.moe_ffn_up(ctypes.byref(d.to_c()), 0x5000, 0x6000, ctypes.byref(w), 0x7000,
+                        0x100000, _ws(d), None)
+    assert st == B.MOE_ERR_INVALID and "d_ff_shared" in lib.moe_last_error().decode()
+    d2 = moe.Desc(64, 256, 512, 8, 2, has_expert_bias=False, d_ff_shared=256)
+    w2 = B.CWeights(0x1000, None, 0x2000, None, 0x4000, None, None, 0x5000, None, None, None)
+    st = lib.moe_shared_ffn(ctypes.byref(d2.to_c()), 0x8000, ctypes.byref(w2), 0x9000,
+                            0x100000, _ws(d2), None)
+    assert st == B.MOE_ERR_INVALID and "w2_shared" in lib.moe_last_error().decode()
+    st = lib.moe_shared_ffn(ctypes.byref(d.to_c()), 0x8000, ctypes.byref(w), 0x9000,
+                            0x100000, _ws(d), None)
+    assert st == B.MOE_ERR_INVALID and "no shared expert" in lib.moe_last_error().decode()
+
+
+def test_shared_expert_grows_the_workspace():
+    base = _ws(moe.Desc(512, 256, 512, 8, 2))
+    shared = _ws(moe.Desc(512, 256, 512, 8, 2, d_ff_shared=1024))
+    # offsets + h (bf16 on the tiled path: 512 rows) + o fp32
+    assert shared - base >= 512 * 1024 * 2 + 512 * 256 * 4

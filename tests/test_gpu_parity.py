@@ -165,13 +165,31 @@ def test_combine(name):
     o[:eo["o"].shape[0]] = eo["o"]
     desc = G.desc_for(spec)
     y = torch.empty(spec.tokens, spec.d_model, dtype=torch.float32, device=G.DEV)
+    sh = O.shared_expert(inp, ref["x64"])
+    o_sh = None if sh is None else G.to_dev(sh.astype(np.float32))
     moe.moe_combine(desc, G.to_dev(o), G.to_dev(ref["dest"].astype(np.int32)),
-                    G.to_dev(ref["topk_w"].astype(np.float32)), y)
+                    G.to_dev(ref["topk_w"].astype(np.float32)), y, o_sh)
     torch.cuda.synchronize()
     yref = O.forward(inp, O.desc_of(spec))["y"]
     assert G.err_over_rms(y.cpu().numpy(), yref) <= 1e-6
     dropped = ~ref["keep"].any(axis=1)
-    assert np.all(y.cpu().numpy()[dropped] == 0.0)
+    want = 0.0 if sh is None else sh.astype(np.float32)[dropped]
+    assert np.all(y.cpu().numpy()[dropped] == want)
+
+
+SHARED_NAMES = [n for n in SMALL if SMALL[n].d_ff_shared]
+
+
+@pytest.mark.parametrize("name", SHARED_NAMES)
+def test_shared_ffn(name):
+    """moe_shared_ffn alone: the shared expert on every token against the oracle."""
+    spec, inp = inputs_for(name)
+    desc = G.desc_for(spec)
+    o_sh = torch.empty(spec.tokens, spec.d_model, dtype=torch.float32, device=G.DEV)
+    moe.moe_shared_ffn(desc, G.to_dev(inp["x"]), G.weights_for(inp), o_sh)
+    torch.cuda.synchronize()
+    ref = O.shared_expert(inp, O.widen(inp["x"]))
+    assert G.err_over_rms(o_sh.cpu().numpy(), ref) <= G.tol_for(spec)
 
 
 def _forward_gpu(spec, inp, path=moe.MOE_FFN_AUTO, h_mode=moe.MOE_H_AUTO):
