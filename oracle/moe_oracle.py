@@ -35,8 +35,11 @@ Readings where the pages are silent or garbled (all listed in the design notes):
   * GELU is the exact erf form;
   * f_i counts the top-1 choice of every token before any capacity drop,
     P_i averages the full softmax over all tokens, aux = E * sum_i f_i P_i;
-  * capacity (top-1 only) keeps, per expert, the C lowest-index tokens that
-    chose it; a dropped token's layer output is 0;
+  * capacity keeps, per expert, the C lowest-index tokens that chose it (any
+    k); a dropped assignment contributes 0 (a token with every slot dropped
+    gets 0);
+  * the reroute policy (optional) serves overflow at the token's next-best
+    unused expert in rounds (see reroute());
   * rows of one expert's segment are ordered by token index;
   * a shared expert (optional) runs on every token, dropped ones included, and
     its output is added to y after the routed sum, with weight 1.
@@ -133,19 +136,85 @@ def routing_weights(p, idx, renormalize):
 # Capacity and dispatch layout   [LH "The central problem", expert capacity]
 # ----------------------------------------------------------------------------
 def capacity_keep(idx, n_experts, capacity):
-    """Boolean keep mask [T,k].  Capacity applies to top-1 only: per expert, the
-    `capacity` lowest-index tokens that chose it are kept, the rest dropped."""
+    """Boolean keep mask [T,k] of the drop policy: per expert, the `capacity`
+    lowest-index tokens that chose it (in any slot) are kept, the rest dropped.
+    A token picks an expert at most once, so this is well defined for any k."""
     T, k = idx.shape
     keep = np.ones((T, k), dtype=bool)
     if capacity and capacity > 0:
-        if k != 1:
-            raise ValueError("capacity is defined for top-1 routing only")
         seen = np.zeros(n_experts, dtype=np.int64)
         for t in range(T):
-            e = idx[t, 0]
-            keep[t, 0] = seen[e] < capacity
-            seen[e] += 1
+            for s in range(k):
+                e = idx[t, s]
+                keep[t, s] = seen[e] < capacity
+                seen[e] += 1
     return keep
+
+
+def reroute(idx, scores, probs, capacity, renormalize):
+    """The reroute policy for expert overflow.  [LD "Experts also have capacity
+    limits": overflow may be routed elsewhere; LH "The central problem: load
+    balancing": overflow tokens are dropped or rerouted]
+
+    Rounds.  Round 0 requests every chosen (t, s) -> idx[t, s].  In each round
+    the requests to an expert are accepted in token order while the expert has
+    capacity left; a rejected assignment asks, in the next round, for its
+    token's best-scored expert that the token has not yet used (a token's
+    pending slots take these in slot order); an assignment with no expert left
+    is dropped.  A served assignment's weight is the router probability of the
+    expert that serves it over the same denominator as the original choices
+    (their probability sum when renormalising, else 1).
+
+    Returns (served [T,k] expert or -1 if dropped, weights [T,k], rounds,
+    margin [T]): margin is the smallest gap between consecutive ranked scores
+    among the ranks the token's decisions consulted (its ranks 0 .. last tried,
+    and the boundary to the next one)."""
+    T, k = idx.shape
+    E = scores.shape[1]
+    order = np.argsort(-scores, axis=1, kind="stable")        # ranking, ties -> lower index
+    served = np.full((T, k), -1, dtype=np.int64)
+    used = [set(int(e) for e in idx[t]) for t in range(T)]
+    nxt = [k] * T                                             # next rank to try, per token
+    request = idx.copy().astype(np.int64)                     # round 0: the router's choices
+    pending = np.ones((T, k), dtype=bool)
+    left = np.full(E, capacity, dtype=np.int64)
+    rounds = 0
+    while pending.any():
+        rounds += 1
+        for t in range(T):                                    # token order within an expert
+            for s in range(k):
+                if pending[t, s] and request[t, s] >= 0:
+                    e = request[t, s]
+                    if left[e] > 0:
+                        left[e] -= 1
+                        served[t, s] = e
+                        pending[t, s] = False
+        for t in range(T):                                    # next candidates, slot order
+            for s in range(k):
+                if not pending[t, s]:
+                    continue
+                cand = -1
+                while nxt[t] < E:
+                    e = int(order[t, nxt[t]])
+                    nxt[t] += 1
+                    if e not in used[t]:
+                        cand = e
+                        break
+                if cand < 0:
+                    pending[t, s] = False                     # nothing left: dropped
+                else:
+                    used[t].add(cand)
+                    request[t, s] = cand
+    denom = probs[np.arange(T)[:, None], idx].sum(axis=1, keepdims=True) if renormalize \
+        else np.ones((T, 1))
+    w = np.where(served >= 0, np.take_along_axis(probs, np.maximum(served, 0), axis=1) / denom, 0.0)
+    ranked = np.take_along_axis(scores, order, axis=1)
+    margin = np.full(T, np.inf)
+    for t in range(T):
+        last = min(nxt[t], E - 1)
+        if last >= 1:
+            margin[t] = float((ranked[t, :last] - ranked[t, 1:last + 1]).min())
+    return served, w, rounds, margin
 
 
 def dispatch_layout(idx, keep, n_experts):
@@ -220,12 +289,23 @@ def route(inputs, desc):
     x64 = widen(inputs["x"])
     g = router_logits(x64, widen(inputs["w_router"]), widen(inputs.get("b_router")))
     p = softmax(g)
-    idx, margin = topk_by_logit(selection_scores(g, widen(inputs.get("b_select"))), desc["top_k"])
+    sc = selection_scores(g, widen(inputs.get("b_select")))
+    idx, margin = topk_by_logit(sc, desc["top_k"])
     w = routing_weights(p, idx, desc["renormalize"])
-    keep = capacity_keep(idx, desc["n_experts"], desc.get("capacity", 0))
-    counts, offsets, dest, src = dispatch_layout(idx, keep, desc["n_experts"])
     aux, f, P, top1 = aux_loss(idx, p, desc["n_experts"])
-    return {"logits": g, "probs": p, "topk_idx": idx, "topk_w": w, "margin": margin,
+    C = desc.get("capacity", 0)
+    if C and desc.get("capacity_policy", "drop") == "reroute":
+        served, final_w, rounds, rr_margin = reroute(idx, sc, p, C, desc["renormalize"])
+        margin = np.minimum(margin, rr_margin)
+        keep = served >= 0
+        final_idx = np.where(keep, served, idx)     # dropped slots keep the router's choice
+        final_w = np.where(keep, final_w, w)
+    else:
+        keep = capacity_keep(idx, desc["n_experts"], C)
+        final_idx, final_w, rounds = idx, w, 0
+    counts, offsets, dest, src = dispatch_layout(final_idx, keep, desc["n_experts"])
+    return {"logits": g, "probs": p, "scores": sc, "router_idx": idx, "router_w": w,
+            "topk_idx": final_idx, "topk_w": final_w, "margin": margin, "reroute_rounds": rounds,
             "keep": keep, "counts": counts, "offsets": offsets, "dest": dest, "src": src,
             "aux": aux, "f": f, "P": P, "top1_count": top1, "z_loss": router_z_loss(g),
             "x64": x64}
@@ -314,4 +394,5 @@ def desc_of(spec):
     """The option set of a workload as a plain dict."""
     return {"tokens": spec.tokens, "d_model": spec.d_model, "d_ff": spec.d_ff,
             "n_experts": spec.n_experts, "top_k": spec.top_k,
-            "renormalize": bool(spec.renormalize), "capacity": spec.capacity}
+            "renormalize": bool(spec.renormalize), "capacity": spec.capacity,
+            "capacity_policy": getattr(spec, "capacity_policy", "drop")}

@@ -57,8 +57,11 @@ def dense_masked(inputs, desc):
     top1 = np.argmin(rank, axis=1)                         # rank 0
     C = desc.get("capacity", 0)
     if C:
-        earlier = np.array([np.sum(top1[:t] == top1[t]) for t in range(T)])
-        mask[np.arange(T), top1] &= earlier < C
+        if desc.get("capacity_policy", "drop") != "drop":
+            raise NotImplementedError("dense_masked covers the drop policy only")
+        # keep (t, e) if fewer than C earlier tokens also chose e
+        earlier = np.cumsum(mask, axis=0) - mask
+        mask &= earlier < C
     y = np.zeros((T, x.shape[1]))
     b1 = inputs.get("b1")
     b2 = inputs.get("b2")
@@ -109,6 +112,9 @@ def loops(inputs, desc):
     d, F = desc["d_model"], desc["d_ff"]
     T = len(X)
     ys, top1s, probs_all, lses = [], [], [], []
+    reroute_served = None
+    if C and desc.get("capacity_policy", "drop") == "reroute":
+        reroute_served = _loops_reroute(X, WR, BR, BS, E, k, C)
     taken = [0] * E
     for t in range(T):
         g = []
@@ -142,7 +148,12 @@ def loops(inputs, desc):
             w = [v / sw for v in w]
         y = [0.0] * d
         for s, e in enumerate(chosen):
-            if C:
+            if reroute_served is not None:
+                e = reroute_served[t][s]
+                if e < 0:
+                    continue
+                w[s] = p[e] / (sum(p[c] for c in chosen) if desc["renormalize"] else 1.0)
+            elif C:
                 if taken[e] >= C:
                     taken[e] += 1
                     continue
@@ -168,3 +179,57 @@ def loops(inputs, desc):
     aux = E * sum(f_frac[e] * P[e] for e in range(E))
     z_loss = sum(v * v for v in lses) / T
     return {"y": np.array(ys), "aux": aux, "top1": top1s, "z_loss": z_loss}
+
+
+def _loops_reroute(X, WR, BR, BS, E, k, C):
+    """Reroute rounds with scalar loops: each round serves requests per expert in
+    token order while capacity lasts; rejected slots ask for their token's next
+    best unused expert (by score, lower index on ties); none left -> dropped."""
+    T = len(X)
+    d = len(X[0])
+    ranking = []
+    for t in range(T):
+        sc = []
+        for e in range(E):
+            v = sum(WR[e][j] * X[t][j] for j in range(d))
+            if BR is not None:
+                v += BR[e]
+            if BS is not None:
+                v += BS[e]
+            sc.append(v)
+        rk = []
+        for _ in range(E):                       # repeated argmax, lower index first on ties
+            best = None
+            for e in range(E):
+                if e in rk:
+                    continue
+                if best is None or sc[e] > sc[best]:
+                    best = e
+            rk.append(best)
+        ranking.append(rk)
+    served = [[-1] * k for _ in range(T)]
+    req = [[ranking[t][s] for s in range(k)] for t in range(T)]
+    used = [set(ranking[t][:k]) for t in range(T)]
+    pos = [k] * T
+    load = [0] * E
+    pend = [[True] * k for _ in range(T)]
+    while any(any(row) for row in pend):
+        for t in range(T):
+            for s in range(k):
+                if pend[t][s] and load[req[t][s]] < C:
+                    load[req[t][s]] += 1
+                    served[t][s] = req[t][s]
+                    pend[t][s] = False
+        for t in range(T):
+            for s in range(k):
+                if not pend[t][s]:
+                    continue
+                while pos[t] < E and ranking[t][pos[t]] in used[t]:
+                    pos[t] += 1
+                if pos[t] >= E:
+                    pend[t][s] = False
+                else:
+                    req[t][s] = ranking[t][pos[t]]
+                    used[t].add(req[t][s])
+                    pos[t] += 1
+    return served

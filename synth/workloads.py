@@ -69,6 +69,7 @@ class Workload:
     seed: int = 0
     selection_bias: bool = False  # fp32 per-expert bias added to the scores used to pick experts
     d_ff_shared: int = 0          # hidden width of the always-active shared expert (0: none)
+    capacity_policy: str = "drop" # overflow beyond capacity: "drop" or "reroute"
 
     def with_(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)

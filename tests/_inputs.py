@@ -43,6 +43,14 @@ SMALL = {
                                      W.capacity_for(300, 16), True, "bf16", router_bias=True,
                                      d_ff_shared=256),
     "shared_fp32": Workload("shared_fp32", 60, 128, 256, 8, 2, True, 0, True, "f32", d_ff_shared=384),
+    # capacity with top-2 (drop), and the reroute policy (top-1 and top-2, bf16 and fp32)
+    "capacity_top2_bf16": Workload("capacity_top2_bf16", 400, 256, 512, 16, 2, True, 40, True,
+                                   "bf16", router_bias=True),
+    "reroute_top1_bf16": Workload("reroute_top1_bf16", 500, 256, 512, 16, 1, False,
+                                  W.capacity_for(500, 16), True, "bf16", router_bias=True,
+                                  capacity_policy="reroute"),
+    "reroute_top2_fp32": Workload("reroute_top2_fp32", 200, 128, 256, 8, 2, True, 40, True, "f32",
+                                  router_bias=True, capacity_policy="reroute"),
     # the mid-size layer's shapes (4096 tokens, 16 experts) with a selection bias
     "mid_select_bias_bf16": Workload("mid_select_bias_bf16", 4096, 1024, 4096, 16, 2, True, 0, True,
                                      "bf16", selection_bias=True),
@@ -60,14 +68,22 @@ def small_router_bias(spec):
 
 
 def repair(spec, router_bias=None, max_rounds=50):
-    """Redraw token rows until every top-k margin of the selection scores exceeds 1e-3."""
+    """Redraw token rows until every margin the routing decisions depend on
+    exceeds 1e-3: the top-k margin of the selection scores and, with rerouting,
+    the gaps among the ranks each token's reroutes consulted."""
     wr64 = O.widen(W.make_router(spec))
     b64 = None if router_bias is None else np.asarray(router_bias, np.float32).astype(np.float64)
     bs64 = O.widen(W.make_selection_bias(spec)) if spec.selection_bias else None
     redraw = {}
     for _ in range(max_rounds):
-        g = O.router_logits(O.widen(W.make_x(spec, redraw)), wr64, b64)
-        _, margin = O.topk_by_logit(O.selection_scores(g, bs64), spec.top_k)
+        if spec.capacity_policy == "reroute":
+            inp = {"x": W.make_x(spec, redraw), "w_router": W.make_router(spec),
+                   "b_router": None if router_bias is None else np.asarray(router_bias, np.float32),
+                   "b_select": W.make_selection_bias(spec) if spec.selection_bias else None}
+            margin = O.route(inp, O.desc_of(spec))["margin"]
+        else:
+            g = O.router_logits(O.widen(W.make_x(spec, redraw)), wr64, b64)
+            _, margin = O.topk_by_logit(O.selection_scores(g, bs64), spec.top_k)
         bad = np.flatnonzero(margin <= O.MARGIN_MIN)
         if bad.size == 0:
             return redraw

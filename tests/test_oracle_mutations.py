@@ -15,6 +15,7 @@ from oracle import moe_oracle as O
 from tests import test_oracle_pins as P
 from tests import test_oracle_router_extras as RX
 from tests import test_oracle_shared_experts as SX
+from tests import test_oracle_capacity as CX
 
 
 def _tanh_gelu(z):
@@ -90,6 +91,36 @@ def _shared_half(inputs, x64_rows):
     return None if r is None else 0.5 * r
 
 
+def _keep_slot0_only(idx, n_experts, capacity):
+    T, k = idx.shape
+    keep = np.ones((T, k), dtype=bool)
+    if capacity:
+        seen = np.zeros(n_experts, dtype=np.int64)
+        for t in range(T):
+            e = idx[t, 0]
+            keep[t, 0] = seen[e] < capacity
+            seen[e] += 1
+    return keep
+
+
+_reroute_true = O.reroute
+
+
+def _reroute_reverse_order(idx, scores, probs, capacity, renormalize):
+    T = idx.shape[0]
+    rev = np.arange(T)[::-1]
+    served, w, rounds, margin = _reroute_true(idx[rev], scores[rev], probs[rev], capacity, renormalize)
+    return served[rev], w[rev], rounds, margin[rev]
+
+
+def _reroute_new_denominator(idx, scores, probs, capacity, renormalize):
+    served, w, rounds, margin = _reroute_true(idx, scores, probs, capacity, renormalize)
+    if renormalize:
+        ps = np.where(served >= 0, np.take_along_axis(probs, np.maximum(served, 0), axis=1), 0.0)
+        w = ps / ps.sum(axis=1, keepdims=True)
+    return served, w, rounds, margin
+
+
 MUTATIONS = [
     ("gelu_erf", _tanh_gelu, [P.test_gelu_against_math_erf_and_identities,
                               P.test_single_expert_reduces_to_dense_mlp]),
@@ -107,6 +138,9 @@ MUTATIONS = [
      [RX.test_dominant_selection_bias_picks_expert_with_unbiased_weights]),
     ("shared_expert", _shared_half, [SX.test_shared_expert_is_added_with_weight_one,
                                      SX.test_dropped_token_keeps_the_shared_expert]),
+    ("capacity_keep", _keep_slot0_only, [CX.test_drop_with_top2_hand_case]),
+    ("reroute", _reroute_reverse_order, [CX.test_reroute_top1_hand_case]),
+    ("reroute", _reroute_new_denominator, [functools.partial(CX.test_reroute_invariants, 1, 2, 4)]),
 ]
 
 
