@@ -130,7 +130,7 @@ def run(args):
     inp = synth.make_inputs(spec)
     desc = moe.Desc(spec.tokens, spec.d_model, spec.d_ff, spec.n_experts, spec.top_k,
                     spec.renormalize, spec.capacity, spec.dtype, spec.expert_bias,
-                    d_ff_shared=spec.d_ff_shared)
+                    d_ff_shared=spec.d_ff_shared, capacity_policy=spec.capacity_policy)
     x = _to_dev(inp["x"], dev)
     w = moe.Weights(**{name: _to_dev(inp.get(name), dev) for name in (
         "w_router", "w1", "w2", "b_router", "b1", "b2", "b_select", "w1_shared", "b1_shared",
@@ -167,6 +167,7 @@ def run(args):
     active = int((routing.counts > 0).sum().item())
     up_ms = _time_events(lambda: moe.moe_ffn_up(desc, x_perm, routing.offsets, w, h, ws), args.kernel_reps)
     down_ms = _time_events(lambda: moe.moe_ffn_down(desc, h, routing.offsets, w, o, ws), args.kernel_reps)
+    route_ms = _time_events(lambda: moe.moe_route(desc, x, w, routing, aux, ws), args.kernel_reps)
     shared_ms = None
     if spec.d_ff_shared:
         o_sh = torch.empty(spec.tokens, spec.d_model, dtype=torch.float32, device=dev)
@@ -218,11 +219,13 @@ def run(args):
         "data": "synthetic",
         "config": {"workload": spec.name, "tokens": spec.tokens, "d_model": spec.d_model,
                    "d_ff": spec.d_ff, "n_experts": spec.n_experts, "top_k": spec.top_k,
-                   "capacity": spec.capacity, "kept_rows": R, "active_experts": active,
+                   "capacity": spec.capacity, "capacity_policy": spec.capacity_policy,
+                   "kept_rows": R, "active_experts": active,
                    "ffn_path": {1: "tiled", 2: "stream"}[plan["ffn_path"]],
                    "h_mode": {0: "f32", 1: "bf16", 2: "split"}[plan["h_mode"]]},
         "roofline": roof,
-        "layer": {"ffn_up_ms": round(up_ms, 4), "ffn_down_ms": round(down_ms, 4),
+        "layer": {"route_ms": round(route_ms, 4),
+                  "ffn_up_ms": round(up_ms, 4), "ffn_down_ms": round(down_ms, 4),
                   "ffn_tflops": round(2 * flops_one / ((up_ms + down_ms) * 1e-3) / 1e12, 1),
                   "ffn_frac_peak": round(2 * flops_one / ((up_ms + down_ms) * 1e-3) / 1e12 / peak_flops, 4),
                   "ffn_gbs": round((up_bytes + down_bytes) / ((up_ms + down_ms) * 1e-3) / 1e9, 1),

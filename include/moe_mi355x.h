@@ -9,9 +9,11 @@
  * FFN_e(x) = W2_e GELU(W1_e x + b1_e) + b2_e and returns the probability-
  * weighted sum of their outputs.  The layer also returns the Switch-style
  * auxiliary loss aux = E * sum_i f_i P_i (same page, section "The central
- * problem: load balancing"), and for top-1 routing an optional expert capacity
- * drops the assignments beyond C per expert, in token order (same section;
- * also "Experts also have capacity limits" on the llmdaily day-59 page).
+ * problem: load balancing").  An optional expert capacity C limits every
+ * expert to C assignments, taken in token order (same section; also "Experts
+ * also have capacity limits" on the llmdaily day-59 page); the overflow is
+ * either dropped or rerouted to the token's next-best experts (moe_desc.
+ * capacity_policy).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -80,6 +82,21 @@ enum { MOE_FFN_AUTO = 0, MOE_FFN_TILED = 1, MOE_FFN_STREAM = 2 };
  * The TILED path supports MOE_H_BF16 only. */
 enum { MOE_H_AUTO = 0, MOE_H_BF16 = 1, MOE_H_SPLIT = 2 };
 
+/* What happens to assignments past an expert's capacity (moe_desc.capacity_policy).
+ *   MOE_CAPACITY_DROP:    the first C assignments of each expert in token order are
+ *                         kept, the rest dropped (moe_permute applies it).
+ *   MOE_CAPACITY_REROUTE: rounds (moe_route applies it).  Round 0 asks every slot's
+ *                         router choice.  In a round each expert accepts the requests
+ *                         in token order while it has capacity left; a rejected slot
+ *                         asks, in the next round, for its token's best-ranked expert
+ *                         the token has not asked yet (ranked as the top-k is; a
+ *                         token's rejected slots take these in slot order); a slot
+ *                         with no expert left is dropped.  A served slot's weight is
+ *                         the probability of the expert serving it over the original
+ *                         denominator (the sum of the k chosen probabilities when
+ *                         renormalising, else 1).  Needs capacity > 0. */
+enum { MOE_CAPACITY_DROP = 0, MOE_CAPACITY_REROUTE = 1 };
+
 /* Options of one layer call (host struct). */
 typedef struct moe_desc {
   int32_t tokens;          /* T */
@@ -88,7 +105,7 @@ typedef struct moe_desc {
   int32_t n_experts;       /* E */
   int32_t top_k;           /* k */
   int32_t renormalize;     /* 1: divide the chosen probabilities by their sum */
-  int32_t capacity;        /* C > 0: keep at most C tokens per expert (top_k == 1 only); 0: no limit */
+  int32_t capacity;        /* C > 0: at most C assignments per expert; 0: no limit */
   int32_t dtype;           /* MOE_DTYPE_* */
   int32_t has_expert_bias; /* 1: b1 and b2 are given; 0: both absent */
   int32_t ffn_path;        /* MOE_FFN_*: AUTO picks by rows per expert; the others force a kernel */
@@ -100,6 +117,7 @@ typedef struct moe_desc {
                               to y with weight 1.  Several shared experts are one of their joint
                               width: W1s stacked along the hidden axis, W2s side by side, b2s
                               summed. */
+  int32_t capacity_policy; /* MOE_CAPACITY_*: overflow past the capacity is dropped or rerouted */
 } moe_desc;
 
 /* What the library will run for a descriptor (host struct, filled by moe_query_plan). */
@@ -133,8 +151,10 @@ typedef struct moe_weights {
  * stated at each call; in moe_forward any field may be NULL (the workspace is
  * used instead). */
 typedef struct moe_routing {
-  int32_t* topk_idx;       /* [T][k] chosen experts in rank order: logit descending, ties -> lower index */
-  float* topk_w;           /* [T][k] routing weights: probabilities, renormalised over the k if asked */
+  int32_t* topk_idx;       /* [T][k] chosen experts in rank order: logit descending, ties -> lower index.
+                              With MOE_CAPACITY_REROUTE: the expert serving each slot, -1 if dropped */
+  float* topk_w;           /* [T][k] routing weights: probabilities, renormalised over the k if asked.
+                              With MOE_CAPACITY_REROUTE: the serving expert's weight, 0 if dropped */
   int32_t* counts;         /* [E]    rows kept per expert (after capacity) */
   int32_t* offsets;        /* [E+1]  exclusive prefix sum of counts; offsets[E] = R, total kept rows */
   int32_t* dest;           /* [T][k] row of assignment (t,s) in x_perm/h/o, -1 if dropped */
@@ -144,6 +164,7 @@ typedef struct moe_routing {
   float* z_loss;           /* [1]    router z-loss: mean over tokens of (log sum_e exp logit_e)^2
                               (same page and section, router z-loss); logits include b_router,
                               not b_select */
+  int32_t* reroute_rounds; /* [1]    acceptance rounds the reroute policy ran (0 without it) */
 } moe_routing;
 
 /* Status code -> static string. */
@@ -160,17 +181,20 @@ int moe_workspace_size(const moe_desc* desc, size_t* bytes);
 int moe_query_plan(const moe_desc* desc, moe_plan* plan);
 
 /* Router: logits = x W_r^T (+ b_router), softmax, top-k by logit (+ b_select
- * when given), routing weights, the aux loss and the router z-loss.
+ * when given), routing weights, the aux loss and the router z-loss; with
+ * MOE_CAPACITY_REROUTE also the rerouting of the overflow (one extra
+ * single-workgroup kernel).
  *   x [T][d] dtype.  Writes out->topk_idx and out->topk_w (both required),
- *   out->top1_count, out->prob_mean and out->z_loss (each optional), and *aux
- *   (device fp32 scalar, optional): aux = E * sum_e (top1_count_e / T) * P_e. */
+ *   out->top1_count, out->prob_mean, out->z_loss and out->reroute_rounds (each
+ *   optional), and *aux (device fp32 scalar, optional):
+ *   aux = E * sum_e (top1_count_e / T) * P_e, from the router's own choices. */
 int moe_route(const moe_desc* desc, const void* x, const moe_weights* w, moe_routing* out,
               float* aux, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Dispatch: per-expert histogram of the assignments, prefix scan, capacity,
- * stable ranks in token order, and the gather of token rows into
- * expert-contiguous rows.
- *   Reads r->topk_idx.  Writes r->counts, r->offsets, r->dest, r->src (all
+/* Dispatch: per-expert histogram of the assignments, prefix scan, capacity
+ * (MOE_CAPACITY_DROP), stable ranks in token order, and the gather of token
+ * rows into expert-contiguous rows.
+ *   Reads r->topk_idx; ids outside [0, E) are dropped assignments.  Writes r->counts, r->offsets, r->dest, r->src (all
  *   required) and x_perm [T*k][d] dtype: rows 0..R-1 get x_perm[dest[t][s]] = x[t];
  *   rows >= R are not written.  Inside expert e's segment rows follow token order. */
 int moe_permute(const moe_desc* desc, const void* x, moe_routing* r, void* x_perm,

@@ -16,7 +16,8 @@ Per workload it records:
   redraw       {row: attempt}: token rows redrawn from their own stream until
                every top-k logit margin (consecutive ranked gaps among ranks
                0..k) exceeds 1e-3, so the GPU's fp32 logits cannot reorder any
-               choice.
+               choice; with the reroute policy, every gap among the ranks a
+               token's reroutes consulted as well.
   stats        achieved loads, drops and the smallest margin (report only).
 """
 from __future__ import annotations
@@ -82,6 +83,10 @@ def repair_margins(spec, wr64, bias, max_rounds=50):
     for _ in range(max_rounds):
         g = _logits(spec, x, wr64, bias)
         _, margin = O.topk_by_logit(g, spec.top_k)
+        if spec.capacity_policy == "reroute":
+            r = O.route({"x": x, "w_router": W.make_router(spec), "b_router": bias},
+                        O.desc_of(spec))
+            margin = np.minimum(margin, r["margin"])
         bad = np.flatnonzero(margin <= O.MARGIN_MIN)
         if bad.size == 0:
             return redraw, g, margin
@@ -99,7 +104,7 @@ def calibrate(spec):
     if spec.name == "mixtral_prefill_bf16":
         bias, share, target = calibrate_zipf(spec, x_raw, wr64)
         out["zipf_target"] = target.tolist()
-    elif spec.name == "switch_capacity_bf16":
+    elif spec.name in ("switch_capacity_bf16", "switch_reroute_bf16"):
         hot = list(range(0, spec.n_experts, 8))
         bias, frac = calibrate_hot(spec, x_raw, wr64, hot)
         out["hot_experts"] = hot
@@ -117,7 +122,13 @@ def calibrate(spec):
         "min_margin": float(margin.min()),
         "redrawn_rows": len(redraw),
     }
-    if spec.name == "switch_capacity_bf16":
+    if spec.capacity_policy == "reroute":
+        r = O.route({"x": W.make_x(spec, redraw), "w_router": W.make_router(spec),
+                     "b_router": bias}, O.desc_of(spec))
+        out["stats"]["reroute"] = {"rounds": int(r["reroute_rounds"]),
+                                   "rerouted": int(((r["topk_idx"] != r["router_idx"]) & r["keep"]).sum()),
+                                   "dropped": int((~r["keep"]).sum())}
+    if spec.name in ("switch_capacity_bf16", "switch_reroute_bf16"):
         out["stats"]["hot_top1_fraction"] = float(np.isin(idx[:, 0], out["hot_experts"]).mean())
     # Workload-level properties the descriptions ask for.
     demand = np.bincount(idx.ravel(), minlength=spec.n_experts)

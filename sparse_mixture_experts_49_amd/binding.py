@@ -18,6 +18,8 @@ MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 MOE_FFN_AUTO, MOE_FFN_TILED, MOE_FFN_STREAM = 0, 1, 2
 MOE_H_AUTO, MOE_H_BF16, MOE_H_SPLIT = 0, 1, 2
+MOE_CAPACITY_DROP, MOE_CAPACITY_REROUTE = 0, 1
+_POLICIES = {"drop": MOE_CAPACITY_DROP, "reroute": MOE_CAPACITY_REROUTE}
 
 ENTRY_POINTS = ("moe_status_string", "moe_last_error", "moe_workspace_size", "moe_query_plan",
                 "moe_route", "moe_permute", "moe_ffn_up", "moe_ffn_down", "moe_grouped_ffn",
@@ -33,7 +35,8 @@ class MoeError(RuntimeError):
 class CDesc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("tokens", "d_model", "d_ff", "n_experts", "top_k", "renormalize", "capacity",
-                 "dtype", "has_expert_bias", "ffn_path", "h_mode", "d_ff_shared")]
+                 "dtype", "has_expert_bias", "ffn_path", "h_mode", "d_ff_shared",
+                 "capacity_policy")]
 
 
 class CPlan(ctypes.Structure):
@@ -50,7 +53,7 @@ class CWeights(ctypes.Structure):
 class CRouting(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("topk_idx", "topk_w", "counts", "offsets", "dest", "src", "top1_count",
-                 "prob_mean", "z_loss")]
+                 "prob_mean", "z_loss", "reroute_rounds")]
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -102,12 +105,14 @@ class Desc:
     ffn_path: int = MOE_FFN_AUTO
     h_mode: int = MOE_H_AUTO
     d_ff_shared: int = 0          # shared expert width, 0 = none
+    capacity_policy: str = "drop"  # "drop" or "reroute": what happens past the capacity
 
     def to_c(self) -> CDesc:
         return CDesc(self.tokens, self.d_model, self.d_ff, self.n_experts, self.top_k,
                      int(bool(self.renormalize)), self.capacity,
                      MOE_DTYPE_BF16 if self.dtype == "bf16" else MOE_DTYPE_F32,
-                     int(bool(self.has_expert_bias)), self.ffn_path, self.h_mode, self.d_ff_shared)
+                     int(bool(self.has_expert_bias)), self.ffn_path, self.h_mode, self.d_ff_shared,
+                     _POLICIES.get(self.capacity_policy, -1))
 
     @property
     def torch_dtype(self):
@@ -143,6 +148,7 @@ class Routing:
     top1_count: Optional[torch.Tensor] = None
     prob_mean: Optional[torch.Tensor] = None
     z_loss: Optional[torch.Tensor] = None
+    reroute_rounds: Optional[torch.Tensor] = None
 
     @classmethod
     def allocate(cls, desc: Desc, device) -> "Routing":
@@ -154,7 +160,8 @@ class Routing:
                    dest=torch.empty(T, k, **i32), src=torch.empty(T * k, **i32),
                    top1_count=torch.empty(E, **i32),
                    prob_mean=torch.empty(E, dtype=torch.float32, device=device),
-                   z_loss=torch.empty(1, dtype=torch.float32, device=device))
+                   z_loss=torch.empty(1, dtype=torch.float32, device=device),
+                   reroute_rounds=torch.empty(1, **i32))
 
     def to_c(self) -> CRouting:
         return CRouting(*(_ptr(getattr(self, f.name)) for f in dataclasses.fields(self)))

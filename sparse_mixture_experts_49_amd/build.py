@@ -14,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe_mi355x.so")
-SOURCES = ["api.cpp", "router.hip", "permute.hip", "ffn.hip", "combine.hip"]
+SOURCES = ["api.cpp", "router.hip", "reroute.hip", "permute.hip", "ffn.hip", "combine.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops.

@@ -57,8 +57,10 @@ int validate_desc(const moe_desc* d) {
   if (d->renormalize != 0 && d->renormalize != 1)
     return fail(MOE_ERR_INVALID, "renormalize must be 0 or 1");
   if (d->capacity < 0) return fail(MOE_ERR_INVALID, "capacity must be >= 0");
-  if (d->capacity > 0 && d->top_k != 1)
-    return fail(MOE_ERR_INVALID, "capacity is defined for top_k == 1 only (top_k = %d)", d->top_k);
+  if (d->capacity_policy != MOE_CAPACITY_DROP && d->capacity_policy != MOE_CAPACITY_REROUTE)
+    return fail(MOE_ERR_INVALID, "capacity_policy must be MOE_CAPACITY_DROP or _REROUTE");
+  if (d->capacity_policy == MOE_CAPACITY_REROUTE && d->capacity == 0)
+    return fail(MOE_ERR_INVALID, "the reroute policy needs a capacity > 0");
   if (d->dtype != MOE_DTYPE_F32 && d->dtype != MOE_DTYPE_BF16)
     return fail(MOE_ERR_INVALID, "dtype must be MOE_DTYPE_F32 or MOE_DTYPE_BF16");
   if (d->has_expert_bias != 0 && d->has_expert_bias != 1)
@@ -177,6 +179,7 @@ struct Layout {
   size_t topk_idx, topk_w, counts, offsets, dest, src, top1, prob_mean;
   size_t x_perm, h, o, partial;
   size_t sh_offsets, h_sh, o_sh;   // shared expert (d_ff_shared > 0)
+  size_t rr_score, rr_wt, rr_list;   // reroute policy
   size_t total;
 };
 
@@ -231,6 +234,11 @@ Layout layout_of(const moe_desc* d) {
     }
   }
   L.partial = take(part);
+  if (d->capacity_policy == MOE_CAPACITY_REROUTE) {
+    L.rr_score = take(T * 64 * sizeof(float));
+    L.rr_wt = take(T * E * sizeof(float));
+    L.rr_list = take(4 * A * sizeof(int32_t));
+  }
   L.total = p;
   return L;
 }
@@ -255,9 +263,11 @@ int hip_status(hipError_t e, const char* what) {
   return ok();
 }
 
+// The router, then (MOE_CAPACITY_REROUTE) the rerouting of the overflow.
 int launch_route(const moe_desc* d, const void* x, const moe_weights* w, int32_t* idx, float* wt,
-                 int32_t* top1, float* pmean, float* aux, float* zl, const Layout& L, void* ws,
-                 hipStream_t s) {
+                 int32_t* top1, float* pmean, float* aux, float* zl, int32_t* rounds,
+                 const Layout& L, void* ws, hipStream_t s) {
+  const bool rr = d->capacity_policy == MOE_CAPACITY_REROUTE;
   moe::RouterArgs a{};
   a.bf16 = d->dtype == MOE_DTYPE_BF16;
   a.x = x;
@@ -278,7 +288,23 @@ int launch_route(const moe_desc* d, const void* x, const moe_weights* w, int32_t
   a.prob_mean = pmean;
   a.aux = aux;
   a.z_loss = zl;
-  return hip_status(moe::launch_router(a, s), "router launch");
+  a.rr_score = rr ? at<float>(ws, L.rr_score) : nullptr;
+  a.rr_wt = rr ? at<float>(ws, L.rr_wt) : nullptr;
+  a.rounds_zero = rr ? nullptr : rounds;
+  if (int st = hip_status(moe::launch_router(a, s), "router launch")) return st;
+  if (!rr) return MOE_OK;
+  moe::RerouteArgs b{};
+  b.score = a.rr_score;
+  b.wt = a.rr_wt;
+  b.T = d->tokens;
+  b.k = d->top_k;
+  b.E = d->n_experts;
+  b.capacity = d->capacity;
+  b.topk_idx = idx;
+  b.topk_w = wt;
+  b.lists = at<int32_t>(ws, L.rr_list);
+  b.rounds = rounds;
+  return hip_status(moe::launch_reroute(b, s), "reroute launch");
 }
 
 int launch_perm(const moe_desc* d, const void* x, const int32_t* idx, int32_t* counts,
@@ -292,7 +318,8 @@ int launch_perm(const moe_desc* d, const void* x, const int32_t* idx, int32_t* c
   a.d = d->d_model;
   a.E = d->n_experts;
   a.k = d->top_k;
-  a.capacity = d->capacity;
+  // Under the reroute policy the router already kept every expert within capacity.
+  a.capacity = d->capacity_policy == MOE_CAPACITY_DROP ? d->capacity : 0;
   a.counts = counts;
   a.offsets = offsets;
   a.dest = dest;
@@ -419,10 +446,12 @@ int moe_route(const moe_desc* desc, const void* x, const moe_weights* w, moe_rou
   MOE_OPTIONAL_PTR(out->top1_count, "out->top1_count");
   MOE_OPTIONAL_PTR(out->prob_mean, "out->prob_mean");
   MOE_OPTIONAL_PTR(out->z_loss, "out->z_loss");
+  MOE_OPTIONAL_PTR(out->reroute_rounds, "out->reroute_rounds");
   Layout L;
   if (int st = check_ws(desc, ws, ws_bytes, L)) return st;
   return launch_route(desc, x, w, out->topk_idx, out->topk_w, out->top1_count, out->prob_mean,
-                      aux, out->z_loss, L, ws, static_cast<hipStream_t>(stream));
+                      aux, out->z_loss, out->reroute_rounds, L, ws,
+                      static_cast<hipStream_t>(stream));
 }
 
 int moe_permute(const moe_desc* desc, const void* x, moe_routing* r, void* x_perm, void* ws,
@@ -523,6 +552,7 @@ int moe_forward(const moe_desc* desc, const void* x, const moe_weights* w, float
     MOE_OPTIONAL_PTR(r.top1_count, "routing->top1_count");
     MOE_OPTIONAL_PTR(r.prob_mean, "routing->prob_mean");
     MOE_OPTIONAL_PTR(r.z_loss, "routing->z_loss");
+    MOE_OPTIONAL_PTR(r.reroute_rounds, "routing->reroute_rounds");
   }
   Layout L;
   if (int st = check_ws(desc, ws, ws_bytes, L)) return st;
@@ -537,7 +567,7 @@ int moe_forward(const moe_desc* desc, const void* x, const moe_weights* w, float
   void* h = at<void>(ws, L.h);
   float* o = at<float>(ws, L.o);
   if (int st = launch_route(desc, x, w, r.topk_idx, r.topk_w, r.top1_count, r.prob_mean, aux,
-                            r.z_loss, L, ws, s))
+                            r.z_loss, r.reroute_rounds, L, ws, s))
     return st;
   if (int st = launch_perm(desc, x, r.topk_idx, r.counts, r.offsets, r.dest, r.src, x_perm, L, ws,
                            s))

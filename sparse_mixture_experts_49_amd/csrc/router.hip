@@ -36,7 +36,8 @@ __global__ __launch_bounds__(256) void router_kernel(
     const T* __restrict__ x, const T* __restrict__ wr, const float* __restrict__ br,
     const float* __restrict__ bsel, int T_, int d, int E, int k, int renorm,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
-    double* __restrict__ part_psum, int32_t* __restrict__ part_top1, double* __restrict__ part_z) {
+    double* __restrict__ part_psum, int32_t* __restrict__ part_top1, double* __restrict__ part_z,
+    float* __restrict__ rr_score, float* __restrict__ rr_wt) {
   constexpr int kPerLane = 64 / sizeof(T);          // elements per lane per chunk
   constexpr int kChunk = 4 * kPerLane;              // 128 bf16 or 64 fp32
   constexpr int kPerVec = 16 / sizeof(T);
@@ -173,6 +174,14 @@ __global__ __launch_bounds__(256) void router_kernel(
         }
       }
     }
+    if (rr_score && t < T_) {                       // inputs of the reroute policy
+#pragma unroll
+      for (int j = 0; j < kMaxPer; ++j) {
+        const int e = q + 4 * j;                     // rows of 64 scores, -inf past E
+        rr_score[(size_t)t * 64 + e] = e < E ? sc[j] : -INFINITY;
+        if (e < E) rr_wt[(size_t)t * E + e] = renorm ? p[j] * winv : p[j];
+      }
+    }
 #pragma unroll
     for (int j = 0; j < kMaxPer; ++j) {
       const int e = q + 4 * j;
@@ -208,7 +217,8 @@ __global__ __launch_bounds__(256) void router_kernel(
 __global__ __launch_bounds__(kAuxThreads) void aux_finalize_kernel(
     const double* __restrict__ part_psum, const int32_t* __restrict__ part_top1,
     const double* __restrict__ part_z, int nblk, int T_, int E, int32_t* __restrict__ top1_count,
-    float* __restrict__ prob_mean, float* __restrict__ aux, float* __restrict__ z_loss) {
+    float* __restrict__ prob_mean, float* __restrict__ aux, float* __restrict__ z_loss,
+    int32_t* __restrict__ rounds_zero) {
   // The partials are [nblk][E] laid out flat.  Thread t < stride (a multiple of
   // E) sums entries t, t + stride, ... (all of expert t % E, coalesced across
   // the block); expert e's per-thread sums are then added in thread order.
@@ -251,6 +261,7 @@ __global__ __launch_bounds__(kAuxThreads) void aux_finalize_kernel(
     for (int i = 0; i < E; ++i) acc += fP[i];
     *aux = (float)((double)E * acc);
   }
+  if (t == 128 && rounds_zero) *rounds_zero = 0;
   if (t == 64 && z_loss) {
     double zt = 0.0;
     for (int u = 0; u < kAuxThreads; ++u) zt += pz[u];
@@ -268,7 +279,8 @@ static hipError_t launch_router_t(const RouterArgs& a, hipStream_t s) {
   case NT:                                                                                  \
     router_kernel<T, NT><<<nblk, 256, 0, s>>>(x, wr, a.b_router, a.b_select, a.T, a.d, a.E, \
                                                a.k, a.renorm, a.topk_idx, a.topk_w,         \
-                                               a.part_psum, a.part_top1, a.part_z);         \
+                                               a.part_psum, a.part_top1, a.part_z,          \
+                                               a.rr_score, a.rr_wt);                        \
     break;
   switch (nt) {
     MOE_ROUTER_CASE(1)
@@ -281,7 +293,8 @@ static hipError_t launch_router_t(const RouterArgs& a, hipStream_t s) {
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   aux_finalize_kernel<<<1, kAuxThreads, 0, s>>>(a.part_psum, a.part_top1, a.part_z, nblk, a.T, a.E,
-                                                a.top1_count, a.prob_mean, a.aux, a.z_loss);
+                                                a.top1_count, a.prob_mean, a.aux, a.z_loss,
+                                                a.rounds_zero);
   return hipGetLastError();
 }
 

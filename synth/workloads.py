@@ -62,7 +62,7 @@ class Workload:
     n_experts: int
     top_k: int
     renormalize: bool
-    capacity: int          # 0 = unlimited; top-1 only
+    capacity: int          # 0 = unlimited
     expert_bias: bool      # b1/b2 present
     dtype: str             # "f32" or "bf16"
     router_bias: bool = False  # fp32 logit bias drawn by calibration (skewed workloads)
@@ -91,6 +91,10 @@ WORKLOADS = {
                                      False, "bf16", router_bias=True),
     "switch_capacity_bf16": Workload("switch_capacity_bf16", 8192, 2048, 8192, 64, 1, False,
                                      capacity_for(8192, 64), True, "bf16", router_bias=True),
+    # the same layer and tokens with the overflow rerouted instead of dropped
+    "switch_reroute_bf16": Workload("switch_reroute_bf16", 8192, 2048, 8192, 64, 1, False,
+                                    capacity_for(8192, 64), True, "bf16", router_bias=True,
+                                    capacity_policy="reroute"),
     "decode_bf16": Workload("decode_bf16", 32, 4096, 14336, 8, 2, True, 0, True, "bf16"),
     # fine-grained experts (64 experts of width 1408, top-6) plus a shared expert of
     # width 2816 (two of width 1408 side by side); no router skew

@@ -26,7 +26,18 @@ def desc_for(spec, path=moe.MOE_FFN_AUTO, h_mode=moe.MOE_H_AUTO):
         h_mode = moe.MOE_H_AUTO
     return moe.Desc(spec.tokens, spec.d_model, spec.d_ff, spec.n_experts, spec.top_k,
                     spec.renormalize, spec.capacity, spec.dtype, spec.expert_bias, path, h_mode,
-                    spec.d_ff_shared)
+                    spec.d_ff_shared, spec.capacity_policy)
+
+
+def abi_topk(spec, ref):
+    """The oracle's final routing in the C ABI's convention: under the reroute
+    policy a dropped slot reads expert -1 and weight 0 (the oracle keeps the
+    router's choice there and marks it in `keep`); under the drop policy the
+    router's choices and weights are returned unchanged."""
+    if spec.capacity_policy != "reroute":
+        return ref["topk_idx"], ref["topk_w"]
+    keep = ref["keep"]
+    return np.where(keep, ref["topk_idx"], -1), np.where(keep, ref["topk_w"], 0.0)
 
 
 def weights_for(inp, dev=DEV):

@@ -68,7 +68,8 @@ def test_workspace_size_grows_with_shape():
     (dict(d_model=200), B.MOE_ERR_UNSUPPORTED),
     (dict(d_ff=100), B.MOE_ERR_UNSUPPORTED),
     (dict(capacity=-1), B.MOE_ERR_INVALID),
-    (dict(capacity=10, top_k=2), B.MOE_ERR_INVALID),
+    (dict(capacity_policy="spill"), B.MOE_ERR_INVALID),
+    (dict(capacity_policy="reroute"), B.MOE_ERR_INVALID),
     (dict(ffn_path=3), B.MOE_ERR_INVALID),
     (dict(ffn_path=B.MOE_FFN_TILED, dtype="f32"), B.MOE_ERR_UNSUPPORTED),
     (dict(tokens=1 << 20, d_ff=4096), B.MOE_ERR_UNSUPPORTED),
@@ -178,3 +179,25 @@ def test_shared_expert_grows_the_workspace():
     shared = _ws(moe.Desc(512, 256, 512, 8, 2, d_ff_shared=1024))
     # offsets + h (bf16 on the tiled path: 512 rows) + o fp32
     assert shared - base >= 512 * 1024 * 2 + 512 * 256 * 4
+
+
+def test_capacity_with_top_k_above_one_is_accepted():
+    assert _ws(moe.Desc(64, 256, 512, 8, 2, capacity=10)) > 0
+    assert _ws(moe.Desc(64, 256, 512, 8, 2, capacity=10, capacity_policy="reroute")) > 0
+
+
+def test_reroute_grows_the_workspace():
+    drop = _ws(moe.Desc(512, 256, 512, 8, 2, capacity=64))
+    rr = _ws(moe.Desc(512, 256, 512, 8, 2, capacity=64, capacity_policy="reroute"))
+    # scores and weights [T][E] fp32, two lists of (assignment, request) [T*k] int32
+    assert rr - drop >= 512 * 8 * 4 * 2 + 4 * 512 * 2 * 4
+
+
+def test_reroute_rounds_pointer_alignment_is_checked():
+    desc = moe.Desc(64, 256, 512, 8, 1, capacity=16, capacity_policy="reroute")
+    lib = moe.load_library()
+    weights = B.CWeights(0x2000, None, None, None, None, None)
+    routing = B.CRouting(0x3000, 0x4000, None, None, None, None, None, None, None, 0x5004)
+    st = lib.moe_route(ctypes.byref(desc.to_c()), 0x1000, ctypes.byref(weights),
+                       ctypes.byref(routing), None, 0x100000, _ws(desc), None)
+    assert st == B.MOE_ERR_INVALID and "reroute_rounds" in lib.moe_last_error().decode()

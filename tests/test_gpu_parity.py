@@ -47,8 +47,10 @@ def test_route(name):
     spec, inp = inputs_for(name)
     ref = O.route(inp, O.desc_of(spec))
     _, _, _, r, aux, _ = _route_gpu(spec, inp)
-    assert np.array_equal(r.topk_idx.cpu().numpy(), ref["topk_idx"])
-    assert G.rel_err(r.topk_w.cpu().numpy(), ref["topk_w"]) <= G.TOL_W
+    idx, wt = G.abi_topk(spec, ref)
+    assert np.array_equal(r.topk_idx.cpu().numpy(), idx)
+    assert G.rel_err(r.topk_w.cpu().numpy(), wt) <= G.TOL_W
+    assert r.reroute_rounds.item() == ref["reroute_rounds"]
     assert np.array_equal(r.top1_count.cpu().numpy(), ref["top1_count"])
     assert G.rel_err(r.prob_mean.cpu().numpy(), ref["P"]) <= G.TOL_W
     assert abs(aux.item() - ref["aux"]) <= G.TOL_AUX * abs(ref["aux"])
@@ -208,11 +210,13 @@ def _forward_gpu(spec, inp, path=moe.MOE_FFN_AUTO, h_mode=moe.MOE_H_AUTO):
 def _check_forward(spec, inp, y, aux, r, tokens=None):
     ref = O.forward(inp, O.desc_of(spec), tokens=tokens)
     sel = ref["tokens"]
-    assert np.array_equal(r.topk_idx.cpu().numpy(), ref["topk_idx"])
+    idx, wt = G.abi_topk(spec, ref)
+    assert np.array_equal(r.topk_idx.cpu().numpy(), idx)
+    assert r.reroute_rounds.item() == ref["reroute_rounds"]
     assert np.array_equal(r.counts.cpu().numpy(), ref["counts"])
     assert np.array_equal(r.offsets.cpu().numpy(), ref["offsets"])
     assert np.array_equal(r.dest.cpu().numpy(), ref["dest"])
-    assert G.rel_err(r.topk_w.cpu().numpy(), ref["topk_w"]) <= G.TOL_W
+    assert G.rel_err(r.topk_w.cpu().numpy(), wt) <= G.TOL_W
     assert abs(aux.item() - ref["aux"]) <= G.TOL_AUX * abs(ref["aux"])
     assert abs(r.z_loss.item() - ref["z_loss"]) <= G.TOL_AUX * abs(ref["z_loss"])
     err = G.err_over_rms(y.cpu().numpy()[sel], ref["y"])
@@ -263,10 +267,13 @@ def _sample_tokens(spec, ref_route, n=256, seed=1):
     pick = set(rng.choice(T, size=min(n, T), replace=False).tolist()) | {0, T - 1}
     dropped = np.flatnonzero(~ref_route["keep"].all(axis=1))
     pick |= set(dropped[:8].tolist())
+    moved = np.flatnonzero((ref_route["topk_idx"] != ref_route["router_idx"]).any(axis=1))
+    pick |= set(moved[:16].tolist())
     return np.array(sorted(pick))
 
 
 @pytest.mark.parametrize("name", ["toy_fp32", "mid_bf16", "decode_bf16", "switch_capacity_bf16",
+                                  "switch_reroute_bf16", "finegrained_shared_bf16",
                                   "mixtral_prefill_bf16"])
 def test_forward_full_size(name):
     """Each full-size workload in the launch configuration the bench times: routing
@@ -316,3 +323,23 @@ def test_selection_bias_changes_choices_not_weights():
     assert not np.array_equal(idx, unbiased["topk_idx"])
     p = np.take_along_axis(ref["probs"], idx, axis=1)
     assert G.rel_err(r.topk_w.cpu().numpy(), p / p.sum(axis=1, keepdims=True)) <= G.TOL_W
+
+
+def test_reroute_moves_overflow_within_capacity():
+    """The Switch-style layer with rerouting: the overflow of the hot experts is
+    served by other experts, no expert exceeds its capacity, and the routing
+    equals the oracle's slot by slot."""
+    spec, inp = inputs_for("switch_reroute_bf16")
+    ref = O.route(inp, O.desc_of(spec))
+    desc, x, _, r, _, ws = _route_gpu(spec, inp)
+    x_perm = torch.empty(spec.tokens * spec.top_k, spec.d_model, dtype=x.dtype, device=G.DEV)
+    moe.moe_permute(desc, x, r, x_perm, ws)
+    torch.cuda.synchronize()
+    idx, wt = G.abi_topk(spec, ref)
+    got = r.topk_idx.cpu().numpy()
+    assert np.array_equal(got, idx)
+    assert (got != ref["router_idx"]).sum() > 1000          # thousands of tokens moved
+    counts = r.counts.cpu().numpy()
+    assert counts.max() <= spec.capacity and np.array_equal(counts, ref["counts"])
+    assert r.reroute_rounds.item() == ref["reroute_rounds"] > 1
+    assert G.rel_err(r.topk_w.cpu().numpy(), wt) <= G.TOL_W
