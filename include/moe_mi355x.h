@@ -65,9 +65,12 @@ enum {
   MOE_ERR_HIP = -4           /* the HIP runtime refused a launch */
 };
 
-/* Expert-FFN kernel choice (moe_desc.ffn_path).  AUTO resolves to TILED for
- * bf16 layers averaging >= 256 rows per expert (MFMA-bound prefill) and to
- * STREAM otherwise (weight-streaming, HBM-bound). */
+/* Expert-FFN kernel choice (moe_desc.ffn_path).  Averages are the host's bound,
+ * min(T*k, E*C) / E rows per expert.  AUTO resolves to TILED (LDS-tiled, bf16
+ * only) for bf16 layers averaging >= 64 rows per expert, with 256-row tiles from
+ * 256 rows per expert (MFMA-bound prefill) and 128- or 160-row tiles below (a
+ * 160-row tile covers a whole expert under a capacity in (128, 160]); and to
+ * STREAM (weight-streaming, HBM-bound) otherwise. */
 enum { MOE_FFN_AUTO = 0, MOE_FFN_TILED = 1, MOE_FFN_STREAM = 2 };
 
 /* Storage of the post-GELU activations h for a bf16 layer (moe_desc.h_mode).
@@ -76,10 +79,11 @@ enum { MOE_FFN_AUTO = 0, MOE_FFN_TILED = 1, MOE_FFN_STREAM = 2 };
  *                lo = bf16(h - hi): plane hi [T*k][F] followed by plane lo
  *                [T*k][F] (4 bytes per element in total); the second product
  *                runs one MFMA per term, so o carries ~16 bits of h.
- *   MOE_H_AUTO:  SPLIT on the STREAM path (its MFMA work is hidden under the
- *                weight stream), BF16 on the TILED path.
- * For an fp32 layer h is fp32 [T*k][F] and h_mode must be AUTO.
- * The TILED path supports MOE_H_BF16 only. */
+ *   MOE_H_AUTO:  BF16 on the TILED path at >= 256 rows per expert (MFMA-bound),
+ *                SPLIT below that and on the STREAM path, where the products
+ *                are weight-bound and the second term costs little.
+ * For an fp32 layer h is fp32 [T*k][F] and h_mode must be AUTO.  On the TILED
+ * path SPLIT uses 128- or 160-row tiles. */
 enum { MOE_H_AUTO = 0, MOE_H_BF16 = 1, MOE_H_SPLIT = 2 };
 
 /* What happens to assignments past an expert's capacity (moe_desc.capacity_policy).

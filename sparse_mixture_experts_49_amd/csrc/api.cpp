@@ -73,8 +73,6 @@ int validate_desc(const moe_desc* d) {
     return fail(MOE_ERR_INVALID, "h_mode must be MOE_H_AUTO, _BF16 or _SPLIT");
   if (d->dtype == MOE_DTYPE_F32 && d->h_mode != MOE_H_AUTO)
     return fail(MOE_ERR_INVALID, "h_mode must be MOE_H_AUTO for an fp32 layer (h is fp32)");
-  if (d->ffn_path == MOE_FFN_TILED && d->h_mode == MOE_H_SPLIT)
-    return fail(MOE_ERR_UNSUPPORTED, "the LDS-tiled expert kernel supports MOE_H_BF16 only");
   const long long rows = (long long)d->tokens * d->top_k;
   const long long widest = d->d_model > d->d_ff ? d->d_model : d->d_ff;
   if (rows * widest > std::numeric_limits<int32_t>::max())
@@ -111,20 +109,24 @@ struct Plan {
   size_t h_elem; // bytes per h element
 };
 
+// AUTO: bf16 layers averaging >= 64 rows per expert (by the host's bound) run
+// the LDS-tiled kernel, the rest stream the weights.  h is one bf16 plane on
+// the tiled path at >= 256 rows per expert (MFMA-bound prefill) and two planes
+// below that, where the products are weight-bound and the second plane's
+// MFMAs and bytes cost little.
 int resolve(const moe_desc* d, Plan& p) {
   const bool bf16 = d->dtype == MOE_DTYPE_BF16;
+  const double avg = (double)max_rows(d) / d->n_experts;
   p.path = d->ffn_path;
-  if (p.path == MOE_FFN_AUTO)
-    p.path = (bf16 && (double)max_rows(d) / d->n_experts >= 256.0) ? MOE_FFN_TILED : MOE_FFN_STREAM;
+  if (p.path == MOE_FFN_AUTO) p.path = (bf16 && avg >= 64.0) ? MOE_FFN_TILED : MOE_FFN_STREAM;
   if (!bf16) {
     p.h_mode = MOE_H_AUTO;
     p.h_elem = 4;
     return MOE_OK;
   }
   p.h_mode = d->h_mode;
-  if (p.h_mode == MOE_H_AUTO) p.h_mode = p.path == MOE_FFN_TILED ? MOE_H_BF16 : MOE_H_SPLIT;
-  if (p.path == MOE_FFN_TILED && p.h_mode == MOE_H_SPLIT)
-    return fail(MOE_ERR_UNSUPPORTED, "the LDS-tiled expert kernel supports MOE_H_BF16 only");
+  if (p.h_mode == MOE_H_AUTO)
+    p.h_mode = (p.path == MOE_FFN_TILED && avg >= 256.0) ? MOE_H_BF16 : MOE_H_SPLIT;
   p.h_elem = p.h_mode == MOE_H_SPLIT ? 4 : 2;
   return MOE_OK;
 }
@@ -336,7 +338,7 @@ int launch_one_ffn(const moe_desc* d, bool up, const void* in, const int32_t* of
   if (int st = resolve(d, plan)) return st;
   moe::FfnArgs a{};
   a.split = plan.h_mode == MOE_H_SPLIT;
-  a.plane = (size_t)d->tokens * d->top_k * d->d_ff;
+  a.plane = (size_t)d->tokens * d->top_k * d->d_ff;   // elements per h plane
   a.bf16 = d->dtype == MOE_DTYPE_BF16;
   a.up = up;
   a.a = in;

@@ -162,10 +162,11 @@ struct TileJob {
   int slot;        // partial-tile slot when parts > 1
 };
 
+template <int BM>
 __device__ __forceinline__ bool tile_job(const int32_t* __restrict__ offsets, int E, int ntn, int nk,
                                          int b, TileJob& job) {
   int total_mt = 0;
-  for (int e = 0; e < E; ++e) total_mt += (offsets[e + 1] - offsets[e] + kTBM - 1) / kTBM;
+  for (int e = 0; e < E; ++e) total_mt += (offsets[e + 1] - offsets[e] + BM - 1) / BM;
   constexpr int kGroupM = kXcds * kBandM;
   const int x = b % kXcds, i = b / kXcds;
   const int G = total_mt / kGroupM;
@@ -201,9 +202,10 @@ __device__ __forceinline__ bool tile_job(const int32_t* __restrict__ offsets, in
 }
 
 // First entry of XCD x's tail (its last, partial round) in tile_job's order.
+template <int BM>
 __device__ __forceinline__ int tail_start(const int32_t* __restrict__ offsets, int E, int ntn, int x) {
   int total_mt = 0;
-  for (int e = 0; e < E; ++e) total_mt += (offsets[e + 1] - offsets[e] + kTBM - 1) / kTBM;
+  for (int e = 0; e < E; ++e) total_mt += (offsets[e + 1] - offsets[e] + BM - 1) / BM;
   constexpr int kGroupM = kXcds * kBandM;
   const int G = total_mt / kGroupM;
   const int left = (total_mt - G * kGroupM) * ntn;
@@ -211,32 +213,57 @@ __device__ __forceinline__ int tail_start(const int32_t* __restrict__ offsets, i
   return cnt / kCusPerXcd * kCusPerXcd;
 }
 
-template <bool UP, int BN, int NW>
-__global__ __launch_bounds__(NW * 64, 1) void ffn_tiled_kernel(
-    const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets,
-    const uint16_t* __restrict__ W, const uint16_t* __restrict__ bias, void* __restrict__ out,
-    int E, int N, int K, float* __restrict__ partial) {
-  constexpr int kWavesN = NW / 2;
+// Rows staged per epilogue pass: the largest multiple of 32 dividing the wave's
+// rows whose staging fits the wave's share of the LDS.
+constexpr int epilogue_pass_rows(int rows, int row_bytes, int budget) {
+  int best = 32;
+  for (int r = 32; r <= rows; r += 32)
+    if (rows % r == 0 && r * row_bytes <= budget) best = r;
+  return best;
+}
+
+// Epilogue modes of the tiled kernel.
+constexpr int kOutGeluBf16 = 0;    // first product: GELU, rounded to bf16
+constexpr int kOutF32 = 1;         // second product, or a partial tile: fp32 as is
+constexpr int kOutGeluSplit = 2;   // first product: GELU as bf16 hi + lo planes
+
+// BM x BN output tile, 4 waves as WM (along rows) x 4/WM, WS stages of W.
+// SPLIT: the first product stores h as hi + lo planes; the second reads A as
+// those two planes (both in one A stage, plane 1 after plane 0) and runs one
+// MFMA per plane against the same W fragment.
+template <bool UP, bool SPLIT, int BM, int BN, int WM, int WS>
+__global__ __launch_bounds__(256, 1) void ffn_tiled_kernel(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ A_lo,
+    const int32_t* __restrict__ offsets, const uint16_t* __restrict__ W,
+    const uint16_t* __restrict__ bias, void* __restrict__ out, size_t out_plane, int E, int N,
+    int K, float* __restrict__ partial) {
+  constexpr int NW = 4;
+  constexpr int kPl = (SPLIT && !UP) ? 2 : 1;   // A planes
+  constexpr int kWavesN = NW / WM;
   constexpr int kWN = BN / kWavesN;       // wave tile columns
   constexpr int kNT = kWN / 32;           // 32-column subtiles per wave
-  constexpr int kMT = 4;                  // 32-row subtiles per wave (128 rows)
-  constexpr int kAStage = kTBM * 128;     // bytes per stage
+  constexpr int kWM = BM / WM;            // wave tile rows
+  constexpr int kMT = kWM / 32;           // 32-row subtiles per wave
+  constexpr int kAF = kMT * kPl;          // A fragments per slice
+  constexpr int kAPlane = BM * 128;       // bytes per A plane per stage
+  constexpr int kAStage = kAPlane * kPl;
   constexpr int kBStage = BN * 128;
-  constexpr int kBBase = 2 * kAStage;     // A: 2 stages, then W: 3 stages
-  constexpr int kLds = kBBase + 3 * kBStage;
-  constexpr int kAInst = kTBM / 8 / NW;   // 1 KB load instructions per wave per stage
+  constexpr int kBBase = 2 * kAStage;     // A: 2 stages, then W: WS stages
+  constexpr int kLds = kBBase + WS * kBStage;
+  constexpr int kAInst = BM * kPl / 8 / NW;   // 1 KB load instructions per wave per stage
   constexpr int kBInst = BN / 8 / NW;
-  static_assert(kNT >= 1 && kAInst >= 1 && kBInst >= 1, "tile shape");
-  static_assert(kLds <= 160 * 1024, "LDS");
+  static_assert(kNT >= 1 && kMT >= 1 && kWM % 32 == 0, "tile shape");
+  static_assert((BM * kPl) % (8 * NW) == 0 && BN % (8 * NW) == 0 && BM % 16 == 0, "load plan");
+  static_assert(kLds <= 160 * 1024 && WS >= 3, "LDS");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kLds];
 
   // ---- which tile ----
   const int ntn = N / BN;
   TileJob job;
-  if (!tile_job(offsets, E, ntn, K / kTBK, blockIdx.x, job)) return;
+  if (!tile_job<BM>(offsets, E, ntn, K / kTBK, blockIdx.x, job)) return;
   const int mt = job.mt, nt = job.nt;
   int e, r0, r1;
-  if (!find_mtile(offsets, E, kTBM, mt, e, r0, r1)) return;
+  if (!find_mtile(offsets, E, BM, mt, e, r0, r1)) return;
   const int n0 = nt * BN;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -244,16 +271,19 @@ __global__ __launch_bounds__(NW * 64, 1) void ffn_tiled_kernel(
   const int wm = wave / kWavesN, wn = wave % kWavesN;
   const int fr = lane & 31, fc = lane >> 5;
 
-  // Load plan: instruction i of wave w fills LDS rows (i*NW + w)*8 + lane/8,
-  // physical chunk lane%8, i.e. logical chunk (lane%8) ^ ((row >> 1) & 7).
+  // Load plan: instruction i of wave w fills LDS rows (i*NW + w)*8 + lane/8 of
+  // the stage (A: plane p's row r is LDS row p*BM + r), physical chunk lane%8,
+  // i.e. logical chunk (lane%8) ^ ((row >> 1) & 7).  BM is a multiple of 16,
+  // so a plane-1 row has the swizzle of its row within the plane.
   const uint16_t* a_src[kAInst];
   const uint16_t* b_src[kBInst];
   const uint16_t* Wexp = W + (size_t)e * N * K;
 #pragma unroll
   for (int i = 0; i < kAInst; ++i) {
-    const int row = (i * NW + wave) * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ ((row >> 1) & 7);
-    a_src[i] = A + (size_t)min(r0 + row, r1 - 1) * K + c * 8;
+    const int lrow = (i * NW + wave) * 8 + (lane >> 3);
+    const int plane = lrow / BM, row = lrow % BM;
+    const int c = (lane & 7) ^ ((lrow >> 1) & 7);
+    a_src[i] = (plane ? A_lo : A) + (size_t)min(r0 + row, r1 - 1) * K + c * 8;
   }
 #pragma unroll
   for (int i = 0; i < kBInst; ++i) {
@@ -294,38 +324,42 @@ __global__ __launch_bounds__(NW * 64, 1) void ffn_tiled_kernel(
 
   // A k-step of 64 is four 16-wide MFMA slices; a half step is two slices.
   // X holds half 0 of a step, Y half 1.  Fragment r of a half (r < kReads) is
-  // slice r / (kMT + kNT) of A subtile q (q < kMT) or of W subtile q - kMT.
-  constexpr int kReads = 2 * (kMT + kNT);
-  constexpr int kMfmas = 2 * kMT * kNT;
+  // slice r / (kAF + kNT) of A fragment q (q < kAF: plane q / kMT, subtile
+  // q % kMT) or of W subtile q - kAF.
+  constexpr int kReads = 2 * (kAF + kNT);
+  constexpr int kMfmas = 2 * kMT * kNT * kPl;
   static_assert(kReads % 2 == 0 && kReads / 2 <= kMfmas, "two reads per MFMA");
   static_assert(kAInst <= kMfmas && kBInst <= kMfmas, "at most one load per MFMA");
-  u32x4 xa[2][kMT], xb[2][kNT], ya[2][kMT], yb[2][kNT];
-  auto read_at = [&](u32x4 (&fa)[2][kMT], u32x4 (&fb)[2][kNT], int sa_, int sb_, int half, int r) {
-    const int sl = r / (kMT + kNT), q = r % (kMT + kNT);
+  u32x4 xa[2][kAF], xb[2][kNT], ya[2][kAF], yb[2][kNT];
+  auto read_at = [&](u32x4 (&fa)[2][kAF], u32x4 (&fb)[2][kNT], int sa_, int sb_, int half, int r) {
+    const int sl = r / (kAF + kNT), q = r % (kAF + kNT);
     const int ch = (half * 2 + sl) * 2 + fc;     // 16 B chunk: 8 k of this slice
-    if (q < kMT) {
-      const int row = wm * 128 + q * 32 + fr;
+    if (q < kAF) {
+      const int row = (q / kMT) * BM + wm * kWM + (q % kMT) * 32 + fr;
       fa[sl][q] = ld16(lds + sa_ * kAStage + row * 128 + ((ch ^ ((row >> 1) & 7)) << 4));
     } else {
-      const int row = wn * kWN + (q - kMT) * 32 + fr;
-      fb[sl][q - kMT] = ld16(lds + kBBase + sb_ * kBStage + row * 128 + ((ch ^ ((row >> 1) & 7)) << 4));
+      const int row = wn * kWN + (q - kAF) * 32 + fr;
+      fb[sl][q - kAF] = ld16(lds + kBBase + sb_ * kBStage + row * 128 + ((ch ^ ((row >> 1) & 7)) << 4));
     }
   };
-  auto read_all = [&](u32x4 (&fa)[2][kMT], u32x4 (&fb)[2][kNT], int sa_, int sb_, int half) {
+  auto read_all = [&](u32x4 (&fa)[2][kAF], u32x4 (&fb)[2][kNT], int sa_, int sb_, int half) {
 #pragma unroll
     for (int r = 0; r < kReads; ++r) read_at(fa, fb, sa_, sb_, half, r);
   };
-  // MFMA m of a half: slice m / (kNT kMT), W subtile (m / kMT) % kNT, A subtile m % kMT.
-  auto mfma_at = [&](const u32x4 (&fa)[2][kMT], const u32x4 (&fb)[2][kNT], int m) {
-    const int sl = m / (kNT * kMT), jn = (m / kMT) % kNT, im = m % kMT;
-    acc[jn][im] = mfma32_bf16(fb[sl][jn], fa[sl][im], acc[jn][im]);
+  // MFMA m of a half: slice m / (kPl kNT kMT), then plane, W subtile, A subtile
+  // (fastest), so consecutive MFMAs update different accumulators.
+  auto mfma_at = [&](const u32x4 (&fa)[2][kAF], const u32x4 (&fb)[2][kNT], int m) {
+    constexpr int kPerSlice = kPl * kNT * kMT;
+    const int sl = m / kPerSlice, rem = m % kPerSlice;
+    const int p = rem / (kNT * kMT), jn = (rem / kMT) % kNT, im = rem % kMT;
+    acc[jn][im] = mfma32_bf16(fb[sl][jn], fa[sl][p * kMT + im], acc[jn][im]);
   };
   // One half step in a fixed instruction order: after each MFMA (whose
   // operands were read in the previous half), up to two LDS reads of the next
   // half's fragments, front-loaded so they return long before they are needed,
   // and, evenly spread, this half's L global->LDS loads.  A wave waiting to
   // issue a load cannot issue MFMAs, so loads are paced rather than burst.
-  auto half_step = [&](const u32x4 (&fa)[2][kMT], const u32x4 (&fb)[2][kNT], u32x4 (&na)[2][kMT],
+  auto half_step = [&](const u32x4 (&fa)[2][kAF], const u32x4 (&fb)[2][kNT], u32x4 (&na)[2][kAF],
                        u32x4 (&nb)[2][kNT], int nsa, int nsb, int nhalf, auto load_fn, auto loads_tag) {
     constexpr int L = decltype(loads_tag)::value;
 #pragma unroll
@@ -344,35 +378,35 @@ __global__ __launch_bounds__(NW * 64, 1) void ffn_tiled_kernel(
   using NoLoads = std::integral_constant<int, 0>;
 
   // Pipeline.  Step t's A tile sits in A stage t % 2, its W tile in W stage
-  // t % 3.  Per step t:
+  // t % WS, and W runs WS - 1 steps ahead.  Per step t:
   //   X <- half 0 of step t is in registers when step t starts;
   //   first half: X MFMAs, reads of Y <- half 1 of step t, and the loads of W
-  //     for step t+2 into W stage (t+2) % 3, which nobody reads any more (it
-  //     held step t-1, finished before the previous barrier);
-  //   wait for our LDS reads and for A and W of step t+1 (W of step t+2, issued
-  //     after them, may still be in flight), barrier;
+  //     for step t+WS-1 into W stage (t-1) % WS, which nobody reads any more
+  //     (it held step t-1, finished before the previous barrier);
+  //   wait for our LDS reads and for A and W of step t+1 (only W of step
+  //     t+WS-1, issued after both, may still be in flight), barrier;
   //   second half: Y MFMAs, reads of X <- half 0 of step t+1, and the loads of
   //     A for step t+2 into A stage t % 2 (every wave is done reading it).
-  // Loads complete in issue order, so "at most kBInst outstanding" means
-  // everything but the last W group has landed.
+  // Loads complete in issue order.  The prologue issues A0, A1, W0 .. W(WS-2),
+  // so every wait counts whole W groups only.
   issue_a(0, 0);
-  issue_b(0, 0);
   issue_a(1, 1);
-  issue_b(1, 1);
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(kAInst + kBInst));
+#pragma unroll
+  for (int d = 0; d < WS - 1; ++d) issue_b(d, d);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm((WS - 2) * kBInst));   // A0, A1 and W0 landed
   __syncthreads();
   read_all(xa, xb, 0, 0, 0);
   int sa = 0, sb = 0;                                // stages of step kt
   for (int kt = 0; kt < nk - 1; ++kt) {
-    const int sa1 = sa ^ 1, sb1 = sb == 2 ? 0 : sb + 1, sb2 = sb1 == 2 ? 0 : sb1 + 1;
-    const int kb = min(kt + 2, nk - 1) * kTBK;
+    const int sa1 = sa ^ 1, sb1 = sb == WS - 1 ? 0 : sb + 1, sbw = sb == 0 ? WS - 1 : sb - 1;
+    const int kbw = min(kt + WS - 1, nk - 1) * kTBK, kba = min(kt + 2, nk - 1) * kTBK;
     half_step(xa, xb, ya, yb, sa, sb, 1,
-              [&](int i) { load_lds16_raw(b_src[i] + kb, lds0 + kBBase + sb2 * kBStage + (i * NW + wave) * 1024); },
+              [&](int i) { load_lds16_raw(b_src[i] + kbw, lds0 + kBBase + sbw * kBStage + (i * NW + wave) * 1024); },
               LoadsB{});
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kBInst));
     __syncthreads();
     half_step(ya, yb, xa, xb, sa1, sb1, 0,
-              [&](int i) { load_lds16_raw(a_src[i] + kb, lds0 + sa * kAStage + (i * NW + wave) * 1024); },
+              [&](int i) { load_lds16_raw(a_src[i] + kba, lds0 + sa * kAStage + (i * NW + wave) * 1024); },
               LoadsA{});
     sa = sa1;
     sb = sb1;
@@ -388,9 +422,9 @@ __global__ __launch_bounds__(NW * 64, 1) void ffn_tiled_kernel(
   // and g = 0..3, row im*32 + fr and columns jn*32 + 8g + 4fc .. +3 of the
   // wave's sub-tile.  Each wave stages rows in its own LDS region with 16 B
   // chunks XOR-swizzled by row, then stores whole row segments of the rows
-  // below row_lim to dst (row stride in elements).  F32: fp32 values (the
-  // second product's output, or a partial tile); otherwise GELU, rounded to
-  // bf16 (the first product's output).
+  // below row_lim to dst (row stride in elements).  kOutGeluBf16 stages bf16;
+  // the other modes stage fp32 (kOutGeluSplit converts to hi + lo on the way
+  // out, the lo plane out_plane elements after the hi plane).
   const uint16_t* bexp = bias ? bias + (size_t)e * N : nullptr;
   auto bias4 = [&](int jn, int g, float (&bv)[4]) {
     const int col = n0 + wn * kWN + jn * 32 + 8 * g + 4 * fc;
@@ -400,13 +434,13 @@ __global__ __launch_bounds__(NW * 64, 1) void ffn_tiled_kernel(
     bv[2] = __uint_as_float(braw.y << 16);
     bv[3] = __uint_as_float(braw.y & 0xffff0000u);
   };
-  auto store_tile = [&](auto f32_tag, uint8_t* dst, size_t row_stride, int row_lim, bool with_bias) {
-    constexpr bool F32 = decltype(f32_tag)::value;
-    constexpr int kElem = F32 ? 4 : 2;
-    constexpr int kRowB = kWN * kElem, kChunks = kRowB / 16;
-    // Rows staged per pass so that NW regions fit in the LDS.
-    constexpr int kPassRows = (kLds / NW) / kRowB >= 128 ? 128 : 64;
-    constexpr int kPasses = 128 / kPassRows;
+  auto store_tile = [&](auto mode_tag, uint8_t* dst, size_t row_stride, int row_lim, bool with_bias) {
+    constexpr int MODE = decltype(mode_tag)::value;
+    constexpr int kSElem = MODE == kOutGeluBf16 ? 2 : 4;   // staged bytes per element
+    constexpr int kOElem = MODE == kOutF32 ? 4 : 2;        // stored bytes per element
+    constexpr int kRowB = kWN * kSElem, kChunks = kRowB / 16;
+    constexpr int kPassRows = epilogue_pass_rows(kWM, kRowB, kLds / NW);
+    constexpr int kPasses = kWM / kPassRows;
     constexpr int kRowsPerInst = 64 / kChunks;
     uint8_t* my = lds + wave * (kPassRows * kRowB);
 #pragma unroll
@@ -421,7 +455,7 @@ __global__ __launch_bounds__(NW * 64, 1) void ffn_tiled_kernel(
           for (int imp = 0; imp < kPassRows / 32; ++imp) {
             const int im = pass * (kPassRows / 32) + imp;
             const int row = imp * 32 + fr;           // row within this pass
-            if constexpr (!F32) {
+            if constexpr (MODE == kOutGeluBf16) {
               const int chunk = jn * 4 + g;           // 16 B = 8 columns; fc picks the half
               uint32_t p[2];
 #pragma unroll
@@ -434,7 +468,10 @@ __global__ __launch_bounds__(NW * 64, 1) void ffn_tiled_kernel(
               const int chunk = jn * 8 + 2 * g + fc;  // 16 B = 4 columns
               f32x4 v;
 #pragma unroll
-              for (int q = 0; q < 4; ++q) v[q] = acc[jn][im][4 * g + q] + bv[q];
+              for (int q = 0; q < 4; ++q) {
+                v[q] = acc[jn][im][4 * g + q] + bv[q];
+                if constexpr (MODE == kOutGeluSplit) v[q] = gelu_erf(v[q]);
+              }
               *reinterpret_cast<f32x4*>(my + row * kRowB + ((chunk ^ (row & (kChunks - 1))) << 4)) = v;
             }
           }
@@ -443,43 +480,64 @@ __global__ __launch_bounds__(NW * 64, 1) void ffn_tiled_kernel(
 #pragma unroll 4
       for (int rb = 0; rb < kPassRows; rb += kRowsPerInst) {
         const int row = rb + lane / kChunks, chunk = lane % kChunks;
-        const int lrow = wm * 128 + pass * kPassRows + row;
+        const int lrow = wm * kWM + pass * kPassRows + row;
         const u32x4 v = ld16(my + row * kRowB + ((chunk ^ (row & (kChunks - 1))) << 4));
-        if (lrow < row_lim) st16(dst + ((size_t)lrow * row_stride + wn * kWN) * kElem + chunk * 16, v);
+        if (lrow < row_lim) {
+          if constexpr (MODE == kOutGeluSplit) {
+            // 4 fp32 GELU values -> 4 bf16 hi (8 B) and 4 bf16 lo (8 B).
+            uint32_t hi[2], lo[2];
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+              const float g0 = __uint_as_float(v[2 * h2]), g1 = __uint_as_float(v[2 * h2 + 1]);
+              hi[h2] = pack_bf16x2(g0, g1);
+              lo[h2] = pack_bf16x2(g0 - __uint_as_float(hi[h2] << 16),
+                                   g1 - __uint_as_float(hi[h2] & 0xffff0000u));
+            }
+            const size_t off = ((size_t)lrow * row_stride + wn * kWN) * kOElem + chunk * 8;
+            *reinterpret_cast<uint2*>(dst + off) = make_uint2(hi[0], hi[1]);
+            *reinterpret_cast<uint2*>(dst + out_plane * 2 + off) = make_uint2(lo[0], lo[1]);
+          } else {
+            st16(dst + ((size_t)lrow * row_stride + wn * kWN) * kOElem + chunk * 16, v);
+          }
+        }
       }
       if (kPasses > 1) __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // reads done before the next pass
     }
   };
+  using ModeBf16 = std::integral_constant<int, kOutGeluBf16>;
+  using ModeF32 = std::integral_constant<int, kOutF32>;
+  using ModeSplit = std::integral_constant<int, kOutGeluSplit>;
   if (job.parts > 1) {
-    store_tile(std::true_type{}, reinterpret_cast<uint8_t*>(partial + job.slot * kPartialTileFloats),
-               BN, r1 - r0, false);
+    store_tile(ModeF32{}, reinterpret_cast<uint8_t*>(partial + job.slot * kPartialTileFloats), BN,
+               r1 - r0, false);
   } else if constexpr (UP) {
-    store_tile(std::false_type{}, static_cast<uint8_t*>(out) + ((size_t)r0 * N + n0) * 2, N, r1 - r0,
+    using Mode = std::conditional_t<SPLIT, ModeSplit, ModeBf16>;
+    store_tile(Mode{}, static_cast<uint8_t*>(out) + ((size_t)r0 * N + n0) * 2, N, r1 - r0,
                bexp != nullptr);
   } else {
-    store_tile(std::true_type{}, static_cast<uint8_t*>(out) + ((size_t)r0 * N + n0) * 4, N, r1 - r0,
+    store_tile(ModeF32{}, static_cast<uint8_t*>(out) + ((size_t)r0 * N + n0) * 4, N, r1 - r0,
                bexp != nullptr);
   }
 }
 
 // Finish the tiles the tiled kernel split along k: block (x = b % 8, j = b / 8)
 // takes the j-th block of XCD x's tail round, i.e. part p of a split tile,
-// and completes rows [p * 256 / S, (p + 1) * 256 / S) of it: the S partial
+// and completes rows [p * BM / S, (p + 1) * BM / S) of it: the S partial
 // tiles summed in part order, plus the bias, then the product's epilogue.
-template <bool UP, int BN>
+template <bool UP, bool SPLIT, int BM, int BN>
 __global__ __launch_bounds__(256) void ffn_tile_reduce(
     const int32_t* __restrict__ offsets, const uint16_t* __restrict__ bias, void* __restrict__ out,
-    int E, int N, int K, const float* __restrict__ partial) {
+    size_t out_plane, int E, int N, int K, const float* __restrict__ partial) {
   const int ntn = N / BN, x = blockIdx.x % kXcds, j = blockIdx.x / kXcds;
   TileJob job;
-  if (!tile_job(offsets, E, ntn, K / kTBK, x + kXcds * (tail_start(offsets, E, ntn, x) + j), job) ||
+  if (!tile_job<BM>(offsets, E, ntn, K / kTBK, x + kXcds * (tail_start<BM>(offsets, E, ntn, x) + j), job) ||
       job.parts == 1)
     return;
   int e, r0, r1;
-  if (!find_mtile(offsets, E, kTBM, job.mt, e, r0, r1)) return;
+  if (!find_mtile(offsets, E, BM, job.mt, e, r0, r1)) return;
   const int n0 = job.nt * BN;
-  const int ra = job.part * kTBM / job.parts;
-  const int rb = min(r1 - r0, (job.part + 1) * kTBM / job.parts);
+  const int ra = job.part * BM / job.parts;
+  const int rb = min(r1 - r0, (job.part + 1) * BM / job.parts);
   const float* p0 = partial + (size_t)(job.slot - job.part) * kPartialTileFloats;
   const uint16_t* bexp = bias ? bias + (size_t)e * N + n0 : nullptr;
   constexpr int kQuads = BN / 4;
@@ -496,7 +554,10 @@ __global__ __launch_bounds__(256) void ffn_tile_reduce(
       v[3] += __uint_as_float(braw.y & 0xffff0000u);
     }
     const size_t idx = (size_t)(r0 + r) * N + n0 + c;
-    if constexpr (UP) {
+    if constexpr (UP && SPLIT) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) emit<uint16_t, true, true>(out, out_plane, idx + u, v[u]);
+    } else if constexpr (UP) {
       *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + idx) =
           make_uint2(pack_bf16x2(gelu_erf(v[0]), gelu_erf(v[1])), pack_bf16x2(gelu_erf(v[2]), gelu_erf(v[3])));
     } else {
@@ -788,36 +849,70 @@ hipError_t launch_dense_offsets(int32_t* offsets, int rows, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Rows per tile of the tiled kernel, from the host's bounds: 256 when experts
+// average at least 256 rows (and h is one bf16 plane); otherwise 160 when no
+// expert can exceed 160 rows but some may exceed 128 (an expert capacity in
+// (128, 160]), else 128.
+static int tile_rows(const FfnArgs& a) {
+  if (!a.split && (long)a.max_rows >= 256L * a.E) return 256;
+  return (a.max_rows_per_expert > 128 && a.max_rows_per_expert <= 160) ? 160 : 128;
+}
+
+// W stages: 3 for 256-row tiles (MFMA-bound: the loads hide behind the
+// matrix work); for the smaller, weight-bound tiles as many as the LDS holds
+// (at most 8), to keep more weight bytes in flight per CU.
+constexpr int tile_w_stages(int bm, int bn, int planes) {
+  return bm == 256 ? 3 : std::min(8, (160 * 1024 - 2 * bm * 128 * planes) / (bn * 128));
+}
+
+template <bool UP, bool SPLIT, int BM, int BN>
+static void launch_tiled_t(const FfnArgs& a, hipStream_t s) {
+  constexpr int WM = BM == 256 ? 2 : 1;
+  constexpr int WS = tile_w_stages(BM, BN, (SPLIT && !UP) ? 2 : 1);
+  // Upper bound on tiles: sum_e ceil(count_e/BM) <= ceil(R/BM) + E; the grid
+  // is a multiple of the XCD count and blocks past the real tile count exit.
+  // Per XCD at most ceil(max_mt * ntn / 8) entries, plus at most one round of
+  // tail-split blocks; blocks without a job exit at once.
+  const int max_mt = (a.max_rows + BM - 1) / BM + a.E;
+  const int per_xcd = (max_mt * (a.N / BN) + kXcds - 1) / kXcds + 1 + kCusPerXcd;
+  const uint16_t* A = static_cast<const uint16_t*>(a.a);
+  const uint16_t* A_lo = (SPLIT && !UP) ? A + a.plane : nullptr;
+  const uint16_t* W = static_cast<const uint16_t*>(a.w);
+  const uint16_t* B = static_cast<const uint16_t*>(a.bias);
+  ffn_tiled_kernel<UP, SPLIT, BM, BN, WM, WS><<<per_xcd * kXcds, 256, 0, s>>>(
+      A, A_lo, a.offsets, W, B, a.out, a.plane, a.E, a.N, a.K, a.partial);
+  ffn_tile_reduce<UP, SPLIT, BM, BN><<<kPartialSlots, 256, 0, s>>>(a.offsets, B, a.out, a.plane,
+                                                                   a.E, a.N, a.K, a.partial);
+}
+
+// Column tile: 256 when N allows it and the LDS holds the stages (a split A
+// operand doubles the A stages), else 128.
+template <bool UP, bool SPLIT, int BM>
+static void launch_tiled_bm(const FfnArgs& a, hipStream_t s) {
+  constexpr bool kWide = !(SPLIT && !UP);
+  if (kWide && a.N % 256 == 0) launch_tiled_t<UP, SPLIT, BM, kWide ? 256 : 128>(a, s);
+  else launch_tiled_t<UP, SPLIT, BM, 128>(a, s);
+}
+
+template <bool UP, bool SPLIT>
+static void launch_tiled(const FfnArgs& a, hipStream_t s) {
+  switch (tile_rows(a)) {
+    case 256:
+      if constexpr (!SPLIT) launch_tiled_bm<UP, false, 256>(a, s);
+      break;
+    case 160: launch_tiled_bm<UP, SPLIT, 160>(a, s); break;
+    default: launch_tiled_bm<UP, SPLIT, 128>(a, s); break;
+  }
+}
+
 hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
   if (a.path == MOE_FFN_TILED) {
-    // Upper bound on tiles: sum_e ceil(count_e/256) <= ceil(R/256) + E; the grid
-    // is a multiple of the XCD count and blocks past the real tile count exit.
-    const int max_mt = (a.max_rows + kTBM - 1) / kTBM + a.E;
-    const uint16_t* A = static_cast<const uint16_t*>(a.a);
-    const uint16_t* W = static_cast<const uint16_t*>(a.w);
-    const uint16_t* B = static_cast<const uint16_t*>(a.bias);
-    // Per XCD at most ceil(max_mt * ntn / 8) entries, plus at most one round of
-    // tail-split blocks; blocks without a job exit at once.
-    constexpr int NW = 4;
-    const int bn = a.N % 256 == 0 ? 256 : 128;
-    const int per_xcd = (max_mt * (a.N / bn) + kXcds - 1) / kXcds + 1 + kCusPerXcd;
-    const int grid = per_xcd * kXcds;
-    if (bn == 256) {
-      if (a.up) {
-        ffn_tiled_kernel<true, 256, NW><<<grid, NW * 64, 0, s>>>(A, a.offsets, W, B, a.out, a.E, a.N, a.K, a.partial);
-        ffn_tile_reduce<true, 256><<<kPartialSlots, 256, 0, s>>>(a.offsets, B, a.out, a.E, a.N, a.K, a.partial);
-      } else {
-        ffn_tiled_kernel<false, 256, NW><<<grid, NW * 64, 0, s>>>(A, a.offsets, W, B, a.out, a.E, a.N, a.K, a.partial);
-        ffn_tile_reduce<false, 256><<<kPartialSlots, 256, 0, s>>>(a.offsets, B, a.out, a.E, a.N, a.K, a.partial);
-      }
+    if (a.split) {
+      if (a.up) launch_tiled<true, true>(a, s);
+      else launch_tiled<false, true>(a, s);
     } else {
-      if (a.up) {
-        ffn_tiled_kernel<true, 128, 4><<<grid, 256, 0, s>>>(A, a.offsets, W, B, a.out, a.E, a.N, a.K, a.partial);
-        ffn_tile_reduce<true, 128><<<kPartialSlots, 256, 0, s>>>(a.offsets, B, a.out, a.E, a.N, a.K, a.partial);
-      } else {
-        ffn_tiled_kernel<false, 128, 4><<<grid, 256, 0, s>>>(A, a.offsets, W, B, a.out, a.E, a.N, a.K, a.partial);
-        ffn_tile_reduce<false, 128><<<kPartialSlots, 256, 0, s>>>(a.offsets, B, a.out, a.E, a.N, a.K, a.partial);
-      }
+      if (a.up) launch_tiled<true, false>(a, s);
+      else launch_tiled<false, false>(a, s);
     }
   } else if (a.bf16) {
     if (a.split) {

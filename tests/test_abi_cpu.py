@@ -75,7 +75,6 @@ def test_workspace_size_grows_with_shape():
     (dict(tokens=1 << 20, d_ff=4096), B.MOE_ERR_UNSUPPORTED),
     (dict(h_mode=3), B.MOE_ERR_INVALID),
     (dict(h_mode=B.MOE_H_SPLIT, dtype="f32"), B.MOE_ERR_INVALID),
-    (dict(h_mode=B.MOE_H_SPLIT, ffn_path=B.MOE_FFN_TILED), B.MOE_ERR_UNSUPPORTED),
     (dict(d_ff_shared=-128), B.MOE_ERR_INVALID),
     (dict(d_ff_shared=100), B.MOE_ERR_UNSUPPORTED),
     (dict(tokens=1 << 20, d_ff_shared=4096, top_k=1), B.MOE_ERR_UNSUPPORTED),
@@ -139,13 +138,14 @@ def test_missing_library_fails_loudly(tmp_path):
 
 
 def test_plan_resolution_of_the_named_workloads():
-    """AUTO: tiled kernel + bf16 h for prefill-sized layers, weight streaming + split h
-    for the rest; h_bytes follows the mode."""
+    """AUTO: tiled kernel + bf16 h for prefill-sized layers, tiled kernel + split h for
+    medium ones (64..255 rows per expert), weight streaming + split h below; h_bytes
+    follows the mode."""
     import synth
     want = {"toy_fp32": (B.MOE_FFN_STREAM, B.MOE_H_AUTO, 4),
             "mid_bf16": (B.MOE_FFN_TILED, B.MOE_H_BF16, 2),
             "mixtral_prefill_bf16": (B.MOE_FFN_TILED, B.MOE_H_BF16, 2),
-            "switch_capacity_bf16": (B.MOE_FFN_STREAM, B.MOE_H_SPLIT, 4),
+            "switch_capacity_bf16": (B.MOE_FFN_TILED, B.MOE_H_SPLIT, 4),
             "decode_bf16": (B.MOE_FFN_STREAM, B.MOE_H_SPLIT, 4)}
     for name, (path, hm, eb) in want.items():
         s = synth.WORKLOADS[name]

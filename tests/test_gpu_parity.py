@@ -123,6 +123,7 @@ def _ffn_inputs(spec, inp, ref):
 
 FFN_CASES = ([(n, moe.MOE_FFN_AUTO, moe.MOE_H_AUTO) for n in SMALL_NAMES] +
              [(n, moe.MOE_FFN_TILED, moe.MOE_H_BF16) for n in BF16_SMALL] +
+             [(n, moe.MOE_FFN_TILED, moe.MOE_H_SPLIT) for n in BF16_SMALL] +
              [(n, moe.MOE_FFN_STREAM, moe.MOE_H_BF16) for n in BF16_SMALL] +
              [(n, moe.MOE_FFN_STREAM, moe.MOE_H_SPLIT) for n in BF16_SMALL])
 
