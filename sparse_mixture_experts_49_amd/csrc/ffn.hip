@@ -244,7 +244,6 @@ __global__ __launch_bounds__(256, 1) void ffn_tiled_kernel(
   constexpr int kNT = kWN / 32;           // 32-column subtiles per wave
   constexpr int kWM = BM / WM;            // wave tile rows
   constexpr int kMT = kWM / 32;           // 32-row subtiles per wave
-  constexpr int kAF = kMT * kPl;          // A fragments per slice
   constexpr int kAPlane = BM * 128;       // bytes per A plane per stage
   constexpr int kAStage = kAPlane * kPl;
   constexpr int kBStage = BN * 128;
@@ -314,209 +313,229 @@ __global__ __launch_bounds__(256, 1) void ffn_tiled_kernel(
     for (int i = 0; i < kBInst; ++i) load_lds16_raw(b_src[i] + k0, base + (i * NW + wave) * 1024);
   };
 
-  f32x16 acc[kNT][kMT];
+  // Main loop and epilogue for a wave whose rows of the tile fill kMA of its
+  // kMT 32-row subtiles.  Tiles under 256 rows instantiate it for all kMT and
+  // for about half, so the padding past an expert's last row costs no MFMAs
+  // when the tile is at most half full; both versions run the same barriers.
+  // (The 256-row kernel keeps one version: a second one makes it spill.)
+  auto body = [&](auto ma_tag) {
+    constexpr int kMA = decltype(ma_tag)::value;
+    constexpr int kAFa = kMA * kPl;
+    f32x16 acc[kNT][kMA];
 #pragma unroll
-  for (int jn = 0; jn < kNT; ++jn)
+    for (int jn = 0; jn < kNT; ++jn)
 #pragma unroll
-    for (int im = 0; im < kMT; ++im)
+      for (int im = 0; im < kMA; ++im)
 #pragma unroll
-      for (int q = 0; q < 16; ++q) acc[jn][im][q] = 0.f;
+        for (int q = 0; q < 16; ++q) acc[jn][im][q] = 0.f;
 
-  // A k-step of 64 is four 16-wide MFMA slices; a half step is two slices.
-  // X holds half 0 of a step, Y half 1.  Fragment r of a half (r < kReads) is
-  // slice r / (kAF + kNT) of A fragment q (q < kAF: plane q / kMT, subtile
-  // q % kMT) or of W subtile q - kAF.
-  constexpr int kReads = 2 * (kAF + kNT);
-  constexpr int kMfmas = 2 * kMT * kNT * kPl;
-  static_assert(kReads % 2 == 0 && kReads / 2 <= kMfmas, "two reads per MFMA");
-  static_assert(kAInst <= kMfmas && kBInst <= kMfmas, "at most one load per MFMA");
-  u32x4 xa[2][kAF], xb[2][kNT], ya[2][kAF], yb[2][kNT];
-  auto read_at = [&](u32x4 (&fa)[2][kAF], u32x4 (&fb)[2][kNT], int sa_, int sb_, int half, int r) {
-    const int sl = r / (kAF + kNT), q = r % (kAF + kNT);
-    const int ch = (half * 2 + sl) * 2 + fc;     // 16 B chunk: 8 k of this slice
-    if (q < kAF) {
-      const int row = (q / kMT) * BM + wm * kWM + (q % kMT) * 32 + fr;
-      fa[sl][q] = ld16(lds + sa_ * kAStage + row * 128 + ((ch ^ ((row >> 1) & 7)) << 4));
-    } else {
-      const int row = wn * kWN + (q - kAF) * 32 + fr;
-      fb[sl][q - kAF] = ld16(lds + kBBase + sb_ * kBStage + row * 128 + ((ch ^ ((row >> 1) & 7)) << 4));
-    }
-  };
-  auto read_all = [&](u32x4 (&fa)[2][kAF], u32x4 (&fb)[2][kNT], int sa_, int sb_, int half) {
-#pragma unroll
-    for (int r = 0; r < kReads; ++r) read_at(fa, fb, sa_, sb_, half, r);
-  };
-  // MFMA m of a half: slice m / (kPl kNT kMT), then plane, W subtile, A subtile
-  // (fastest), so consecutive MFMAs update different accumulators.
-  auto mfma_at = [&](const u32x4 (&fa)[2][kAF], const u32x4 (&fb)[2][kNT], int m) {
-    constexpr int kPerSlice = kPl * kNT * kMT;
-    const int sl = m / kPerSlice, rem = m % kPerSlice;
-    const int p = rem / (kNT * kMT), jn = (rem / kMT) % kNT, im = rem % kMT;
-    acc[jn][im] = mfma32_bf16(fb[sl][jn], fa[sl][p * kMT + im], acc[jn][im]);
-  };
-  // One half step in a fixed instruction order: after each MFMA (whose
-  // operands were read in the previous half), up to two LDS reads of the next
-  // half's fragments, front-loaded so they return long before they are needed,
-  // and, evenly spread, this half's L global->LDS loads.  A wave waiting to
-  // issue a load cannot issue MFMAs, so loads are paced rather than burst.
-  auto half_step = [&](const u32x4 (&fa)[2][kAF], const u32x4 (&fb)[2][kNT], u32x4 (&na)[2][kAF],
-                       u32x4 (&nb)[2][kNT], int nsa, int nsb, int nhalf, auto load_fn, auto loads_tag) {
-    constexpr int L = decltype(loads_tag)::value;
-#pragma unroll
-    for (int m = 0; m < kMfmas; ++m) {
-      mfma_at(fa, fb, m);
-      if (2 * m < kReads) {
-        read_at(na, nb, nsa, nsb, nhalf, 2 * m);
-        read_at(na, nb, nsa, nsb, nhalf, 2 * m + 1);
+    // A k-step of 64 is four 16-wide MFMA slices; a half step is two slices.
+    // X holds half 0 of a step, Y half 1.  Fragment r of a half (r < kReads) is
+    // slice r / (kAFa + kNT) of A fragment q (q < kAFa: plane q / kMA, subtile
+    // q % kMA) or of W subtile q - kAFa.
+    constexpr int kReads = 2 * (kAFa + kNT);
+    constexpr int kMfmas = 2 * kMA * kNT * kPl;
+    static_assert(kReads % 2 == 0 && kReads / 2 <= kMfmas, "two reads per MFMA");
+    static_assert(kAInst <= kMfmas && kBInst <= kMfmas, "at most one load per MFMA");
+    u32x4 xa[2][kAFa], xb[2][kNT], ya[2][kAFa], yb[2][kNT];
+    auto read_at = [&](u32x4 (&fa)[2][kAFa], u32x4 (&fb)[2][kNT], int sa_, int sb_, int half, int r) {
+      const int sl = r / (kAFa + kNT), q = r % (kAFa + kNT);
+      const int ch = (half * 2 + sl) * 2 + fc;     // 16 B chunk: 8 k of this slice
+      if (q < kAFa) {
+        const int row = (q / kMA) * BM + wm * kWM + (q % kMA) * 32 + fr;
+        fa[sl][q] = ld16(lds + sa_ * kAStage + row * 128 + ((ch ^ ((row >> 1) & 7)) << 4));
+      } else {
+        const int row = wn * kWN + (q - kAFa) * 32 + fr;
+        fb[sl][q - kAFa] = ld16(lds + kBBase + sb_ * kBStage + row * 128 + ((ch ^ ((row >> 1) & 7)) << 4));
       }
-      if ((m + 1) * L / kMfmas > m * L / kMfmas) load_fn(m * L / kMfmas);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-  using LoadsA = std::integral_constant<int, kAInst>;
-  using LoadsB = std::integral_constant<int, kBInst>;
-  using NoLoads = std::integral_constant<int, 0>;
-
-  // Pipeline.  Step t's A tile sits in A stage t % 2, its W tile in W stage
-  // t % WS, and W runs WS - 1 steps ahead.  Per step t:
-  //   X <- half 0 of step t is in registers when step t starts;
-  //   first half: X MFMAs, reads of Y <- half 1 of step t, and the loads of W
-  //     for step t+WS-1 into W stage (t-1) % WS, which nobody reads any more
-  //     (it held step t-1, finished before the previous barrier);
-  //   wait for our LDS reads and for A and W of step t+1 (only W of step
-  //     t+WS-1, issued after both, may still be in flight), barrier;
-  //   second half: Y MFMAs, reads of X <- half 0 of step t+1, and the loads of
-  //     A for step t+2 into A stage t % 2 (every wave is done reading it).
-  // Loads complete in issue order.  The prologue issues A0, A1, W0 .. W(WS-2),
-  // so every wait counts whole W groups only.
-  issue_a(0, 0);
-  issue_a(1, 1);
+    };
+    auto read_all = [&](u32x4 (&fa)[2][kAFa], u32x4 (&fb)[2][kNT], int sa_, int sb_, int half) {
 #pragma unroll
-  for (int d = 0; d < WS - 1; ++d) issue_b(d, d);
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm((WS - 2) * kBInst));   // A0, A1 and W0 landed
-  __syncthreads();
-  read_all(xa, xb, 0, 0, 0);
-  int sa = 0, sb = 0;                                // stages of step kt
-  for (int kt = 0; kt < nk - 1; ++kt) {
-    const int sa1 = sa ^ 1, sb1 = sb == WS - 1 ? 0 : sb + 1, sbw = sb == 0 ? WS - 1 : sb - 1;
-    const int kbw = min(kt + WS - 1, nk - 1) * kTBK, kba = min(kt + 2, nk - 1) * kTBK;
-    half_step(xa, xb, ya, yb, sa, sb, 1,
-              [&](int i) { load_lds16_raw(b_src[i] + kbw, lds0 + kBBase + sbw * kBStage + (i * NW + wave) * 1024); },
-              LoadsB{});
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kBInst));
+      for (int r = 0; r < kReads; ++r) read_at(fa, fb, sa_, sb_, half, r);
+    };
+    // MFMA m of a half: slice m / (kPl kNT kMA), then plane, W subtile, A subtile
+    // (fastest), so consecutive MFMAs update different accumulators.
+    auto mfma_at = [&](const u32x4 (&fa)[2][kAFa], const u32x4 (&fb)[2][kNT], int m) {
+      constexpr int kPerSlice = kPl * kNT * kMA;
+      const int sl = m / kPerSlice, rem = m % kPerSlice;
+      const int p = rem / (kNT * kMA), jn = (rem / kMA) % kNT, im = rem % kMA;
+      acc[jn][im] = mfma32_bf16(fb[sl][jn], fa[sl][p * kMA + im], acc[jn][im]);
+    };
+    // One half step in a fixed instruction order: after each MFMA (whose
+    // operands were read in the previous half), up to two LDS reads of the next
+    // half's fragments, front-loaded so they return long before they are needed,
+    // and, evenly spread, this half's L global->LDS loads.  A wave waiting to
+    // issue a load cannot issue MFMAs, so loads are paced rather than burst.
+    auto half_step = [&](const u32x4 (&fa)[2][kAFa], const u32x4 (&fb)[2][kNT], u32x4 (&na)[2][kAFa],
+                         u32x4 (&nb)[2][kNT], int nsa, int nsb, int nhalf, auto load_fn, auto loads_tag) {
+      constexpr int L = decltype(loads_tag)::value;
+#pragma unroll
+      for (int m = 0; m < kMfmas; ++m) {
+        mfma_at(fa, fb, m);
+        if (2 * m < kReads) {
+          read_at(na, nb, nsa, nsb, nhalf, 2 * m);
+          read_at(na, nb, nsa, nsb, nhalf, 2 * m + 1);
+        }
+        if ((m + 1) * L / kMfmas > m * L / kMfmas) load_fn(m * L / kMfmas);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    using LoadsA = std::integral_constant<int, kAInst>;
+    using LoadsB = std::integral_constant<int, kBInst>;
+    using NoLoads = std::integral_constant<int, 0>;
+
+    // Pipeline.  Step t's A tile sits in A stage t % 2, its W tile in W stage
+    // t % WS, and W runs WS - 1 steps ahead.  Per step t:
+    //   X <- half 0 of step t is in registers when step t starts;
+    //   first half: X MFMAs, reads of Y <- half 1 of step t, and the loads of W
+    //     for step t+WS-1 into W stage (t-1) % WS, which nobody reads any more
+    //     (it held step t-1, finished before the previous barrier);
+    //   wait for our LDS reads and for A and W of step t+1 (only W of step
+    //     t+WS-1, issued after both, may still be in flight), barrier;
+    //   second half: Y MFMAs, reads of X <- half 0 of step t+1, and the loads of
+    //     A for step t+2 into A stage t % 2 (every wave is done reading it).
+    // Loads complete in issue order.  The prologue issues A0, A1, W0 .. W(WS-2),
+    // so every wait counts whole W groups only.
+    issue_a(0, 0);
+    issue_a(1, 1);
+#pragma unroll
+    for (int d = 0; d < WS - 1; ++d) issue_b(d, d);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm((WS - 2) * kBInst));   // A0, A1 and W0 landed
     __syncthreads();
-    half_step(ya, yb, xa, xb, sa1, sb1, 0,
-              [&](int i) { load_lds16_raw(a_src[i] + kba, lds0 + sa * kAStage + (i * NW + wave) * 1024); },
-              LoadsA{});
-    sa = sa1;
-    sb = sb1;
-  }
-  half_step(xa, xb, ya, yb, sa, sb, 1, [&](int) {}, NoLoads{});
-  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    read_all(xa, xb, 0, 0, 0);
+    int sa = 0, sb = 0;                                // stages of step kt
+    for (int kt = 0; kt < nk - 1; ++kt) {
+      const int sa1 = sa ^ 1, sb1 = sb == WS - 1 ? 0 : sb + 1, sbw = sb == 0 ? WS - 1 : sb - 1;
+      const int kbw = min(kt + WS - 1, nk - 1) * kTBK, kba = min(kt + 2, nk - 1) * kTBK;
+      half_step(xa, xb, ya, yb, sa, sb, 1,
+                [&](int i) { load_lds16_raw(b_src[i] + kbw, lds0 + kBBase + sbw * kBStage + (i * NW + wave) * 1024); },
+                LoadsB{});
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kBInst));
+      __syncthreads();
+      half_step(ya, yb, xa, xb, sa1, sb1, 0,
+                [&](int i) { load_lds16_raw(a_src[i] + kba, lds0 + sa * kAStage + (i * NW + wave) * 1024); },
+                LoadsA{});
+      sa = sa1;
+      sb = sb1;
+    }
+    half_step(xa, xb, ya, yb, sa, sb, 1, [&](int) {}, NoLoads{});
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
 #pragma unroll
-  for (int m = 0; m < kMfmas; ++m) mfma_at(ya, yb, m);
-  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-  __syncthreads();                                   // LDS free for the epilogue
+    for (int m = 0; m < kMfmas; ++m) mfma_at(ya, yb, m);
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    __syncthreads();                                   // LDS free for the epilogue
 
-  // Epilogue through LDS.  Lane (fr, fc) holds, for each 32x32 subtile (jn, im)
-  // and g = 0..3, row im*32 + fr and columns jn*32 + 8g + 4fc .. +3 of the
-  // wave's sub-tile.  Each wave stages rows in its own LDS region with 16 B
-  // chunks XOR-swizzled by row, then stores whole row segments of the rows
-  // below row_lim to dst (row stride in elements).  kOutGeluBf16 stages bf16;
-  // the other modes stage fp32 (kOutGeluSplit converts to hi + lo on the way
-  // out, the lo plane out_plane elements after the hi plane).
-  const uint16_t* bexp = bias ? bias + (size_t)e * N : nullptr;
-  auto bias4 = [&](int jn, int g, float (&bv)[4]) {
-    const int col = n0 + wn * kWN + jn * 32 + 8 * g + 4 * fc;
-    const uint2 braw = *reinterpret_cast<const uint2*>(bexp + col);
-    bv[0] = __uint_as_float(braw.x << 16);
-    bv[1] = __uint_as_float(braw.x & 0xffff0000u);
-    bv[2] = __uint_as_float(braw.y << 16);
-    bv[3] = __uint_as_float(braw.y & 0xffff0000u);
-  };
-  auto store_tile = [&](auto mode_tag, uint8_t* dst, size_t row_stride, int row_lim, bool with_bias) {
-    constexpr int MODE = decltype(mode_tag)::value;
-    constexpr int kSElem = MODE == kOutGeluBf16 ? 2 : 4;   // staged bytes per element
-    constexpr int kOElem = MODE == kOutF32 ? 4 : 2;        // stored bytes per element
-    constexpr int kRowB = kWN * kSElem, kChunks = kRowB / 16;
-    constexpr int kPassRows = epilogue_pass_rows(kWM, kRowB, kLds / NW);
-    constexpr int kPasses = kWM / kPassRows;
-    constexpr int kRowsPerInst = 64 / kChunks;
-    uint8_t* my = lds + wave * (kPassRows * kRowB);
+    // Epilogue through LDS.  Lane (fr, fc) holds, for each 32x32 subtile (jn, im)
+    // and g = 0..3, row im*32 + fr and columns jn*32 + 8g + 4fc .. +3 of the
+    // wave's sub-tile.  Each wave stages rows in its own LDS region with 16 B
+    // chunks XOR-swizzled by row, then stores whole row segments of the rows
+    // below row_lim to dst (row stride in elements).  kOutGeluBf16 stages bf16;
+    // the other modes stage fp32 (kOutGeluSplit converts to hi + lo on the way
+    // out, the lo plane out_plane elements after the hi plane).
+    const uint16_t* bexp = bias ? bias + (size_t)e * N : nullptr;
+    auto bias4 = [&](int jn, int g, float (&bv)[4]) {
+      const int col = n0 + wn * kWN + jn * 32 + 8 * g + 4 * fc;
+      const uint2 braw = *reinterpret_cast<const uint2*>(bexp + col);
+      bv[0] = __uint_as_float(braw.x << 16);
+      bv[1] = __uint_as_float(braw.x & 0xffff0000u);
+      bv[2] = __uint_as_float(braw.y << 16);
+      bv[3] = __uint_as_float(braw.y & 0xffff0000u);
+    };
+    auto store_tile = [&](auto mode_tag, uint8_t* dst, size_t row_stride, int row_lim, bool with_bias) {
+      constexpr int MODE = decltype(mode_tag)::value;
+      constexpr int kSElem = MODE == kOutGeluBf16 ? 2 : 4;   // staged bytes per element
+      constexpr int kOElem = MODE == kOutF32 ? 4 : 2;        // stored bytes per element
+      constexpr int kRowB = kWN * kSElem, kChunks = kRowB / 16;
+      constexpr int kPassRows = epilogue_pass_rows(kWM, kRowB, kLds / NW);
+      constexpr int kPasses = kWM / kPassRows;
+      constexpr int kRowsPerInst = 64 / kChunks;
+      uint8_t* my = lds + wave * (kPassRows * kRowB);
 #pragma unroll
-    for (int pass = 0; pass < kPasses; ++pass) {
+      for (int pass = 0; pass < kPasses; ++pass) {
+        if (pass * kPassRows >= kMA * 32) continue;    // rows past the active subtiles
 #pragma unroll
-      for (int jn = 0; jn < kNT; ++jn)
+        for (int jn = 0; jn < kNT; ++jn)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          float bv[4] = {0.f, 0.f, 0.f, 0.f};
-          if (with_bias) bias4(jn, g, bv);
+          for (int g = 0; g < 4; ++g) {
+            float bv[4] = {0.f, 0.f, 0.f, 0.f};
+            if (with_bias) bias4(jn, g, bv);
 #pragma unroll
-          for (int imp = 0; imp < kPassRows / 32; ++imp) {
-            const int im = pass * (kPassRows / 32) + imp;
-            const int row = imp * 32 + fr;           // row within this pass
-            if constexpr (MODE == kOutGeluBf16) {
-              const int chunk = jn * 4 + g;           // 16 B = 8 columns; fc picks the half
-              uint32_t p[2];
+            for (int imp = 0; imp < kPassRows / 32; ++imp) {
+              const int im = pass * (kPassRows / 32) + imp;
+              const int row = imp * 32 + fr;           // row within this pass
+              if (im >= kMA) continue;                 // never active: nothing to store
+              if constexpr (MODE == kOutGeluBf16) {
+                const int chunk = jn * 4 + g;           // 16 B = 8 columns; fc picks the half
+                uint32_t p[2];
 #pragma unroll
-              for (int h2 = 0; h2 < 2; ++h2)
-                p[h2] = pack_bf16x2(gelu_erf(acc[jn][im][4 * g + 2 * h2] + bv[2 * h2]),
-                                    gelu_erf(acc[jn][im][4 * g + 2 * h2 + 1] + bv[2 * h2 + 1]));
-              *reinterpret_cast<uint2*>(my + row * kRowB + ((chunk ^ (row & (kChunks - 1))) << 4) + fc * 8) =
-                  make_uint2(p[0], p[1]);
-            } else {
-              const int chunk = jn * 8 + 2 * g + fc;  // 16 B = 4 columns
-              f32x4 v;
+                for (int h2 = 0; h2 < 2; ++h2)
+                  p[h2] = pack_bf16x2(gelu_erf(acc[jn][im][4 * g + 2 * h2] + bv[2 * h2]),
+                                      gelu_erf(acc[jn][im][4 * g + 2 * h2 + 1] + bv[2 * h2 + 1]));
+                *reinterpret_cast<uint2*>(my + row * kRowB + ((chunk ^ (row & (kChunks - 1))) << 4) + fc * 8) =
+                    make_uint2(p[0], p[1]);
+              } else {
+                const int chunk = jn * 8 + 2 * g + fc;  // 16 B = 4 columns
+                f32x4 v;
 #pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                v[q] = acc[jn][im][4 * g + q] + bv[q];
-                if constexpr (MODE == kOutGeluSplit) v[q] = gelu_erf(v[q]);
+                for (int q = 0; q < 4; ++q) {
+                  v[q] = acc[jn][im][4 * g + q] + bv[q];
+                  if constexpr (MODE == kOutGeluSplit) v[q] = gelu_erf(v[q]);
+                }
+                *reinterpret_cast<f32x4*>(my + row * kRowB + ((chunk ^ (row & (kChunks - 1))) << 4)) = v;
               }
-              *reinterpret_cast<f32x4*>(my + row * kRowB + ((chunk ^ (row & (kChunks - 1))) << 4)) = v;
             }
           }
-        }
-      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);        // our own LDS writes are done
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);        // our own LDS writes are done
 #pragma unroll 4
-      for (int rb = 0; rb < kPassRows; rb += kRowsPerInst) {
-        const int row = rb + lane / kChunks, chunk = lane % kChunks;
-        const int lrow = wm * kWM + pass * kPassRows + row;
-        const u32x4 v = ld16(my + row * kRowB + ((chunk ^ (row & (kChunks - 1))) << 4));
-        if (lrow < row_lim) {
-          if constexpr (MODE == kOutGeluSplit) {
-            // 4 fp32 GELU values -> 4 bf16 hi (8 B) and 4 bf16 lo (8 B).
-            uint32_t hi[2], lo[2];
+        for (int rb = 0; rb < kPassRows; rb += kRowsPerInst) {
+          const int row = rb + lane / kChunks, chunk = lane % kChunks;
+          const int lrow = wm * kWM + pass * kPassRows + row;
+          const u32x4 v = ld16(my + row * kRowB + ((chunk ^ (row & (kChunks - 1))) << 4));
+          if (lrow < row_lim) {
+            if constexpr (MODE == kOutGeluSplit) {
+              // 4 fp32 GELU values -> 4 bf16 hi (8 B) and 4 bf16 lo (8 B).
+              uint32_t hi[2], lo[2];
 #pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
-              const float g0 = __uint_as_float(v[2 * h2]), g1 = __uint_as_float(v[2 * h2 + 1]);
-              hi[h2] = pack_bf16x2(g0, g1);
-              lo[h2] = pack_bf16x2(g0 - __uint_as_float(hi[h2] << 16),
-                                   g1 - __uint_as_float(hi[h2] & 0xffff0000u));
+              for (int h2 = 0; h2 < 2; ++h2) {
+                const float g0 = __uint_as_float(v[2 * h2]), g1 = __uint_as_float(v[2 * h2 + 1]);
+                hi[h2] = pack_bf16x2(g0, g1);
+                lo[h2] = pack_bf16x2(g0 - __uint_as_float(hi[h2] << 16),
+                                     g1 - __uint_as_float(hi[h2] & 0xffff0000u));
+              }
+              const size_t off = ((size_t)lrow * row_stride + wn * kWN) * kOElem + chunk * 8;
+              *reinterpret_cast<uint2*>(dst + off) = make_uint2(hi[0], hi[1]);
+              *reinterpret_cast<uint2*>(dst + out_plane * 2 + off) = make_uint2(lo[0], lo[1]);
+            } else {
+              st16(dst + ((size_t)lrow * row_stride + wn * kWN) * kOElem + chunk * 16, v);
             }
-            const size_t off = ((size_t)lrow * row_stride + wn * kWN) * kOElem + chunk * 8;
-            *reinterpret_cast<uint2*>(dst + off) = make_uint2(hi[0], hi[1]);
-            *reinterpret_cast<uint2*>(dst + out_plane * 2 + off) = make_uint2(lo[0], lo[1]);
-          } else {
-            st16(dst + ((size_t)lrow * row_stride + wn * kWN) * kOElem + chunk * 16, v);
           }
         }
+        if (kPasses > 1) __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // reads done before the next pass
       }
-      if (kPasses > 1) __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // reads done before the next pass
+    };
+    using ModeBf16 = std::integral_constant<int, kOutGeluBf16>;
+    using ModeF32 = std::integral_constant<int, kOutF32>;
+    using ModeSplit = std::integral_constant<int, kOutGeluSplit>;
+    if (job.parts > 1) {
+      store_tile(ModeF32{}, reinterpret_cast<uint8_t*>(partial + job.slot * kPartialTileFloats), BN,
+                 r1 - r0, false);
+    } else if constexpr (UP) {
+      using Mode = std::conditional_t<SPLIT, ModeSplit, ModeBf16>;
+      store_tile(Mode{}, static_cast<uint8_t*>(out) + ((size_t)r0 * N + n0) * 2, N, r1 - r0,
+                 bexp != nullptr);
+    } else {
+      store_tile(ModeF32{}, static_cast<uint8_t*>(out) + ((size_t)r0 * N + n0) * 4, N, r1 - r0,
+                 bexp != nullptr);
     }
   };
-  using ModeBf16 = std::integral_constant<int, kOutGeluBf16>;
-  using ModeF32 = std::integral_constant<int, kOutF32>;
-  using ModeSplit = std::integral_constant<int, kOutGeluSplit>;
-  if (job.parts > 1) {
-    store_tile(ModeF32{}, reinterpret_cast<uint8_t*>(partial + job.slot * kPartialTileFloats), BN,
-               r1 - r0, false);
-  } else if constexpr (UP) {
-    using Mode = std::conditional_t<SPLIT, ModeSplit, ModeBf16>;
-    store_tile(Mode{}, static_cast<uint8_t*>(out) + ((size_t)r0 * N + n0) * 2, N, r1 - r0,
-               bexp != nullptr);
+  const int act = __builtin_amdgcn_readfirstlane(min(kMT, max(0, (r1 - r0 - wm * kWM + 31) / 32)));
+  constexpr int kHalf = (kMT + 1) / 2;
+  if constexpr (BM == 256) {
+    (void)act;
+    body(std::integral_constant<int, kMT>{});
   } else {
-    store_tile(ModeF32{}, static_cast<uint8_t*>(out) + ((size_t)r0 * N + n0) * 4, N, r1 - r0,
-               bexp != nullptr);
+    if (act <= kHalf) body(std::integral_constant<int, kHalf>{});
+    else body(std::integral_constant<int, kMT>{});
   }
 }
 
