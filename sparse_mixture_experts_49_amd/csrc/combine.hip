@@ -14,14 +14,17 @@
 
 namespace moe {
 
+// Thread (blockIdx.y * 256 + threadIdx.x) of block row t sums four adjacent
+// columns of token t: its k expert-output loads are independent, so they are
+// all in flight at once, and a few tokens (decode) still spread over many waves.
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ o,
                                                       const int32_t* __restrict__ dest,
                                                       const float* __restrict__ topk_w,
                                                       const float* __restrict__ shared, int T,
                                                       int d, int k, float* __restrict__ y) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t = blockIdx.x * 4 + wave;
-  if (t >= T) return;
+  const int t = blockIdx.x;
+  const int v = blockIdx.y * 256 + threadIdx.x;   // float4 column group
+  if (v >= (d >> 2)) return;
   int dst[8];
   float w[8];
 #pragma unroll
@@ -29,26 +32,23 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     dst[s] = (s < k) ? dest[(size_t)t * k + s] : -1;
     w[s] = (s < k) ? topk_w[(size_t)t * k + s] : 0.f;
   }
-  const int nvec = d >> 2;
-  float* yr = y + (size_t)t * d;
-#pragma unroll 2
-  for (int v = lane; v < nvec; v += 64) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4 ov[8];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      if (dst[s] >= 0) {
-        const f32x4 ov = *reinterpret_cast<const f32x4*>(o + (size_t)dst[s] * d + (size_t)v * 4);
+  for (int s = 0; s < 8; ++s)
+    if (dst[s] >= 0) ov[s] = *reinterpret_cast<const f32x4*>(o + (size_t)dst[s] * d + (size_t)v * 4);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] = fmaf(w[s], ov[i], acc[i]);
-      }
-    }
-    if (shared) acc += *reinterpret_cast<const f32x4*>(shared + (size_t)t * d + (size_t)v * 4);
-    *reinterpret_cast<f32x4*>(yr + (size_t)v * 4) = acc;
-  }
+  for (int s = 0; s < 8; ++s)
+    if (dst[s] >= 0)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = fmaf(w[s], ov[s][i], acc[i]);
+  if (shared) acc += *reinterpret_cast<const f32x4*>(shared + (size_t)t * d + (size_t)v * 4);
+  *reinterpret_cast<f32x4*>(y + (size_t)t * d + (size_t)v * 4) = acc;
 }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
-  combine_kernel<<<(a.T + 3) / 4, 256, 0, s>>>(a.o, a.dest, a.topk_w, a.shared, a.T, a.d, a.k, a.y);
+  const dim3 grid(a.T, (a.d / 4 + 255) / 256);
+  combine_kernel<<<grid, 256, 0, s>>>(a.o, a.dest, a.topk_w, a.shared, a.T, a.d, a.k, a.y);
   return hipGetLastError();
 }
 

@@ -33,6 +33,41 @@ template <> struct Elem<uint16_t> {
   static __device__ __forceinline__ float to_f32(uint16_t v) { return bf16_to_f32(v); }
 };
 
+// Lanes e >= 0 (an expert id < 64; -1 = none) of a wave: the rank of this
+// lane among the lanes with the same id (lower lanes first), and in `cnt` the
+// size of that group.  The lanes whose id equals this lane's are the AND over
+// the six bits of the id of the bit's ballot, complemented where this lane's
+// bit is 0.  lt_mask = the lanes below this one.
+__device__ __forceinline__ int wave_rank(int e, uint64_t lt_mask, int& cnt) {
+  const uint64_t valid = __ballot(e >= 0);
+  uint32_t lo = (uint32_t)valid, hi = (uint32_t)(valid >> 32);
+#pragma unroll
+  for (int b = 0; b < 6; ++b) {
+    const uint64_t bb = __ballot((e >> b) & 1);
+    const uint32_t flip = ((uint32_t)(e >> b) & 1u) - 1u;   // 0 where the bit is set, else ~0
+    lo &= (uint32_t)bb ^ flip;
+    hi &= (uint32_t)(bb >> 32) ^ flip;
+  }
+  const uint64_t same = ((uint64_t)hi << 32) | lo;
+  cnt = __popcll(same);
+  return __popcll(same & lt_mask);
+}
+
+// Lanes e >= 0 (an expert id < 64; -1 = none) of a wave: how many lanes hold
+// id x, returned in lane x (the same bit-ballot match, against x's bits).
+__device__ __forceinline__ int wave_count_of_lane(int e, int lane) {
+  const uint64_t valid = __ballot(e >= 0);
+  uint32_t lo = (uint32_t)valid, hi = (uint32_t)(valid >> 32);
+#pragma unroll
+  for (int b = 0; b < 6; ++b) {
+    const uint64_t bb = __ballot((e >> b) & 1);
+    const uint32_t flip = ((uint32_t)(lane >> b) & 1u) - 1u;
+    lo &= (uint32_t)bb ^ flip;
+    hi &= (uint32_t)(bb >> 32) ^ flip;
+  }
+  return __popcll(((uint64_t)hi << 32) | lo);
+}
+
 // One 16x16 output tile, K = 32 (bf16) per instruction.  Operand lane layout:
 // lane l holds row/column (l % 16) and the 8 consecutive k-slots 8*(l/16)..+7.
 // Since the product sums over k, the kernels may map k-slots to any k as long

@@ -56,25 +56,6 @@ __device__ __forceinline__ int req_expert(int r) { return r & 0xff; }
 __device__ __forceinline__ int req_cursor(int r) { return (r >> 8) & 0xff; }
 __device__ __forceinline__ int req_slot(int r) { return (r >> 16) & 0xff; }
 
-// Rank of this lane's request among the wave's lanes asking the same expert
-// (lower lanes first), and in `cnt` the size of that group.  The lanes whose
-// id equals this lane's are the AND over the six bits of the id of the
-// bit's ballot, complemented where this lane's bit is 0 (ids < 64).
-__device__ __forceinline__ int wave_rank(int e, uint64_t lt_mask, int& cnt) {
-  const uint64_t valid = __ballot(e >= 0);
-  uint32_t lo = (uint32_t)valid, hi = (uint32_t)(valid >> 32);
-#pragma unroll
-  for (int b = 0; b < 6; ++b) {
-    const uint64_t bb = __ballot((e >> b) & 1);
-    const uint32_t flip = ((uint32_t)(e >> b) & 1u) - 1u;   // 0 where the bit is set, else ~0
-    lo &= (uint32_t)bb ^ flip;
-    hi &= (uint32_t)(bb >> 32) ^ flip;
-  }
-  const uint64_t same = ((uint64_t)hi << 32) | lo;
-  cnt = __popcll(same);
-  return __popcll(same & lt_mask);
-}
-
 // Quad-wide search: the best-ranked expert strictly below expert c (score
 // cv) in the ranking of the token's scores (higher score first, equal scores
 // by lower index), -1 if there is none.  Lane ql of the quad holds scores

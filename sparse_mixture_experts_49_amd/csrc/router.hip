@@ -60,27 +60,45 @@ __global__ __launch_bounds__(256) void router_kernel(
   for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nch = d / kChunk;
-  for (int ch = wave; ch < nch; ch += kRouterWaves) {
+  auto load_chunk = [&](int ch, u32x4 (&a)[4], u32x4 (&b)[NT][4]) {
     const int kk = ch * kChunk;
-    u32x4 a[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) a[q] = ld16(xrow + kk + q * kPerVec);
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      u32x4 b[4];
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) b[q] = ld16(wrow[nt] + kk + q * kPerVec);
+      for (int q = 0; q < 4; ++q) b[nt][q] = ld16(wrow[nt] + kk + q * kPerVec);
+  };
+  auto mma_chunk = [&](const u32x4 (&a)[4], const u32x4 (&b)[NT][4]) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
       if constexpr (sizeof(T) == 2) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[nt] = mfma_bf16(a[q], b[q], acc[nt]);
+        for (int q = 0; q < 4; ++q) acc[nt] = mfma_bf16(a[q], b[nt][q], acc[nt]);
       } else {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            acc[nt] = mfma_f32(__uint_as_float(a[q][i]), __uint_as_float(b[q][i]), acc[nt]);
+            acc[nt] = mfma_f32(__uint_as_float(a[q][i]), __uint_as_float(b[nt][q][i]), acc[nt]);
       }
     }
+  };
+  // Two chunks per iteration, both loaded before either is multiplied: with
+  // few tokens (decode) the loop is bound by load latency.  The chunks are
+  // accumulated in order ch = wave, wave + 4, ... either way.
+  int ch = wave;
+  for (; ch + kRouterWaves < nch; ch += 2 * kRouterWaves) {
+    u32x4 a0[4], b0[NT][4], a1[4], b1[NT][4];
+    load_chunk(ch, a0, b0);
+    load_chunk(ch + kRouterWaves, a1, b1);
+    mma_chunk(a0, b0);
+    mma_chunk(a1, b1);
+  }
+  if (ch < nch) {
+    u32x4 a0[4], b0[NT][4];
+    load_chunk(ch, a0, b0);
+    mma_chunk(a0, b0);
   }
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt)
