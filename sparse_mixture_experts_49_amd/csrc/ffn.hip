@@ -9,11 +9,11 @@
 //
 // Two kernels, chosen on the host from a bound on rows per expert (the
 // device-side counts are never read back):
-//   * ffn_tiled_kernel  -- many rows per expert (prefill): 256 x 256 output
-//     tiles, both operands loaded straight into LDS in 64-wide k-steps, bf16
-//     MFMA 16x16x32 with fp32 accumulation, double-buffered with one barrier
-//     per k-step, XCD-aware tile order.  Each block finds its expert from
-//     `offsets`.
+//   * ffn_tiled_kernel  -- many rows per expert: 256 x 256 (or x 128) output
+//     tiles for prefill, 160- or 128-row tiles from 64 rows per expert; both
+//     operands loaded straight into LDS in 64-wide k-steps, bf16 MFMA 32x32x16
+//     with fp32 accumulation, pipelined with one barrier per k-step, XCD-aware
+//     tile order.  Each block finds its expert from `offsets`.
 //   * ffn_stream_kernel -- few rows per expert (decode, many small experts):
 //     each wave streams its own 16*NWN rows of W_e straight from HBM into
 //     registers in the MFMA operand layout, while the block's (at most
