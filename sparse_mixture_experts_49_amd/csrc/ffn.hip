@@ -256,8 +256,9 @@ __global__ __launch_bounds__(256, 1) void ffn_tiled_kernel(
   static_assert(kLds <= 160 * 1024 && WS >= 3, "LDS");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kLds];
 
-  // ---- which tile ----
-  const int ntn = N / BN;
+  // ---- which tile ----  (N need not be a multiple of BN: the last n-tile's
+  // columns past N load the last W row and are not stored)
+  const int ntn = (N + BN - 1) / BN;
   TileJob job;
   if (!tile_job<BM>(offsets, E, ntn, K / kTBK, blockIdx.x, job)) return;
   const int mt = job.mt, nt = job.nt;
@@ -288,7 +289,7 @@ __global__ __launch_bounds__(256, 1) void ffn_tiled_kernel(
   for (int i = 0; i < kBInst; ++i) {
     const int row = (i * NW + wave) * 8 + (lane >> 3);
     const int c = (lane & 7) ^ ((row >> 1) & 7);
-    b_src[i] = Wexp + (size_t)(n0 + row) * K + c * 8;
+    b_src[i] = Wexp + (size_t)min(n0 + row, N - 1) * K + c * 8;
   }
   const int nk_all = K / kTBK;
   const int ks0 = (int)((long)job.part * nk_all / job.parts);
@@ -435,13 +436,14 @@ __global__ __launch_bounds__(256, 1) void ffn_tiled_kernel(
     const uint16_t* bexp = bias ? bias + (size_t)e * N : nullptr;
     auto bias4 = [&](int jn, int g, float (&bv)[4]) {
       const int col = n0 + wn * kWN + jn * 32 + 8 * g + 4 * fc;
-      const uint2 braw = *reinterpret_cast<const uint2*>(bexp + col);
+      const uint2 braw = col < N ? *reinterpret_cast<const uint2*>(bexp + col) : make_uint2(0u, 0u);
       bv[0] = __uint_as_float(braw.x << 16);
       bv[1] = __uint_as_float(braw.x & 0xffff0000u);
       bv[2] = __uint_as_float(braw.y << 16);
       bv[3] = __uint_as_float(braw.y & 0xffff0000u);
     };
-    auto store_tile = [&](auto mode_tag, uint8_t* dst, size_t row_stride, int row_lim, bool with_bias) {
+    auto store_tile = [&](auto mode_tag, uint8_t* dst, size_t row_stride, int row_lim, int col_lim,
+                          bool with_bias) {
       constexpr int MODE = decltype(mode_tag)::value;
       constexpr int kSElem = MODE == kOutGeluBf16 ? 2 : 4;   // staged bytes per element
       constexpr int kOElem = MODE == kOutF32 ? 4 : 2;        // stored bytes per element
@@ -491,7 +493,7 @@ __global__ __launch_bounds__(256, 1) void ffn_tiled_kernel(
           const int row = rb + lane / kChunks, chunk = lane % kChunks;
           const int lrow = wm * kWM + pass * kPassRows + row;
           const u32x4 v = ld16(my + row * kRowB + ((chunk ^ (row & (kChunks - 1))) << 4));
-          if (lrow < row_lim) {
+          if (lrow < row_lim && wn * kWN + chunk * (16 / kSElem) < col_lim) {
             if constexpr (MODE == kOutGeluSplit) {
               // 4 fp32 GELU values -> 4 bf16 hi (8 B) and 4 bf16 lo (8 B).
               uint32_t hi[2], lo[2];
@@ -518,13 +520,13 @@ __global__ __launch_bounds__(256, 1) void ffn_tiled_kernel(
     using ModeSplit = std::integral_constant<int, kOutGeluSplit>;
     if (job.parts > 1) {
       store_tile(ModeF32{}, reinterpret_cast<uint8_t*>(partial + job.slot * kPartialTileFloats), BN,
-                 r1 - r0, false);
+                 r1 - r0, BN, false);
     } else if constexpr (UP) {
       using Mode = std::conditional_t<SPLIT, ModeSplit, ModeBf16>;
-      store_tile(Mode{}, static_cast<uint8_t*>(out) + ((size_t)r0 * N + n0) * 2, N, r1 - r0,
+      store_tile(Mode{}, static_cast<uint8_t*>(out) + ((size_t)r0 * N + n0) * 2, N, r1 - r0, N - n0,
                  bexp != nullptr);
     } else {
-      store_tile(ModeF32{}, static_cast<uint8_t*>(out) + ((size_t)r0 * N + n0) * 4, N, r1 - r0,
+      store_tile(ModeF32{}, static_cast<uint8_t*>(out) + ((size_t)r0 * N + n0) * 4, N, r1 - r0, N - n0,
                  bexp != nullptr);
     }
   };
@@ -547,7 +549,7 @@ template <bool UP, bool SPLIT, int BM, int BN>
 __global__ __launch_bounds__(256) void ffn_tile_reduce(
     const int32_t* __restrict__ offsets, const uint16_t* __restrict__ bias, void* __restrict__ out,
     size_t out_plane, int E, int N, int K, const float* __restrict__ partial) {
-  const int ntn = N / BN, x = blockIdx.x % kXcds, j = blockIdx.x / kXcds;
+  const int ntn = (N + BN - 1) / BN, x = blockIdx.x % kXcds, j = blockIdx.x / kXcds;
   TileJob job;
   if (!tile_job<BM>(offsets, E, ntn, K / kTBK, x + kXcds * (tail_start<BM>(offsets, E, ntn, x) + j), job) ||
       job.parts == 1)
@@ -562,6 +564,7 @@ __global__ __launch_bounds__(256) void ffn_tile_reduce(
   constexpr int kQuads = BN / 4;
   for (int q = ra * kQuads + threadIdx.x; q < rb * kQuads; q += 256) {
     const int r = q / kQuads, c = (q % kQuads) * 4;
+    if (n0 + c >= N) continue;                      // past the last column
     f32x4 v = *reinterpret_cast<const f32x4*>(p0 + (size_t)r * BN + c);
     for (int sp = 1; sp < job.parts; ++sp)
       v += *reinterpret_cast<const f32x4*>(p0 + sp * kPartialTileFloats + (size_t)r * BN + c);
@@ -893,7 +896,7 @@ static void launch_tiled_t(const FfnArgs& a, hipStream_t s) {
   // Per XCD at most ceil(max_mt * ntn / 8) entries, plus at most one round of
   // tail-split blocks; blocks without a job exit at once.
   const int max_mt = (a.max_rows + BM - 1) / BM + a.E;
-  const int per_xcd = (max_mt * (a.N / BN) + kXcds - 1) / kXcds + 1 + kCusPerXcd;
+  const int per_xcd = (max_mt * ((a.N + BN - 1) / BN) + kXcds - 1) / kXcds + 1 + kCusPerXcd;
   const uint16_t* A = static_cast<const uint16_t*>(a.a);
   const uint16_t* A_lo = (SPLIT && !UP) ? A + a.plane : nullptr;
   const uint16_t* W = static_cast<const uint16_t*>(a.w);
@@ -904,12 +907,14 @@ static void launch_tiled_t(const FfnArgs& a, hipStream_t s) {
                                                                    a.E, a.N, a.K, a.partial);
 }
 
-// Column tile: 256 when N allows it and the LDS holds the stages (a split A
-// operand doubles the A stages), else 128.
+// Column tile: 256 when the LDS holds the stages (a split A operand doubles
+// the A stages) and N >= 256, else 128.  A 256-wide tile moves half the A
+// bytes per MFMA of a 128-wide one; when N is an odd multiple of 128 the last
+// n-tile is half padding, which costs less than 128-wide tiles throughout.
 template <bool UP, bool SPLIT, int BM>
 static void launch_tiled_bm(const FfnArgs& a, hipStream_t s) {
   constexpr bool kWide = !(SPLIT && !UP);
-  if (kWide && a.N % 256 == 0) launch_tiled_t<UP, SPLIT, BM, kWide ? 256 : 128>(a, s);
+  if (kWide && a.N >= 256) launch_tiled_t<UP, SPLIT, BM, kWide ? 256 : 128>(a, s);
   else launch_tiled_t<UP, SPLIT, BM, 128>(a, s);
 }
 

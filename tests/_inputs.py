@@ -43,6 +43,10 @@ SMALL = {
                                      W.capacity_for(300, 16), True, "bf16", router_bias=True,
                                      d_ff_shared=256),
     "shared_fp32": Workload("shared_fp32", 60, 128, 256, 8, 2, True, 0, True, "f32", d_ff_shared=384),
+    # widths that are odd multiples of 128 (the tiled kernel's last n-tile is half padding)
+    "odd_width_bf16": Workload("odd_width_bf16", 700, 384, 640, 8, 2, True, 0, True, "bf16"),
+    "odd_fine_shared_bf16": Workload("odd_fine_shared_bf16", 1200, 256, 384, 16, 6, True, 0, True,
+                                     "bf16", d_ff_shared=384),
     # capacity with top-2 (drop), and the reroute policy (top-1 and top-2, bf16 and fp32)
     "capacity_top2_bf16": Workload("capacity_top2_bf16", 400, 256, 512, 16, 2, True, 40, True,
                                    "bf16", router_bias=True),
