@@ -25,6 +25,10 @@
  * workspace sized by moe_workspace_size().  The library never allocates or
  * frees device memory, never synchronises the stream or the device, and
  * keeps no state between calls except a thread-local error message.
+ * Aliasing.  No output, the workspace included, may overlap another output or
+ * an input of the same call (byte ranges from the descriptor's shapes); a call
+ * that finds such an overlap returns MOE_ERR_INVALID.  moe_route's topk_idx
+ * counts as an output.
  * Streams.  `stream` is a hipStream_t passed as void* (NULL = the null
  * stream).  Every call only enqueues work on that stream, in order; buffers
  * must stay alive until the stream has passed that work.

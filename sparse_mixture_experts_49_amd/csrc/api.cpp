@@ -260,6 +260,107 @@ int check_ws(const moe_desc* d, void* ws, size_t bytes, Layout& L) {
   return MOE_OK;
 }
 
+// ---- aliasing -------------------------------------------------------------
+// Outputs (the workspace included) must be disjoint from each other and from
+// every input; a call that would write over its own operands is refused.
+
+struct Span {
+  const void* p;
+  size_t n;
+  const char* name;
+};
+
+struct Spans {
+  Span s[24];
+  int n = 0;
+  void add(const void* p, size_t bytes, const char* name) {
+    if (p && bytes && n < 24) s[n++] = Span{p, bytes, name};
+  }
+};
+
+bool overlaps(const Span& a, const Span& b) {
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+  return a0 < b0 + b.n && b0 < a0 + a.n;
+}
+
+int check_alias(const Spans& outs, const Spans& ins) {
+  for (int i = 0; i < outs.n; ++i) {
+    for (int j = i + 1; j < outs.n; ++j)
+      if (overlaps(outs.s[i], outs.s[j]))
+        return fail(MOE_ERR_INVALID, "%s overlaps %s", outs.s[i].name, outs.s[j].name);
+    for (int j = 0; j < ins.n; ++j)
+      if (overlaps(outs.s[i], ins.s[j]))
+        return fail(MOE_ERR_INVALID, "%s overlaps %s", outs.s[i].name, ins.s[j].name);
+  }
+  return MOE_OK;
+}
+
+// Byte sizes of the arrays a descriptor implies.
+struct Bytes {
+  size_t x, w_router, b_router, w1, b1, w2, b2, w1s, b1s, w2s, b2s;
+  size_t tk, e, e1, x_perm, h, o, y;
+};
+
+Bytes bytes_of(const moe_desc* d) {
+  const size_t T = d->tokens, D = d->d_model, F = d->d_ff, E = d->n_experts, k = d->top_k;
+  const size_t s = elem_bytes(d), Fs = d->d_ff_shared;
+  Plan p{};
+  resolve(d, p);
+  Bytes b{};
+  b.x = T * D * s;
+  b.w_router = E * D * s;
+  b.b_router = E * 4;
+  b.w1 = E * F * D * s;
+  b.b1 = E * F * s;
+  b.w2 = E * D * F * s;
+  b.b2 = E * D * s;
+  b.w1s = Fs * D * s;
+  b.b1s = Fs * s;
+  b.w2s = D * Fs * s;
+  b.b2s = D * s;
+  b.tk = T * k * 4;
+  b.e = E * 4;
+  b.e1 = (E + 1) * 4;
+  b.x_perm = T * k * D * s;
+  b.h = T * k * F * p.h_elem;
+  b.o = T * k * D * 4;
+  b.y = T * D * 4;
+  return b;
+}
+
+void add_weights(Spans& in, const moe_desc* d, const moe_weights* w, bool router, bool experts) {
+  const Bytes b = bytes_of(d);
+  if (router) {
+    in.add(w->w_router, b.w_router, "w_router");
+    in.add(w->b_router, b.b_router, "b_router");
+    in.add(w->b_select, b.b_router, "b_select");
+  }
+  if (experts) {
+    in.add(w->w1, b.w1, "w1");
+    in.add(w->b1, b.b1, "b1");
+    in.add(w->w2, b.w2, "w2");
+    in.add(w->b2, b.b2, "b2");
+    in.add(w->w1_shared, b.w1s, "w1_shared");
+    in.add(w->b1_shared, b.b1s, "b1_shared");
+    in.add(w->w2_shared, b.w2s, "w2_shared");
+    in.add(w->b2_shared, b.b2s, "b2_shared");
+  }
+}
+
+void add_routing_outputs(Spans& out, const moe_desc* d, const moe_routing& r) {
+  const Bytes b = bytes_of(d);
+  out.add(r.topk_idx, b.tk, "topk_idx");
+  out.add(r.topk_w, b.tk, "topk_w");
+  out.add(r.counts, b.e, "counts");
+  out.add(r.offsets, b.e1, "offsets");
+  out.add(r.dest, b.tk, "dest");
+  out.add(r.src, b.tk, "src");
+  out.add(r.top1_count, b.e, "top1_count");
+  out.add(r.prob_mean, b.e, "prob_mean");
+  out.add(r.z_loss, 4, "z_loss");
+  out.add(r.reroute_rounds, 4, "reroute_rounds");
+}
+
 int hip_status(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
   return ok();
@@ -451,6 +552,23 @@ int moe_route(const moe_desc* desc, const void* x, const moe_weights* w, moe_rou
   MOE_OPTIONAL_PTR(out->reroute_rounds, "out->reroute_rounds");
   Layout L;
   if (int st = check_ws(desc, ws, ws_bytes, L)) return st;
+  {
+    const Bytes b = bytes_of(desc);
+    Spans o, in;
+    moe_routing r{};
+    r.topk_idx = out->topk_idx;
+    r.topk_w = out->topk_w;
+    r.top1_count = out->top1_count;
+    r.prob_mean = out->prob_mean;
+    r.z_loss = out->z_loss;
+    r.reroute_rounds = out->reroute_rounds;
+    add_routing_outputs(o, desc, r);
+    o.add(aux, 4, "aux");
+    o.add(ws, ws_bytes, "workspace");
+    in.add(x, b.x, "x");
+    add_weights(in, desc, w, true, false);
+    if (int st = check_alias(o, in)) return st;
+  }
   return launch_route(desc, x, w, out->topk_idx, out->topk_w, out->top1_count, out->prob_mean,
                       aux, out->z_loss, out->reroute_rounds, L, ws,
                       static_cast<hipStream_t>(stream));
@@ -469,6 +587,19 @@ int moe_permute(const moe_desc* desc, const void* x, moe_routing* r, void* x_per
   MOE_REQUIRE_PTR(x_perm, "x_perm");
   Layout L;
   if (int st = check_ws(desc, ws, ws_bytes, L)) return st;
+  {
+    const Bytes b = bytes_of(desc);
+    Spans o, in;
+    o.add(r->counts, b.e, "counts");
+    o.add(r->offsets, b.e1, "offsets");
+    o.add(r->dest, b.tk, "dest");
+    o.add(r->src, b.tk, "src");
+    o.add(x_perm, b.x_perm, "x_perm");
+    o.add(ws, ws_bytes, "workspace");
+    in.add(x, b.x, "x");
+    in.add(r->topk_idx, b.tk, "topk_idx");
+    if (int st = check_alias(o, in)) return st;
+  }
   return launch_perm(desc, x, r->topk_idx, r->counts, r->offsets, r->dest, r->src, x_perm, L, ws,
                      static_cast<hipStream_t>(stream));
 }
@@ -482,6 +613,16 @@ int moe_ffn_up(const moe_desc* desc, const void* x_perm, const int32_t* offsets,
   if (int st = validate_weights(desc, w, false, true)) return st;
   Layout L;
   if (int st = check_ws(desc, ws, ws_bytes, L)) return st;
+  {
+    const Bytes b = bytes_of(desc);
+    Spans o, in;
+    o.add(h, b.h, "h");
+    o.add(ws, ws_bytes, "workspace");
+    in.add(x_perm, b.x_perm, "x_perm");
+    in.add(offsets, b.e1, "offsets");
+    add_weights(in, desc, w, false, true);
+    if (int st = check_alias(o, in)) return st;
+  }
   return launch_one_ffn(desc, true, x_perm, offsets, w, h, ws, L, static_cast<hipStream_t>(stream));
 }
 
@@ -494,6 +635,16 @@ int moe_ffn_down(const moe_desc* desc, const void* h, const int32_t* offsets,
   if (int st = validate_weights(desc, w, false, true)) return st;
   Layout L;
   if (int st = check_ws(desc, ws, ws_bytes, L)) return st;
+  {
+    const Bytes b = bytes_of(desc);
+    Spans out, in;
+    out.add(o, b.o, "o");
+    out.add(ws, ws_bytes, "workspace");
+    in.add(h, b.h, "h");
+    in.add(offsets, b.e1, "offsets");
+    add_weights(in, desc, w, false, true);
+    if (int st = check_alias(out, in)) return st;
+  }
   return launch_one_ffn(desc, false, h, offsets, w, o, ws, L, static_cast<hipStream_t>(stream));
 }
 
@@ -508,6 +659,17 @@ int moe_grouped_ffn(const moe_desc* desc, const void* x_perm, const int32_t* off
   if (int st = validate_weights(desc, w, false, true)) return st;
   Layout L;
   if (int st = check_ws(desc, ws, ws_bytes, L)) return st;
+  {
+    const Bytes b = bytes_of(desc);
+    Spans out, in;
+    out.add(h, b.h, "h");
+    out.add(o, b.o, "o");
+    out.add(ws, ws_bytes, "workspace");
+    in.add(x_perm, b.x_perm, "x_perm");
+    in.add(offsets, b.e1, "offsets");
+    add_weights(in, desc, w, false, true);
+    if (int st = check_alias(out, in)) return st;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (int st = launch_one_ffn(desc, true, x_perm, offsets, w, h, ws, L, s)) return st;
   return launch_one_ffn(desc, false, h, offsets, w, o, ws, L, s);
@@ -521,6 +683,16 @@ int moe_combine(const moe_desc* desc, const float* o, const int32_t* dest, const
   MOE_REQUIRE_PTR(topk_w, "topk_w");
   MOE_OPTIONAL_PTR(o_shared, "o_shared");
   MOE_REQUIRE_PTR(y, "y");
+  {
+    const Bytes b = bytes_of(desc);
+    Spans out, in;
+    out.add(y, b.y, "y");
+    in.add(o, b.o, "o");
+    in.add(dest, b.tk, "dest");
+    in.add(topk_w, b.tk, "topk_w");
+    in.add(o_shared, b.y, "o_shared");
+    if (int st = check_alias(out, in)) return st;
+  }
   return launch_comb(desc, o, dest, topk_w, o_shared, y, static_cast<hipStream_t>(stream));
 }
 
@@ -533,6 +705,15 @@ int moe_shared_ffn(const moe_desc* desc, const void* x, const moe_weights* w, fl
   if (int st = validate_weights(desc, w, false, true)) return st;
   Layout L;
   if (int st = check_ws(desc, ws, ws_bytes, L)) return st;
+  {
+    const Bytes b = bytes_of(desc);
+    Spans out, in;
+    out.add(o_shared, b.y, "o_shared");
+    out.add(ws, ws_bytes, "workspace");
+    in.add(x, b.x, "x");
+    add_weights(in, desc, w, false, true);
+    if (int st = check_alias(out, in)) return st;
+  }
   return launch_shared(desc, x, w, o_shared, ws, L, static_cast<hipStream_t>(stream));
 }
 
@@ -558,6 +739,17 @@ int moe_forward(const moe_desc* desc, const void* x, const moe_weights* w, float
   }
   Layout L;
   if (int st = check_ws(desc, ws, ws_bytes, L)) return st;
+  {
+    const Bytes b = bytes_of(desc);
+    Spans out, in;
+    out.add(y, b.y, "y");
+    out.add(aux, 4, "aux");
+    add_routing_outputs(out, desc, r);
+    out.add(ws, ws_bytes, "workspace");
+    in.add(x, b.x, "x");
+    add_weights(in, desc, w, true, true);
+    if (int st = check_alias(out, in)) return st;
+  }
   if (!r.topk_idx) r.topk_idx = at<int32_t>(ws, L.topk_idx);
   if (!r.topk_w) r.topk_w = at<float>(ws, L.topk_w);
   if (!r.counts) r.counts = at<int32_t>(ws, L.counts);

@@ -201,3 +201,51 @@ def test_reroute_rounds_pointer_alignment_is_checked():
     st = lib.moe_route(ctypes.byref(desc.to_c()), 0x1000, ctypes.byref(weights),
                        ctypes.byref(routing), None, 0x100000, _ws(desc), None)
     assert st == B.MOE_ERR_INVALID and "reroute_rounds" in lib.moe_last_error().decode()
+
+
+# ---- aliasing: outputs must not overlap inputs, each other or the workspace ----
+_D = moe.Desc(64, 256, 512, 8, 2)          # bf16: x = 64*256*2 B, o = 128*256*4 B
+
+
+def test_combine_refuses_y_overlapping_o():
+    lib = moe.load_library()
+    st = lib.moe_combine(ctypes.byref(_D.to_c()), 0x100000, 0x200000, 0x300000, None,
+                         0x100000 + 4096, None)
+    assert st == B.MOE_ERR_INVALID and "y overlaps o" in lib.moe_last_error().decode()
+
+
+def test_ffn_up_refuses_h_overlapping_a_weight():
+    lib = moe.load_library()
+    w = B.CWeights(0x10000, None, 0x4000000, 0x5000000, 0x6000000, 0x7000000)
+    # h starts inside w1 ([8][512][256] bf16 = 2 MiB from 0x4000000)
+    st = lib.moe_ffn_up(ctypes.byref(_D.to_c()), 0x1000000, 0x2000000, ctypes.byref(w),
+                        0x4000000 + 0x10000, 0x9000000, _ws(_D), None)
+    assert st == B.MOE_ERR_INVALID and "h overlaps w1" in lib.moe_last_error().decode()
+
+
+def test_forward_refuses_y_inside_the_workspace():
+    lib = moe.load_library()
+    w = B.CWeights(0x10000, None, 0x4000000, 0x5000000, 0x6000000, 0x7000000)
+    ws = 0x10000000
+    st = lib.moe_forward(ctypes.byref(_D.to_c()), 0x1000000, ctypes.byref(w), ws + 0x100, None,
+                         None, ws, _ws(_D), None)
+    assert st == B.MOE_ERR_INVALID and "overlaps workspace" in lib.moe_last_error().decode()
+
+
+def test_route_refuses_topk_w_overlapping_topk_idx():
+    lib = moe.load_library()
+    weights = B.CWeights(0x2000, None, None, None, None, None)
+    routing = B.CRouting(0x30000, 0x30000 + 256, None, None, None, None, None, None)
+    st = lib.moe_route(ctypes.byref(_D.to_c()), 0x100000, ctypes.byref(weights),
+                       ctypes.byref(routing), None, 0x1000000, _ws(_D), None)
+    assert st == B.MOE_ERR_INVALID and "overlaps" in lib.moe_last_error().decode()
+
+
+def test_disjoint_buffers_pass_the_alias_check():
+    """Adjacent but disjoint ranges are accepted: the call then fails only at the
+    launch (no GPU here) or succeeds on a GPU, never with an overlap error."""
+    lib = moe.load_library()
+    o_bytes = 128 * 256 * 4
+    st = lib.moe_combine(ctypes.byref(_D.to_c()), 0x100000, 0x100000 + o_bytes,
+                         0x100000 + o_bytes + 1024, None, 0x100000 + o_bytes + 2048, None)
+    assert "overlaps" not in lib.moe_last_error().decode()
