@@ -22,34 +22,42 @@ constexpr int kRouterTokens = 16;   // tokens per block (one MFMA row tile)
 constexpr int kAuxThreads = 512;    // threads of the single aux-reduction block
 constexpr int kRouterWaves = 4;     // the block's waves split d between them
 
-// One block = 16 tokens x all experts.  Wave w accumulates the k-chunks
-// w, w+4, w+8, ... of the d-long dot products; the four partial logit tiles
-// are summed in wave order through LDS, so the result does not depend on
-// scheduling.
+// LDS of one token tile: the waves' partial logits, then each token's
+// probabilities, first choice and log-sum-exp for the aux and z-loss sums.
+template <int WAVES>
+struct RouterTileLds {
+  float red[WAVES][kRouterTokens][65];
+  float prob[kRouterTokens][64];
+  int top1[kRouterTokens];
+  float lse[kRouterTokens];
+};
+
+// Tokens t0 .. t0+15 of the router: logits on MFMA (the WAVES waves split d),
+// softmax, top-k and the routing weights; fills sm.prob / top1 / lse.  Ends
+// with a barrier.  Wave w accumulates the k-chunks w, w+WAVES, ... of the
+// d-long dot products; the partial logit tiles are summed in wave order
+// through LDS, so the result does not depend on scheduling.
 //
 // Lane layout of the loads: lane l reads row (l % 16) -- a token of x, or an
 // expert row of W_r -- and 64 contiguous bytes starting at k-chunk offset
 // (l / 16) * 64 B, so each row's 256 B per chunk come from 4 lanes.  MFMA j of
 // the chunk consumes the lane's j-th 16-byte piece; A and B use the same map.
-template <typename T, int NT>
-__global__ __launch_bounds__(256) void router_kernel(
+template <typename T, int NT, int WAVES>
+__device__ __forceinline__ void route_tile(
     const T* __restrict__ x, const T* __restrict__ wr, const float* __restrict__ br,
-    const float* __restrict__ bsel, int T_, int d, int E, int k, int renorm,
-    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
-    double* __restrict__ part_psum, int32_t* __restrict__ part_top1, double* __restrict__ part_z,
-    float* __restrict__ rr_score, float* __restrict__ rr_wt) {
+    const float* __restrict__ bsel, int T_, int d, int E, int k, int renorm, int t0,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, float* __restrict__ rr_score,
+    float* __restrict__ rr_wt, RouterTileLds<WAVES>& sm) {
   constexpr int kPerLane = 64 / sizeof(T);          // elements per lane per chunk
   constexpr int kChunk = 4 * kPerLane;              // 128 bf16 or 64 fp32
   constexpr int kPerVec = 16 / sizeof(T);
-
-  __shared__ float red[kRouterWaves][kRouterTokens][65];
-  __shared__ float prob[kRouterTokens][64];
-  __shared__ int top1[kRouterTokens];
-  __shared__ float lse[kRouterTokens];
+  auto& red = sm.red;
+  auto& prob = sm.prob;
+  auto& top1 = sm.top1;
+  auto& lse = sm.lse;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, c = lane >> 4;
-  const int t0 = blockIdx.x * kRouterTokens;
   const T* xrow = x + (size_t)min(t0 + r, T_ - 1) * d + c * kPerLane;
   const T* wrow[NT];
 #pragma unroll
@@ -86,12 +94,12 @@ __global__ __launch_bounds__(256) void router_kernel(
   };
   // Two chunks per iteration, both loaded before either is multiplied: with
   // few tokens (decode) the loop is bound by load latency.  The chunks are
-  // accumulated in order ch = wave, wave + 4, ... either way.
+  // accumulated in order ch = wave, wave + WAVES, ... either way.
   int ch = wave;
-  for (; ch + kRouterWaves < nch; ch += 2 * kRouterWaves) {
+  for (; ch + WAVES < nch; ch += 2 * WAVES) {
     u32x4 a0[4], b0[NT][4], a1[4], b1[NT][4];
     load_chunk(ch, a0, b0);
-    load_chunk(ch + kRouterWaves, a1, b1);
+    load_chunk(ch + WAVES, a1, b1);
     mma_chunk(a0, b0);
     mma_chunk(a1, b1);
   }
@@ -118,7 +126,9 @@ __global__ __launch_bounds__(256) void router_kernel(
       const int e = q + 4 * j;
       g[j] = -INFINITY;
       if (e < E) {
-        g[j] = ((red[0][tq][e] + red[1][tq][e]) + red[2][tq][e]) + red[3][tq][e];
+        g[j] = red[0][tq][e];
+#pragma unroll
+        for (int w = 1; w < WAVES; ++w) g[j] += red[w][tq][e];   // in wave order
         if (br) g[j] += br[e];
         m = fmaxf(m, g[j]);
       }
@@ -208,7 +218,24 @@ __global__ __launch_bounds__(256) void router_kernel(
     if (q == 0) top1[tq] = (t < T_) ? sel_e[0] : -1;
   }
   __syncthreads();
+}
 
+// One block = 16 tokens x all experts, 4 waves splitting d.  The block then
+// writes its partial sums of the aux loss and z-loss for aux_finalize_kernel.
+template <typename T, int NT>
+__global__ __launch_bounds__(256) void router_kernel(
+    const T* __restrict__ x, const T* __restrict__ wr, const float* __restrict__ br,
+    const float* __restrict__ bsel, int T_, int d, int E, int k, int renorm,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+    double* __restrict__ part_psum, int32_t* __restrict__ part_top1, double* __restrict__ part_z,
+    float* __restrict__ rr_score, float* __restrict__ rr_wt) {
+  __shared__ RouterTileLds<kRouterWaves> sm;
+  const int t0 = blockIdx.x * kRouterTokens;
+  route_tile<T, NT, kRouterWaves>(x, wr, br, bsel, T_, d, E, k, renorm, t0, topk_idx, topk_w,
+                                  rr_score, rr_wt, sm);
+  auto& prob = sm.prob;
+  auto& top1 = sm.top1;
+  auto& lse = sm.lse;
   // Per-block partials of the aux loss, summed in token order.
   if (threadIdx.x < E) {
     const int e = threadIdx.x;
