@@ -19,8 +19,8 @@
 namespace moe {
 
 constexpr int kRouterTokens = 16;   // tokens per block (one MFMA row tile)
-constexpr int kAuxThreads = 512;    // threads of the single aux-reduction block
-constexpr int kRouterWaves = 4;     // the block's waves split d between them
+constexpr int kAuxThreads = 1024;   // threads of the single aux-reduction block
+constexpr int kRouterWaves = 8;     // the block's waves split d between them
 
 // LDS of one token tile: the waves' partial logits, then each token's
 // probabilities, first choice and log-sum-exp for the aux and z-loss sums.
@@ -220,10 +220,10 @@ __device__ __forceinline__ void route_tile(
   __syncthreads();
 }
 
-// One block = 16 tokens x all experts, 4 waves splitting d.  The block then
+// One block = 16 tokens x all experts, 8 waves splitting d.  The block then
 // writes its partial sums of the aux loss and z-loss for aux_finalize_kernel.
 template <typename T, int NT>
-__global__ __launch_bounds__(256) void router_kernel(
+__global__ __launch_bounds__(kRouterWaves * 64) void router_kernel(
     const T* __restrict__ x, const T* __restrict__ wr, const float* __restrict__ br,
     const float* __restrict__ bsel, int T_, int d, int E, int k, int renorm,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
@@ -270,23 +270,30 @@ __global__ __launch_bounds__(kAuxThreads) void aux_finalize_kernel(
   // The grouping depends only on (nblk, E), so the result is deterministic.
   __shared__ double ps[kAuxThreads];
   __shared__ long long pc[kAuxThreads];
-  __shared__ double pz[kAuxThreads];
   __shared__ double fP[64];
-  const int t = threadIdx.x;
+  __shared__ double wz[kAuxThreads / 64];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int stride = (kAuxThreads / E) * E;
   const long n = (long)nblk * E;
   double sum = 0.0;
   long long cnt = 0;
-  if (t < stride)
+  if (t < stride) {
+    // Unrolled so that several loads are in flight; the sum still runs in i order.
+#pragma unroll 8
     for (long i = t; i < n; i += stride) {
       sum += part_psum[i];
       cnt += part_top1[i];
     }
+  }
   ps[t] = sum;
   pc[t] = cnt;
   double zs = 0.0;                                   // z-loss: block partials t, t + threads, ...
+#pragma unroll 4
   for (int b = t; b < nblk; b += kAuxThreads) zs += part_z[b];
-  pz[t] = zs;
+  // Fixed shuffle tree per wave, then the waves in order.
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) zs += __shfl_down(zs, off);
+  if (lane == 0) wz[wave] = zs;
   __syncthreads();
   if (t < E) {
     double S = 0.0;
@@ -309,7 +316,7 @@ __global__ __launch_bounds__(kAuxThreads) void aux_finalize_kernel(
   if (t == 128 && rounds_zero) *rounds_zero = 0;
   if (t == 64 && z_loss) {
     double zt = 0.0;
-    for (int u = 0; u < kAuxThreads; ++u) zt += pz[u];
+    for (int w = 0; w < kAuxThreads / 64; ++w) zt += wz[w];
     *z_loss = (float)(zt / (double)T_);
   }
 }
@@ -322,10 +329,9 @@ static hipError_t launch_router_t(const RouterArgs& a, hipStream_t s) {
   const T* wr = static_cast<const T*>(a.w_router);
 #define MOE_ROUTER_CASE(NT)                                                                   \
   case NT:                                                                                  \
-    router_kernel<T, NT><<<nblk, 256, 0, s>>>(x, wr, a.b_router, a.b_select, a.T, a.d, a.E, \
-                                               a.k, a.renorm, a.topk_idx, a.topk_w,         \
-                                               a.part_psum, a.part_top1, a.part_z,          \
-                                               a.rr_score, a.rr_wt);                        \
+    router_kernel<T, NT><<<nblk, kRouterWaves * 64, 0, s>>>(                                  \
+        x, wr, a.b_router, a.b_select, a.T, a.d, a.E, a.k, a.renorm, a.topk_idx, a.topk_w,   \
+        a.part_psum, a.part_top1, a.part_z, a.rr_score, a.rr_wt);                             \
     break;
   switch (nt) {
     MOE_ROUTER_CASE(1)
