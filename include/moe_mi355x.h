@@ -72,8 +72,7 @@ enum {
 /* Expert-FFN kernel choice (moe_desc.ffn_path).  Averages are the host's bound,
  * min(T*k, E*C) / E rows per expert.  AUTO resolves to TILED (LDS-tiled, bf16
  * only) for bf16 layers averaging >= 64 rows per expert, with 256-row tiles from
- * 256 rows per expert (MFMA-bound prefill) and 128- or 160-row tiles below (a
- * 160-row tile covers a whole expert under a capacity in (128, 160]); and to
+ * 256 rows per expert (MFMA-bound prefill) and 128-row tiles below; and to
  * STREAM (weight-streaming, HBM-bound) otherwise. */
 enum { MOE_FFN_AUTO = 0, MOE_FFN_TILED = 1, MOE_FFN_STREAM = 2 };
 
@@ -87,7 +86,7 @@ enum { MOE_FFN_AUTO = 0, MOE_FFN_TILED = 1, MOE_FFN_STREAM = 2 };
  *                SPLIT below that and on the STREAM path, where the products
  *                are weight-bound and the second term costs little.
  * For an fp32 layer h is fp32 [T*k][F] and h_mode must be AUTO.  On the TILED
- * path SPLIT uses 128- or 160-row tiles. */
+ * path SPLIT uses 128-row tiles. */
 enum { MOE_H_AUTO = 0, MOE_H_BF16 = 1, MOE_H_SPLIT = 2 };
 
 /* What happens to assignments past an expert's capacity (moe_desc.capacity_policy).

@@ -131,6 +131,21 @@ int resolve(const moe_desc* d, Plan& p) {
   return MOE_OK;
 }
 
+// Rows per tile of the LDS-tiled kernel, from the descriptor: 256 when experts
+// average at least 256 rows and h is one bf16 plane (prefill, MFMA-bound).
+// Below that the products are weight-bound and every tile reads its expert's
+// W slice: 192-row tiles when the reroute policy fills every expert toward a
+// capacity in (128, 192], so one tile covers an expert; else 128-row tiles,
+// whose padding under a drop policy (loads well below the capacity) costs
+// less.  Measured on MI355X for the switch-style layer (64 experts, capacity
+// 160): 128 rows best when dropping, 192 when rerouting.
+int tile_rows(const moe_desc* d, bool split, int path_rows, int experts) {
+  if (!split && path_rows >= 256L * experts) return 256;
+  if (d->capacity_policy == MOE_CAPACITY_REROUTE && d->capacity > 128 && d->capacity <= 192)
+    return 192;
+  return 128;
+}
+
 // The shared expert is one dense product over all T tokens: the LDS-tiled
 // kernel with bf16 h when T >= 256 rows (bf16), else weight streaming with
 // split h (bf16) or fp32 h.
@@ -453,6 +468,7 @@ int launch_one_ffn(const moe_desc* d, bool up, const void* in, const int32_t* of
   a.max_rows_per_expert = row_bound(d);
   a.max_rows = max_rows(d);
   a.path = plan.path;
+  a.tile_rows = tile_rows(d, a.split, a.max_rows, a.E);
   a.partial = at<float>(ws, L.partial);
   return hip_status(moe::launch_ffn(a, s), up ? "ffn up launch" : "ffn down launch");
 }
@@ -474,6 +490,7 @@ int launch_shared(const moe_desc* d, const void* x, const moe_weights* w, float*
   a.max_rows_per_expert = d->tokens;
   a.max_rows = d->tokens;
   a.path = sh.path;
+  a.tile_rows = a.split || d->tokens < 256 ? 128 : 256;
   a.partial = at<float>(ws, L.partial);
   void* h = at<void>(ws, L.h_sh);
   a.up = true;

@@ -10,7 +10,7 @@
 // Two kernels, chosen on the host from a bound on rows per expert (the
 // device-side counts are never read back):
 //   * ffn_tiled_kernel  -- many rows per expert: 256 x 256 (or x 128) output
-//     tiles for prefill, 160- or 128-row tiles from 64 rows per expert; both
+//     tiles for prefill, 128- or 192-row tiles from 64 rows per expert; both
 //     operands loaded straight into LDS in 64-wide k-steps, bf16 MFMA 32x32x16
 //     with fp32 accumulation, pipelined with one barrier per k-step, XCD-aware
 //     tile order.  Each block finds its expert from `offsets`.
@@ -871,14 +871,6 @@ hipError_t launch_dense_offsets(int32_t* offsets, int rows, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Rows per tile of the tiled kernel, from the host's bounds: 256 when experts
-// average at least 256 rows (and h is one bf16 plane); otherwise 160 when no
-// expert can exceed 160 rows but some may exceed 128 (an expert capacity in
-// (128, 160]), else 128.
-static int tile_rows(const FfnArgs& a) {
-  if (!a.split && (long)a.max_rows >= 256L * a.E) return 256;
-  return (a.max_rows_per_expert > 128 && a.max_rows_per_expert <= 160) ? 160 : 128;
-}
 
 // W stages: 3 for 256-row tiles (MFMA-bound: the loads hide behind the
 // matrix work); for the smaller, weight-bound tiles as many as the LDS holds
@@ -889,7 +881,7 @@ constexpr int tile_w_stages(int bm, int bn, int planes) {
 
 template <bool UP, bool SPLIT, int BM, int BN>
 static void launch_tiled_t(const FfnArgs& a, hipStream_t s) {
-  constexpr int WM = BM == 256 ? 2 : 1;
+  constexpr int WM = 2;
   constexpr int WS = tile_w_stages(BM, BN, (SPLIT && !UP) ? 2 : 1);
   // Upper bound on tiles: sum_e ceil(count_e/BM) <= ceil(R/BM) + E; the grid
   // is a multiple of the XCD count and blocks past the real tile count exit.
@@ -918,13 +910,15 @@ static void launch_tiled_bm(const FfnArgs& a, hipStream_t s) {
   else launch_tiled_t<UP, SPLIT, BM, 128>(a, s);
 }
 
+// Rows per tile (FfnArgs::tile_rows, chosen by the caller): 256, 192 or 128,
+// all run as 2 x 2 waves.
 template <bool UP, bool SPLIT>
 static void launch_tiled(const FfnArgs& a, hipStream_t s) {
-  switch (tile_rows(a)) {
+  switch (a.tile_rows) {
     case 256:
       if constexpr (!SPLIT) launch_tiled_bm<UP, false, 256>(a, s);
       break;
-    case 160: launch_tiled_bm<UP, SPLIT, 160>(a, s); break;
+    case 192: launch_tiled_bm<UP, SPLIT, 192>(a, s); break;
     default: launch_tiled_bm<UP, SPLIT, 128>(a, s); break;
   }
 }
