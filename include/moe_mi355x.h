@@ -244,7 +244,8 @@ int moe_combine(const moe_desc* desc, const float* o, const int32_t* dest, const
                 const float* o_shared, float* y, void* stream);
 
 /* The whole layer: route, permute, grouped FFN, the shared expert (if any),
- * combine.
+ * combine.  The first expert product reads each dispatched row's token
+ * straight from x (through src), so no x_perm is materialised.
  *   x [T][d] dtype -> y [T][d] fp32 and *aux (device fp32 scalar, optional).
  *   routing may be NULL; any non-NULL field of it receives that result. */
 int moe_forward(const moe_desc* desc, const void* x, const moe_weights* w, float* y, float* aux,

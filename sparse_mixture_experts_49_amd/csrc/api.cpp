@@ -194,7 +194,7 @@ size_t elem_bytes(const moe_desc* d) { return d->dtype == MOE_DTYPE_BF16 ? 2 : 4
 struct Layout {
   size_t part_psum, part_top1, part_z, blk_hist, blk_base;
   size_t topk_idx, topk_w, counts, offsets, dest, src, top1, prob_mean;
-  size_t x_perm, h, o, partial;
+  size_t h, o, partial;
   size_t sh_offsets, h_sh, o_sh;   // shared expert (d_ff_shared > 0)
   size_t rr_score, rr_wt, rr_list;   // reroute policy
   size_t total;
@@ -222,7 +222,6 @@ Layout layout_of(const moe_desc* d) {
   L.src = take(A * 4);
   L.top1 = take(E * 4);
   L.prob_mean = take(E * 4);
-  L.x_perm = take(A * d->d_model * s);
   Plan plan{};
   resolve(d, plan);
   L.h = take(A * d->d_ff * plan.h_elem);
@@ -448,8 +447,11 @@ int launch_perm(const moe_desc* d, const void* x, const int32_t* idx, int32_t* c
   return hip_status(moe::launch_permute(a, s), "permute launch");
 }
 
+// One expert product.  gather (first product only, or null): `in` is x and
+// dispatched row r reads token gather[r] / top_k (gather = the dispatch's src).
 int launch_one_ffn(const moe_desc* d, bool up, const void* in, const int32_t* offsets,
-                   const moe_weights* w, void* out, void* ws, const Layout& L, hipStream_t s) {
+                   const moe_weights* w, void* out, void* ws, const Layout& L, hipStream_t s,
+                   const int32_t* gather = nullptr) {
   Plan plan{};
   if (int st = resolve(d, plan)) return st;
   moe::FfnArgs a{};
@@ -470,6 +472,8 @@ int launch_one_ffn(const moe_desc* d, bool up, const void* in, const int32_t* of
   a.path = plan.path;
   a.tile_rows = tile_rows(d, a.split, a.max_rows, a.E);
   a.partial = at<float>(ws, L.partial);
+  a.gather = gather;
+  a.gather_k = d->top_k;
   return hip_status(moe::launch_ffn(a, s), up ? "ffn up launch" : "ffn down launch");
 }
 
@@ -774,16 +778,17 @@ int moe_forward(const moe_desc* desc, const void* x, const moe_weights* w, float
   if (!r.dest) r.dest = at<int32_t>(ws, L.dest);
   if (!r.src) r.src = at<int32_t>(ws, L.src);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  void* x_perm = at<void>(ws, L.x_perm);
   void* h = at<void>(ws, L.h);
   float* o = at<float>(ws, L.o);
   if (int st = launch_route(desc, x, w, r.topk_idx, r.topk_w, r.top1_count, r.prob_mean, aux,
                             r.z_loss, r.reroute_rounds, L, ws, s))
     return st;
-  if (int st = launch_perm(desc, x, r.topk_idx, r.counts, r.offsets, r.dest, r.src, x_perm, L, ws,
+  // The dispatch layout only: the first product reads each row's token straight
+  // from x through src, so x_perm is never materialised.
+  if (int st = launch_perm(desc, x, r.topk_idx, r.counts, r.offsets, r.dest, r.src, nullptr, L, ws,
                            s))
     return st;
-  if (int st = launch_one_ffn(desc, true, x_perm, r.offsets, w, h, ws, L, s)) return st;
+  if (int st = launch_one_ffn(desc, true, x, r.offsets, w, h, ws, L, s, r.src)) return st;
   if (int st = launch_one_ffn(desc, false, h, r.offsets, w, o, ws, L, s)) return st;
   float* o_sh = nullptr;
   if (desc->d_ff_shared > 0) {

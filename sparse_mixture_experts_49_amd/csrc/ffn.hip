@@ -51,6 +51,13 @@ __device__ __forceinline__ bool find_mtile(const int32_t* __restrict__ offsets, 
   return false;
 }
 
+// Row of A holding dispatched row r: r itself, or -- when the first product
+// reads the tokens straight from x -- the token of assignment gather[r]
+// (gather = the dispatch's src array, gather_k = top_k).
+__device__ __forceinline__ int a_row(const int32_t* __restrict__ gather, int gather_k, int r) {
+  return gather ? gather[r] / gather_k : r;
+}
+
 template <typename T, bool UP>
 __device__ __forceinline__ void store_out(void* out, size_t idx, float v) {
   if constexpr (UP) {
@@ -236,7 +243,7 @@ __global__ __launch_bounds__(256, 1) void ffn_tiled_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ A_lo,
     const int32_t* __restrict__ offsets, const uint16_t* __restrict__ W,
     const uint16_t* __restrict__ bias, void* __restrict__ out, size_t out_plane, int E, int N,
-    int K, float* __restrict__ partial) {
+    int K, float* __restrict__ partial, const int32_t* __restrict__ gather, int gather_k) {
   constexpr int NW = 4;
   constexpr int kPl = (SPLIT && !UP) ? 2 : 1;   // A planes
   constexpr int kWavesN = NW / WM;
@@ -283,7 +290,7 @@ __global__ __launch_bounds__(256, 1) void ffn_tiled_kernel(
     const int lrow = (i * NW + wave) * 8 + (lane >> 3);
     const int plane = lrow / BM, row = lrow % BM;
     const int c = (lane & 7) ^ ((lrow >> 1) & 7);
-    a_src[i] = (plane ? A_lo : A) + (size_t)min(r0 + row, r1 - 1) * K + c * 8;
+    a_src[i] = (plane ? A_lo : A) + (size_t)a_row(gather, gather_k, min(r0 + row, r1 - 1)) * K + c * 8;
   }
 #pragma unroll
   for (int i = 0; i < kBInst; ++i) {
@@ -613,7 +620,8 @@ template <typename T, bool UP, bool SPLIT, int NMT, int NWN>
 __global__ __launch_bounds__(256) void ffn_stream_kernel(
     const T* __restrict__ A, const T* __restrict__ A_lo, const int32_t* __restrict__ offsets,
     const T* __restrict__ W, const T* __restrict__ bias, void* __restrict__ out,
-    size_t out_plane, int E, int N, int K, int splits, float* __restrict__ partial, int rows_cap) {
+    size_t out_plane, int E, int N, int K, int splits, float* __restrict__ partial, int rows_cap,
+    const int32_t* __restrict__ gather, int gather_k) {
   constexpr bool kTwoA = SPLIT && !UP;             // A operand is split h
   constexpr int kQ = kTwoA ? 2 : 4;                // 16 B pieces per lane per chunk
   constexpr int kPerVec = 16 / sizeof(T);
@@ -656,7 +664,7 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(
     const int row = (byte % kPlaneBytes) / kRowBytes;
     const int logical = ((byte % kRowBytes) / 16) ^ swz(row);
     const T* base = (kTwoA && plane) ? A_lo : A;
-    a_src[i] = base + (size_t)min(r0 + row, r1 - 1) * K + logical * kPerVec;
+    a_src[i] = base + (size_t)a_row(gather, gather_k, min(r0 + row, r1 - 1)) * K + logical * kPerVec;
   }
   const T* w_src[NWN];
   const T* Wexp = W + (size_t)e * N * K;
@@ -835,11 +843,13 @@ static void launch_stream_nmt(const FfnArgs& a, const StreamShape& sh, hipStream
   if (sh.nwn == 2) {
     dim3 grid(a.N / 128, a.E, z);
     ffn_stream_kernel<T, UP, SPLIT, NMT, 2><<<grid, 256, 0, s>>>(
-        A, A_lo, a.offsets, W, B, a.out, a.plane, a.E, a.N, a.K, sh.splits, a.partial, a.max_rows);
+        A, A_lo, a.offsets, W, B, a.out, a.plane, a.E, a.N, a.K, sh.splits, a.partial, a.max_rows,
+        a.gather, a.gather_k);
   } else {
     dim3 grid(a.N / 64, a.E, z);
     ffn_stream_kernel<T, UP, SPLIT, NMT, 1><<<grid, 256, 0, s>>>(
-        A, A_lo, a.offsets, W, B, a.out, a.plane, a.E, a.N, a.K, sh.splits, a.partial, a.max_rows);
+        A, A_lo, a.offsets, W, B, a.out, a.plane, a.E, a.N, a.K, sh.splits, a.partial, a.max_rows,
+        a.gather, a.gather_k);
   }
   if (sh.splits > 1) {
     const size_t quads = (size_t)a.max_rows * (a.N / 4);
@@ -894,7 +904,7 @@ static void launch_tiled_t(const FfnArgs& a, hipStream_t s) {
   const uint16_t* W = static_cast<const uint16_t*>(a.w);
   const uint16_t* B = static_cast<const uint16_t*>(a.bias);
   ffn_tiled_kernel<UP, SPLIT, BM, BN, WM, WS><<<per_xcd * kXcds, 256, 0, s>>>(
-      A, A_lo, a.offsets, W, B, a.out, a.plane, a.E, a.N, a.K, a.partial);
+      A, A_lo, a.offsets, W, B, a.out, a.plane, a.E, a.N, a.K, a.partial, a.gather, a.gather_k);
   ffn_tile_reduce<UP, SPLIT, BM, BN><<<kPartialSlots, 256, 0, s>>>(a.offsets, B, a.out, a.plane,
                                                                    a.E, a.N, a.K, a.partial);
 }

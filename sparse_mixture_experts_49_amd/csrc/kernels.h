@@ -73,6 +73,8 @@ struct FfnArgs {
   bool split;              // bf16 h kept as hi + lo planes (MOE_H_SPLIT)
   size_t plane;            // elements per h plane (T*k*F) when split
   float* partial;          // workspace for split-k partial sums (ffn_partial_bytes bytes)
+  const int32_t* gather;   // first product only, or null: A is x [T][K] and dispatched row r
+  int gather_k;            // reads token gather[r] / gather_k (gather = src, gather_k = top_k)
 };
 hipError_t launch_ffn(const FfnArgs& a, hipStream_t s);
 // Writes offsets = {0, rows}: the segment table of a dense product (one

@@ -239,7 +239,8 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t s) {
   const int A = a.T * a.k;
   const int row_bytes = a.d * (a.bf16 ? 2 : 4);
   if (A <= kPermChunk) {
-    perm_small_kernel<<<(a.T + 3) / 4, 256, 0, s>>>(
+    // Without x_perm only block 0's layout is needed.
+    perm_small_kernel<<<a.x_perm ? (a.T + 3) / 4 : 1, 256, 0, s>>>(
         a.topk_idx, a.T, a.k, a.E, a.capacity, a.counts, a.offsets, a.dest, a.src,
         static_cast<const uint8_t*>(a.x), row_bytes, static_cast<uint8_t*>(a.x_perm));
     return hipGetLastError();
