@@ -238,8 +238,8 @@ constexpr int kOutGeluSplit = 2;   // first product: GELU as bf16 hi + lo planes
 // SPLIT: the first product stores h as hi + lo planes; the second reads A as
 // those two planes (both in one A stage, plane 1 after plane 0) and runs one
 // MFMA per plane against the same W fragment.
-template <bool UP, bool SPLIT, int BM, int BN, int WM, int WS>
-__global__ __launch_bounds__(256, 1) void ffn_tiled_kernel(
+template <bool UP, bool SPLIT, int BM, int BN, int WM, int WS, int OCC>
+__global__ __launch_bounds__(256, OCC) void ffn_tiled_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ A_lo,
     const int32_t* __restrict__ offsets, const uint16_t* __restrict__ W,
     const uint16_t* __restrict__ bias, void* __restrict__ out, size_t out_plane, int E, int N,
@@ -892,7 +892,12 @@ constexpr int tile_w_stages(int bm, int bn, int planes) {
 template <bool UP, bool SPLIT, int BM, int BN>
 static void launch_tiled_t(const FfnArgs& a, hipStream_t s) {
   constexpr int WM = 2;
-  constexpr int WS = tile_w_stages(BM, BN, (SPLIT && !UP) ? 2 : 1);
+  // The split first product on 128 x 128 tiles runs two blocks per CU (80 KB
+  // of LDS each, three W stages): one block's two-plane GELU epilogue then
+  // overlaps the other's main loop.
+  constexpr bool kTwoPerCu = UP && SPLIT && BM == 128 && BN == 128;
+  constexpr int WS = kTwoPerCu ? 3 : tile_w_stages(BM, BN, (SPLIT && !UP) ? 2 : 1);
+  constexpr int OCC = kTwoPerCu ? 2 : 1;
   // Upper bound on tiles: sum_e ceil(count_e/BM) <= ceil(R/BM) + E; the grid
   // is a multiple of the XCD count and blocks past the real tile count exit.
   // Per XCD at most ceil(max_mt * ntn / 8) entries, plus at most one round of
@@ -903,7 +908,7 @@ static void launch_tiled_t(const FfnArgs& a, hipStream_t s) {
   const uint16_t* A_lo = (SPLIT && !UP) ? A + a.plane : nullptr;
   const uint16_t* W = static_cast<const uint16_t*>(a.w);
   const uint16_t* B = static_cast<const uint16_t*>(a.bias);
-  ffn_tiled_kernel<UP, SPLIT, BM, BN, WM, WS><<<per_xcd * kXcds, 256, 0, s>>>(
+  ffn_tiled_kernel<UP, SPLIT, BM, BN, WM, WS, OCC><<<per_xcd * kXcds, 256, 0, s>>>(
       A, A_lo, a.offsets, W, B, a.out, a.plane, a.E, a.N, a.K, a.partial, a.gather, a.gather_k);
   ffn_tile_reduce<UP, SPLIT, BM, BN><<<kPartialSlots, 256, 0, s>>>(a.offsets, B, a.out, a.plane,
                                                                    a.E, a.N, a.K, a.partial);
@@ -913,9 +918,11 @@ static void launch_tiled_t(const FfnArgs& a, hipStream_t s) {
 // the A stages) and N >= 256, else 128.  A 256-wide tile moves half the A
 // bytes per MFMA of a 128-wide one; when N is an odd multiple of 128 the last
 // n-tile is half padding, which costs less than 128-wide tiles throughout.
+// The split first product on 128-row tiles takes 128 columns so that two
+// blocks fit on a CU (measured faster than one 256-wide block).
 template <bool UP, bool SPLIT, int BM>
 static void launch_tiled_bm(const FfnArgs& a, hipStream_t s) {
-  constexpr bool kWide = !(SPLIT && !UP);
+  constexpr bool kWide = !SPLIT || (UP && BM != 128);
   if (kWide && a.N >= 256) launch_tiled_t<UP, SPLIT, BM, kWide ? 256 : 128>(a, s);
   else launch_tiled_t<UP, SPLIT, BM, 128>(a, s);
 }
