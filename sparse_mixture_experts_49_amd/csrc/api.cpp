@@ -131,19 +131,12 @@ int resolve(const moe_desc* d, Plan& p) {
   return MOE_OK;
 }
 
-// Rows per tile of the LDS-tiled kernel, from the descriptor: 256 when experts
-// average at least 256 rows and h is one bf16 plane (prefill, MFMA-bound).
-// Below that the products are weight-bound and every tile reads its expert's
-// W slice: 192-row tiles when the reroute policy fills every expert toward a
-// capacity in (128, 192], so one tile covers an expert; else 128-row tiles,
-// whose padding under a drop policy (loads well below the capacity) costs
-// less.  Measured on MI355X for the switch-style layer (64 experts, capacity
-// 160): 128 rows best when dropping, 192 when rerouting.
-int tile_rows(const moe_desc* d, bool split, int path_rows, int experts) {
-  if (!split && path_rows >= 256L * experts) return 256;
-  if (d->capacity_policy == MOE_CAPACITY_REROUTE && d->capacity > 128 && d->capacity <= 192)
-    return 192;
-  return 128;
+// Rows per tile of the LDS-tiled kernel: 256 when experts average at least
+// 256 rows and h is one bf16 plane (prefill, MFMA-bound), else 128.  Measured
+// on MI355X for the switch-style layer (64 experts, capacity 160), 128-row
+// tiles also beat 192-row ones when rerouting fills every expert to 160 rows.
+int tile_rows(bool split, int path_rows, int experts) {
+  return (!split && path_rows >= 256L * experts) ? 256 : 128;
 }
 
 // The shared expert is one dense product over all T tokens: the LDS-tiled
@@ -470,7 +463,7 @@ int launch_one_ffn(const moe_desc* d, bool up, const void* in, const int32_t* of
   a.max_rows_per_expert = row_bound(d);
   a.max_rows = max_rows(d);
   a.path = plan.path;
-  a.tile_rows = tile_rows(d, a.split, a.max_rows, a.E);
+  a.tile_rows = tile_rows(a.split, a.max_rows, a.E);
   a.partial = at<float>(ws, L.partial);
   a.gather = gather;
   a.gather_k = d->top_k;

@@ -10,7 +10,7 @@
 // Two kernels, chosen on the host from a bound on rows per expert (the
 // device-side counts are never read back):
 //   * ffn_tiled_kernel  -- many rows per expert: 256 x 256 (or x 128) output
-//     tiles for prefill, 128- or 192-row tiles from 64 rows per expert; both
+//     tiles for prefill, 128-row tiles from 64 rows per expert; both
 //     operands loaded straight into LDS in 64-wide k-steps, bf16 MFMA 32x32x16
 //     with fp32 accumulation, pipelined with one barrier per k-step, XCD-aware
 //     tile order.  Each block finds its expert from `offsets`.
@@ -914,30 +914,31 @@ static void launch_tiled_t(const FfnArgs& a, hipStream_t s) {
                                                                    a.E, a.N, a.K, a.partial);
 }
 
-// Column tile: 256 when the LDS holds the stages (a split A operand doubles
-// the A stages) and N >= 256, else 128.  A 256-wide tile moves half the A
-// bytes per MFMA of a 128-wide one; when N is an odd multiple of 128 the last
-// n-tile is half padding, which costs less than 128-wide tiles throughout.
-// The split first product on 128-row tiles takes 128 columns so that two
-// blocks fit on a CU (measured faster than one 256-wide block).
+// Column tile: 256 when N >= 256, else 128.  A 256-wide tile moves half the
+// A bytes per MFMA of a 128-wide one; when N is an odd multiple of 128 the
+// last n-tile is half padding, which costs less than 128-wide tiles
+// throughout.  The split second product (128-row tiles only) fits its two A
+// planes and three W stages in the LDS at 256 columns.  The split first
+// product takes 128 columns so that two blocks fit on a CU (measured faster
+// than one 256-wide block).
 template <bool UP, bool SPLIT, int BM>
 static void launch_tiled_bm(const FfnArgs& a, hipStream_t s) {
-  constexpr bool kWide = !SPLIT || (UP && BM != 128);
+  constexpr bool kWide = !(UP && SPLIT);
   if (kWide && a.N >= 256) launch_tiled_t<UP, SPLIT, BM, kWide ? 256 : 128>(a, s);
   else launch_tiled_t<UP, SPLIT, BM, 128>(a, s);
 }
 
-// Rows per tile (FfnArgs::tile_rows, chosen by the caller): 256, 192 or 128,
-// all run as 2 x 2 waves.
+// Rows per tile (FfnArgs::tile_rows, chosen by the caller): 256 (one h plane
+// only) or 128, both run as 2 x 2 waves.
 template <bool UP, bool SPLIT>
 static void launch_tiled(const FfnArgs& a, hipStream_t s) {
-  switch (a.tile_rows) {
-    case 256:
-      if constexpr (!SPLIT) launch_tiled_bm<UP, false, 256>(a, s);
-      break;
-    case 192: launch_tiled_bm<UP, SPLIT, 192>(a, s); break;
-    default: launch_tiled_bm<UP, SPLIT, 128>(a, s); break;
+  if constexpr (!SPLIT) {
+    if (a.tile_rows == 256) {
+      launch_tiled_bm<UP, false, 256>(a, s);
+      return;
+    }
   }
+  launch_tiled_bm<UP, SPLIT, 128>(a, s);
 }
 
 hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {

@@ -69,7 +69,7 @@ struct FfnArgs {
   int max_rows_per_expert; // host bound on any expert's rows (no device sync)
   int max_rows;            // host bound on the total rows R
   int path;                // resolved MOE_FFN_TILED or MOE_FFN_STREAM
-  int tile_rows;           // TILED: rows per tile, 256, 192 or 128 (256 needs one h plane)
+  int tile_rows;           // TILED: rows per tile, 256 or 128 (256 needs one h plane)
   bool split;              // bf16 h kept as hi + lo planes (MOE_H_SPLIT)
   size_t plane;            // elements per h plane (T*k*F) when split
   float* partial;          // workspace for split-k partial sums (ffn_partial_bytes bytes)

@@ -55,7 +55,7 @@ SMALL = {
                                   capacity_policy="reroute"),
     "reroute_top2_fp32": Workload("reroute_top2_fp32", 200, 128, 256, 8, 2, True, 40, True, "f32",
                                   router_bias=True, capacity_policy="reroute"),
-    # rerouting under a capacity in (128, 192]: 192-row tiles on the tiled path
+    # rerouting that fills experts past one 128-row tile (tiled path, split h)
     "reroute_c160_bf16": Workload("reroute_c160_bf16", 1400, 256, 384, 10, 1, False, 160, True,
                                   "bf16", router_bias=True, capacity_policy="reroute"),
     # the mid-size layer's shapes (4096 tokens, 16 experts) with a selection bias
