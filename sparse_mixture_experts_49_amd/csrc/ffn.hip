@@ -615,7 +615,15 @@ __global__ __launch_bounds__(256) void ffn_tile_reduce(
 //   - MFMA q of the chunk uses the lane's piece 4q + l / 16 of A (and of A's
 //     low term when h is split) and of W.
 // m-tiles past the block's last row issue no MFMA, so padding costs nothing.
+// Long weight rows (K >= kStreamRotateK): block x walks its chunks starting
+// at chunk (x % 4) * nch / 4 and wraps around, so the blocks in flight read
+// four different parts of their rows instead of the same column band
+// (measured on MI355X: ~3% faster weight streaming for the decode layer's
+// second product; for K = 4096 it was slower).  The sum order is fixed per
+// block, so results stay bitwise repeatable.
 // ---------------------------------------------------------------------------
+constexpr int kStreamRotateK = 8192;
+
 template <typename T, bool UP, bool SPLIT, int NMT, int NWN>
 __global__ __launch_bounds__(256) void ffn_stream_kernel(
     const T* __restrict__ A, const T* __restrict__ A_lo, const int32_t* __restrict__ offsets,
@@ -680,11 +688,14 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(
   const int nch_all = K / kChunk;
   const int c0 = (int)((long)split * nch_all / splits);
   const int nch = (int)((long)(split + 1) * nch_all / splits) - c0;
+  const int rot = K >= kStreamRotateK ? (int)((long)(blockIdx.x % 4) * nch / 4) : 0;
   const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
   u32x4 wbuf[kDepth][NWN][kQ];
-  // Issue chunk ch: W into register slot `slot`, A into LDS stage `slot`.
+  // Issue the block's chunk ch (chunk c0 + (ch + rot) mod nch of the row):
+  // W into register slot `slot`, A into LDS stage `slot`.
   auto issue = [&](u32x4 (&wdst)[NWN][kQ], int slot, int ch) {
-    const int k0 = (c0 + ch) * kChunk;
+    const int cr = ch + rot < nch ? ch + rot : ch + rot - nch;
+    const int k0 = (c0 + cr) * kChunk;
 #pragma unroll
     for (int j = 0; j < NWN; ++j)
 #pragma unroll

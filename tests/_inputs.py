@@ -58,6 +58,16 @@ SMALL = {
     # rerouting that fills experts past one 128-row tile (tiled path, split h)
     "reroute_c160_bf16": Workload("reroute_c160_bf16", 1400, 256, 384, 10, 1, False, 160, True,
                                   "bf16", router_bias=True, capacity_policy="reroute"),
+    # small batches on the weight-streaming path: bf16 with biases, with a shared
+    # expert, with a capacity no expert can reach (drop and reroute), ragged widths
+    "batch32_bf16": Workload("batch32_bf16", 32, 512, 1024, 8, 2, True, 0, True, "bf16"),
+    "batch48_shared_bf16": Workload("batch48_shared_bf16", 48, 256, 384, 8, 2, True, 0, True,
+                                    "bf16", d_ff_shared=256),
+    "batch24_cap_bf16": Workload("batch24_cap_bf16", 24, 256, 512, 4, 2, True, 30, True, "bf16"),
+    "batch40_reroute_bf16": Workload("batch40_reroute_bf16", 40, 256, 512, 8, 2, True, 40, True,
+                                     "bf16", capacity_policy="reroute"),
+    "batch64_top1_bf16": Workload("batch64_top1_bf16", 64, 384, 640, 16, 1, False, 0, False,
+                                  "bf16"),
     # the mid-size layer's shapes (4096 tokens, 16 experts) with a selection bias
     "mid_select_bias_bf16": Workload("mid_select_bias_bf16", 4096, 1024, 4096, 16, 2, True, 0, True,
                                      "bf16", selection_bias=True),
