@@ -373,10 +373,23 @@ int hip_status(hipError_t e, const char* what) {
   return ok();
 }
 
+// Dispatch layout outputs that the router's aux reduction fills for small
+// layers under the drop policy (see small_dispatch).
+struct LayoutOut {
+  int32_t *counts, *offsets, *dest, *src;
+};
+
+// Whether moe_forward takes the dispatch layout from the router's aux
+// reduction (one launch less): drop policy and at most 1024 assignments.
+bool small_dispatch(const moe_desc* d) {
+  return d->capacity_policy == MOE_CAPACITY_DROP && moe::router_can_permute(d->tokens * d->top_k);
+}
+
 // The router, then (MOE_CAPACITY_REROUTE) the rerouting of the overflow.
+// layout (small_dispatch layers only, or null): also the dispatch layout.
 int launch_route(const moe_desc* d, const void* x, const moe_weights* w, int32_t* idx, float* wt,
                  int32_t* top1, float* pmean, float* aux, float* zl, int32_t* rounds,
-                 const Layout& L, void* ws, hipStream_t s) {
+                 const Layout& L, void* ws, hipStream_t s, const LayoutOut* layout = nullptr) {
   const bool rr = d->capacity_policy == MOE_CAPACITY_REROUTE;
   moe::RouterArgs a{};
   a.bf16 = d->dtype == MOE_DTYPE_BF16;
@@ -401,6 +414,14 @@ int launch_route(const moe_desc* d, const void* x, const moe_weights* w, int32_t
   a.rr_score = rr ? at<float>(ws, L.rr_score) : nullptr;
   a.rr_wt = rr ? at<float>(ws, L.rr_wt) : nullptr;
   a.rounds_zero = rr ? nullptr : rounds;
+  if (layout) {
+    a.perm = true;
+    a.capacity = d->capacity;
+    a.counts = layout->counts;
+    a.offsets = layout->offsets;
+    a.dest = layout->dest;
+    a.src = layout->src;
+  }
   if (int st = hip_status(moe::launch_router(a, s), "router launch")) return st;
   if (!rr) return MOE_OK;
   moe::RerouteArgs b{};
@@ -440,11 +461,19 @@ int launch_perm(const moe_desc* d, const void* x, const int32_t* idx, int32_t* c
   return hip_status(moe::launch_permute(a, s), "permute launch");
 }
 
+// Split-k partial sums of the second product that the combine finishes.
+struct Deferred {
+  const float* partial = nullptr;
+  int splits = 1, rows_cap = 0;
+};
+
 // One expert product.  gather (first product only, or null): `in` is x and
 // dispatched row r reads token gather[r] / top_k (gather = the dispatch's src).
+// defer (second product only, or null): if the product splits k, its partial
+// sums are left for the combine and described in *defer.
 int launch_one_ffn(const moe_desc* d, bool up, const void* in, const int32_t* offsets,
                    const moe_weights* w, void* out, void* ws, const Layout& L, hipStream_t s,
-                   const int32_t* gather = nullptr) {
+                   const int32_t* gather = nullptr, Deferred* defer = nullptr) {
   Plan plan{};
   if (int st = resolve(d, plan)) return st;
   moe::FfnArgs a{};
@@ -467,6 +496,15 @@ int launch_one_ffn(const moe_desc* d, bool up, const void* in, const int32_t* of
   a.partial = at<float>(ws, L.partial);
   a.gather = gather;
   a.gather_k = d->top_k;
+  if (defer && !up) {
+    const int splits = moe::ffn_k_splits(a);
+    a.defer_reduce = splits > 1;
+    if (a.defer_reduce) {
+      defer->partial = a.partial;
+      defer->splits = splits;
+      defer->rows_cap = a.max_rows;
+    }
+  }
   return hip_status(moe::launch_ffn(a, s), up ? "ffn up launch" : "ffn down launch");
 }
 
@@ -509,8 +547,9 @@ int launch_shared(const moe_desc* d, const void* x, const moe_weights* w, float*
 }
 
 int launch_comb(const moe_desc* d, const float* o, const int32_t* dest, const float* wt,
-                const float* o_sh, float* y, hipStream_t s) {
-  moe::CombineArgs a{o, dest, wt, y, d->tokens, d->d_model, d->top_k, o_sh};
+                const float* o_sh, float* y, hipStream_t s, const Deferred& part = Deferred{}) {
+  moe::CombineArgs a{o,  dest, wt, y, d->tokens, d->d_model, d->top_k, o_sh, part.partial,
+                     part.splits, part.rows_cap};
   return hip_status(moe::launch_combine(a, s), "combine launch");
 }
 
@@ -773,22 +812,32 @@ int moe_forward(const moe_desc* desc, const void* x, const moe_weights* w, float
   hipStream_t s = static_cast<hipStream_t>(stream);
   void* h = at<void>(ws, L.h);
   float* o = at<float>(ws, L.o);
-  if (int st = launch_route(desc, x, w, r.topk_idx, r.topk_w, r.top1_count, r.prob_mean, aux,
-                            r.z_loss, r.reroute_rounds, L, ws, s))
-    return st;
   // The dispatch layout only: the first product reads each row's token straight
-  // from x through src, so x_perm is never materialised.
-  if (int st = launch_perm(desc, x, r.topk_idx, r.counts, r.offsets, r.dest, r.src, nullptr, L, ws,
-                           s))
+  // from x through src, so x_perm is never materialised.  Small layers get it
+  // from the router's aux reduction.
+  const LayoutOut layout{r.counts, r.offsets, r.dest, r.src};
+  const bool small = small_dispatch(desc);
+  if (int st = launch_route(desc, x, w, r.topk_idx, r.topk_w, r.top1_count, r.prob_mean, aux,
+                            r.z_loss, r.reroute_rounds, L, ws, s, small ? &layout : nullptr))
     return st;
+  if (!small) {
+    if (int st = launch_perm(desc, x, r.topk_idx, r.counts, r.offsets, r.dest, r.src, nullptr, L,
+                             ws, s))
+      return st;
+  }
   if (int st = launch_one_ffn(desc, true, x, r.offsets, w, h, ws, L, s, r.src)) return st;
-  if (int st = launch_one_ffn(desc, false, h, r.offsets, w, o, ws, L, s)) return st;
+  // The shared expert before the second routed product: both use the split-k
+  // partial region, and the second product may leave its partial sums there
+  // for the combine to finish (no separate reduction pass over o).
   float* o_sh = nullptr;
   if (desc->d_ff_shared > 0) {
     o_sh = at<float>(ws, L.o_sh);
     if (int st = launch_shared(desc, x, w, o_sh, ws, L, s)) return st;
   }
-  return launch_comb(desc, o, r.dest, r.topk_w, o_sh, y, s);
+  Deferred part;
+  if (int st = launch_one_ffn(desc, false, h, r.offsets, w, o, ws, L, s, nullptr, &part))
+    return st;
+  return launch_comb(desc, o, r.dest, r.topk_w, o_sh, y, s, part);
 }
 
 }  // extern "C"

@@ -9,6 +9,9 @@
 // connection outside the layer carries x).  A shared expert's output, when
 // given, is added after the slot sum (same page, section "Design variations":
 // shared experts are always active), also for tokens whose slots were dropped.
+// When the second expert product left its k-split partial sums unreduced, each
+// slot's row is summed here from them, in part order, exactly as the product's
+// own reduction would have stored it.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -21,7 +24,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                                                       const int32_t* __restrict__ dest,
                                                       const float* __restrict__ topk_w,
                                                       const float* __restrict__ shared, int T,
-                                                      int d, int k, float* __restrict__ y) {
+                                                      int d, int k, float* __restrict__ y,
+                                                      const float* __restrict__ partial, int splits,
+                                                      int rows_cap) {
   const int t = blockIdx.x;
   const int v = blockIdx.y * 256 + threadIdx.x;   // float4 column group
   if (v >= (d >> 2)) return;
@@ -33,9 +38,20 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     w[s] = (s < k) ? topk_w[(size_t)t * k + s] : 0.f;
   }
   f32x4 ov[8];
+  if (partial) {
 #pragma unroll
-  for (int s = 0; s < 8; ++s)
-    if (dst[s] >= 0) ov[s] = *reinterpret_cast<const f32x4*>(o + (size_t)dst[s] * d + (size_t)v * 4);
+    for (int s = 0; s < 8; ++s)
+      if (dst[s] >= 0) {
+        const float* p = partial + (size_t)dst[s] * d + (size_t)v * 4;
+        ov[s] = *reinterpret_cast<const f32x4*>(p);
+        for (int sp = 1; sp < splits; ++sp)
+          ov[s] += *reinterpret_cast<const f32x4*>(p + (size_t)sp * rows_cap * d);
+      }
+  } else {
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      if (dst[s] >= 0) ov[s] = *reinterpret_cast<const f32x4*>(o + (size_t)dst[s] * d + (size_t)v * 4);
+  }
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < 8; ++s)
@@ -48,7 +64,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
   const dim3 grid(a.T, (a.d / 4 + 255) / 256);
-  combine_kernel<<<grid, 256, 0, s>>>(a.o, a.dest, a.topk_w, a.shared, a.T, a.d, a.k, a.y);
+  combine_kernel<<<grid, 256, 0, s>>>(a.o, a.dest, a.topk_w, a.shared, a.T, a.d, a.k, a.y,
+                                      a.partial, a.splits, a.rows_cap);
   return hipGetLastError();
 }
 

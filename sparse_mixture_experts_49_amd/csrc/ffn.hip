@@ -862,7 +862,7 @@ static void launch_stream_nmt(const FfnArgs& a, const StreamShape& sh, hipStream
         A, A_lo, a.offsets, W, B, a.out, a.plane, a.E, a.N, a.K, sh.splits, a.partial, a.max_rows,
         a.gather, a.gather_k);
   }
-  if (sh.splits > 1) {
+  if (sh.splits > 1 && !(a.defer_reduce && !UP)) {
     const size_t quads = (size_t)a.max_rows * (a.N / 4);
     ffn_splitk_reduce<T, UP, SPLIT><<<(unsigned)((quads + 255) / 256), 256, 0, s>>>(
         a.partial, a.offsets, a.E, a.N, sh.splits, a.max_rows, a.out, a.plane);
@@ -950,6 +950,11 @@ static void launch_tiled(const FfnArgs& a, hipStream_t s) {
     }
   }
   launch_tiled_bm<UP, SPLIT, 128>(a, s);
+}
+
+int ffn_k_splits(const FfnArgs& a) {
+  if (a.path == MOE_FFN_TILED) return 1;
+  return stream_shape(a.bf16, a.up, a.split, a.E, a.N, a.K, a.max_rows_per_expert).splits;
 }
 
 hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {

@@ -25,7 +25,18 @@ struct RouterArgs {
   float* rr_score;         // [T][64] selection scores for the reroute policy (-inf past E), or null
   float* rr_wt;            // [T][E] the weight each expert would get (prob / denominator), or null
   int32_t* rounds_zero;    // optional: set to 0 (no reroute runs)
+  // Optional dispatch layout of a small layer (T*k <= 1024, drop policy), computed by
+  // the aux reduction block right after the router: counts, offsets, dest and src as
+  // the permute writes them, with `capacity` (0 = none).
+  bool perm;
+  int capacity;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* dest;
+  int32_t* src;
 };
+// Whether RouterArgs::perm may be used for T*k assignments.
+bool router_can_permute(int assignments);
 int router_blocks(int T);
 hipError_t launch_router(const RouterArgs& a, hipStream_t s);
 
@@ -75,8 +86,12 @@ struct FfnArgs {
   float* partial;          // workspace for split-k partial sums (ffn_partial_bytes bytes)
   const int32_t* gather;   // first product only, or null: A is x [T][K] and dispatched row r
   int gather_k;            // reads token gather[r] / gather_k (gather = src, gather_k = top_k)
+  bool defer_reduce;       // second product on the stream path: leave split-k partial sums in
+                           // `partial` ([splits][max_rows][N], bias in part 0) for the combine
 };
 hipError_t launch_ffn(const FfnArgs& a, hipStream_t s);
+// k parts the product of `a` is split into: > 1 only on the stream path.
+int ffn_k_splits(const FfnArgs& a);
 // Writes offsets = {0, rows}: the segment table of a dense product (one
 // "expert" owning every row), e.g. the shared expert over all tokens.
 hipError_t launch_dense_offsets(int32_t* offsets, int rows, hipStream_t s);
@@ -92,6 +107,8 @@ struct CombineArgs {
   float* y;
   int T, d, k;
   const float* shared;     // [T][d] shared expert output added after the slot sum, or null
+  const float* partial;    // or null: o is not stored, row r of o is the sum over p < splits
+  int splits, rows_cap;    // of partial[(p * rows_cap + r) * d + c], added in p order
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 

@@ -23,10 +23,9 @@
 // Expert ids outside [0, E) are treated as dropped assignments.
 #include "device_common.h"
 #include "kernels.h"
+#include "perm_small.h"
 
 namespace moe {
-
-constexpr int kPermChunk = 1024;   // assignments per block (4 waves x 4 batches x 64)
 
 int permute_blocks(int assignments) { return (assignments + kPermChunk - 1) / kPermChunk; }
 
@@ -155,75 +154,22 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(const uint8_t* __rest
   }
 }
 
-// All four steps for A <= kPermChunk assignments.  Wave w ranks assignments
-// w*256 .. +255 in four batches of 64 (lane e of the wave keeps its running
-// count of expert e); the per-wave counts give each expert's total, the
-// capacity clamp and the offsets; then every assignment gets its row.  Block b
+// All four steps for A <= kPermChunk assignments: every block builds the
+// layout in LDS (perm_small_layout), block 0 writes it out, and block b
 // scatters tokens 4b .. 4b+3, one wave each.
 __global__ __launch_bounds__(256) void perm_small_kernel(
     const int32_t* __restrict__ topk_idx, int T, int k, int E, int capacity,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ dest,
     int32_t* __restrict__ src, const uint8_t* __restrict__ x, int row_bytes,
     uint8_t* __restrict__ x_perm) {
-  __shared__ int wcount[4][64];
-  __shared__ int s_off[65];
-  __shared__ int s_dest[kPermChunk];
+  __shared__ PermSmallLds sm;
+  perm_small_layout(topk_idx, T, k, E, capacity, blockIdx.x == 0, counts, offsets, dest, src, sm);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int A = T * k;
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  int ex[4], rk[4], run = 0;
-#pragma unroll
-  for (int bt = 0; bt < 4; ++bt) {
-    const int a = wave * 256 + bt * 64 + lane;
-    int e = (a < A) ? topk_idx[a] : -1;
-    if (e < 0 || e >= E) e = -1;
-    int cnt;
-    const int r = wave_rank(e, lt_mask, cnt);
-    ex[bt] = e;
-    rk[bt] = __shfl(run, e >= 0 ? e : 0) + r;   // this wave's earlier batches + rank in this one
-    run += wave_count_of_lane(e, lane);         // lane x: requests for expert x in this batch
-  }
-  wcount[wave][lane] = run;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int acc = 0;
-    for (int e = 0; e < E; ++e) {
-      const int tot = wcount[0][e] + wcount[1][e] + wcount[2][e] + wcount[3][e];
-      const int kept = capacity > 0 ? min(tot, capacity) : tot;
-      s_off[e] = acc;
-      if (blockIdx.x == 0) {
-        offsets[e] = acc;
-        counts[e] = kept;
-      }
-      acc += kept;
-    }
-    s_off[E] = acc;
-    if (blockIdx.x == 0) offsets[E] = acc;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int bt = 0; bt < 4; ++bt) {
-    const int a = wave * 256 + bt * 64 + lane;
-    if (a >= A) continue;
-    const int e = ex[bt];
-    int row = -1;
-    if (e >= 0) {
-      int r = rk[bt];
-      for (int w = 0; w < wave; ++w) r += wcount[w][e];
-      if (capacity <= 0 || r < capacity) row = s_off[e] + r;
-    }
-    s_dest[a] = row;
-    if (blockIdx.x == 0) {
-      dest[a] = row;
-      if (row >= 0) src[row] = a;
-    }
-  }
-  __syncthreads();
   const int t = blockIdx.x * 4 + wave;
   if (t >= T || !x_perm) return;
   int dst[8];
 #pragma unroll
-  for (int sl = 0; sl < 8; ++sl) dst[sl] = (sl < k) ? s_dest[t * k + sl] : -1;
+  for (int sl = 0; sl < 8; ++sl) dst[sl] = (sl < k) ? sm.s_dest[t * k + sl] : -1;
   const uint8_t* xr = x + (size_t)t * row_bytes;
   const int nvec = row_bytes >> 4;
 #pragma unroll 4

@@ -15,6 +15,7 @@
 // squared log-sum-exp of the logits (same section: router z-loss).
 #include "device_common.h"
 #include "kernels.h"
+#include "perm_small.h"
 
 namespace moe {
 
@@ -263,7 +264,9 @@ __global__ __launch_bounds__(kAuxThreads) void aux_finalize_kernel(
     const double* __restrict__ part_psum, const int32_t* __restrict__ part_top1,
     const double* __restrict__ part_z, int nblk, int T_, int E, int32_t* __restrict__ top1_count,
     float* __restrict__ prob_mean, float* __restrict__ aux, float* __restrict__ z_loss,
-    int32_t* __restrict__ rounds_zero) {
+    int32_t* __restrict__ rounds_zero, const int32_t* __restrict__ topk_idx, int k, bool perm,
+    int capacity, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ dest, int32_t* __restrict__ src) {
   // The partials are [nblk][E] laid out flat.  Thread t < stride (a multiple of
   // E) sums entries t, t + stride, ... (all of expert t % E, coalesced across
   // the block); expert e's per-thread sums are then added in thread order.
@@ -272,6 +275,7 @@ __global__ __launch_bounds__(kAuxThreads) void aux_finalize_kernel(
   __shared__ long long pc[kAuxThreads];
   __shared__ double fP[64];
   __shared__ double wz[kAuxThreads / 64];
+  __shared__ PermSmallLds psm;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int stride = (kAuxThreads / E) * E;
   const long n = (long)nblk * E;
@@ -319,7 +323,11 @@ __global__ __launch_bounds__(kAuxThreads) void aux_finalize_kernel(
     for (int w = 0; w < kAuxThreads / 64; ++w) zt += wz[w];
     *z_loss = (float)(zt / (double)T_);
   }
+  // Small layers: the dispatch layout too, saving the permute's own launch.
+  if (perm) perm_small_layout(topk_idx, T_, k, E, capacity, true, counts, offsets, dest, src, psm);
 }
+
+bool router_can_permute(int assignments) { return assignments <= kPermChunk; }
 
 template <typename T>
 static hipError_t launch_router_t(const RouterArgs& a, hipStream_t s) {
@@ -343,9 +351,11 @@ static hipError_t launch_router_t(const RouterArgs& a, hipStream_t s) {
 #undef MOE_ROUTER_CASE
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
+  if (a.perm && !router_can_permute(a.T * a.k)) return hipErrorInvalidValue;
   aux_finalize_kernel<<<1, kAuxThreads, 0, s>>>(a.part_psum, a.part_top1, a.part_z, nblk, a.T, a.E,
                                                 a.top1_count, a.prob_mean, a.aux, a.z_loss,
-                                                a.rounds_zero);
+                                                a.rounds_zero, a.topk_idx, a.k, a.perm, a.capacity,
+                                                a.counts, a.offsets, a.dest, a.src);
   return hipGetLastError();
 }
 

@@ -253,6 +253,41 @@ def test_forward_is_deterministic():
     assert torch.equal(r1.src[:R], r2.src[:R])       # rows >= R are never written
 
 
+@pytest.mark.parametrize("name", ["toy_fp32", "batch32_bf16", "batch48_shared_bf16",
+                                  "batch24_cap_bf16", "decode_small_bf16", "switch_small_bf16",
+                                  "shared_fine_bf16", "capacity_top2_bf16", "reroute_top1_bf16"])
+def test_forward_matches_entry_point_chain(name):
+    """moe_forward against the chain of entry points on the same inputs (route,
+    permute with x_perm, up, down, shared, combine), bit for bit.  moe_forward
+    differs in how it schedules the same arithmetic: the first product reads x
+    through src, small layers take the dispatch layout from the router's aux
+    reduction, and the combine finishes the second product's split-k sums."""
+    spec, inp = inputs_for(name)
+    y1, a1, r1 = _forward_gpu(spec, inp)
+    desc, x, w, r2, a2, ws = _route_gpu(spec, inp)
+    Tk = spec.tokens * spec.top_k
+    x_perm = torch.empty(Tk, spec.d_model, dtype=x.dtype, device=G.DEV)
+    moe.moe_permute(desc, x, r2, x_perm, ws)
+    h = moe.alloc_h(desc, G.DEV)
+    o = torch.empty(Tk, spec.d_model, dtype=torch.float32, device=G.DEV)
+    moe.moe_ffn_up(desc, x_perm, r2.offsets, w, h, ws)
+    moe.moe_ffn_down(desc, h, r2.offsets, w, o, ws)
+    o_sh = None
+    if spec.d_ff_shared:
+        o_sh = torch.empty(spec.tokens, spec.d_model, dtype=torch.float32, device=G.DEV)
+        moe.moe_shared_ffn(desc, x, w, o_sh, ws)
+    y2 = torch.empty_like(y1)
+    moe.moe_combine(desc, o, r2.dest, r2.topk_w, y2, o_sh)
+    torch.cuda.synchronize()
+    R = int(r2.offsets[-1].item())
+    for f in ("topk_idx", "topk_w", "counts", "offsets", "dest", "top1_count", "prob_mean",
+              "z_loss", "reroute_rounds"):
+        assert torch.equal(getattr(r1, f), getattr(r2, f)), f
+    assert torch.equal(r1.src[:R], r2.src[:R])
+    assert torch.equal(a1, a2)
+    assert torch.equal(y1, y2)
+
+
 def test_module_style_forward():
     spec, inp = inputs_for("toy_fp32")
     y, aux = moe.forward(G.to_dev(inp["x"]), G.weights_for(inp), G.desc_for(spec))
