@@ -84,9 +84,16 @@ enum { MOE_FFN_AUTO = 0, MOE_FFN_TILED = 1, MOE_FFN_STREAM = 2 };
  *                runs one MFMA per term, so o carries ~16 bits of h.
  *   MOE_H_AUTO:  BF16 on the TILED path at >= 256 rows per expert (MFMA-bound),
  *                SPLIT below that and on the STREAM path, where the products
- *                are weight-bound and the second term costs little.
+ *                are weight-bound and the second term costs little, and SPLIT
+ *                for top-1 layers without renormalisation (below).
  * For an fp32 layer h is fp32 [T*k][F] and h_mode must be AUTO.  On the TILED
- * path SPLIT uses 128-row tiles. */
+ * path SPLIT uses 128-row tiles.
+ * MOE_H_BF16 on a top-1 layer without renormalisation returns
+ * MOE_ERR_UNSUPPORTED: there y_t = p_t * FFN(x_t) with the raw probability p_t,
+ * and capacity drops add zero rows, so max|y - y_exact| / RMS(y) is far larger
+ * than for averaged outputs; with bf16-rounded h it measured 0.025 (777
+ * tokens, 64 experts, capacity 16) and 0.041 (8192 tokens, 64 experts,
+ * capacity 160), past the 2e-2 bar, while two bf16 terms keep it near 1e-5. */
 enum { MOE_H_AUTO = 0, MOE_H_BF16 = 1, MOE_H_SPLIT = 2 };
 
 /* What happens to assignments past an expert's capacity (moe_desc.capacity_policy).
@@ -187,7 +194,12 @@ int moe_workspace_size(const moe_desc* desc, size_t* bytes);
 /* Resolve the descriptor's AUTO choices (host output). */
 int moe_query_plan(const moe_desc* desc, moe_plan* plan);
 
-/* Router: logits = x W_r^T (+ b_router), softmax, top-k by logit (+ b_select
+/* Router (web page "Mixture of Experts: Scaling Parameters Without Scaling
+ * Compute", section "The MoE layer", steps 1-2: logits, softmax, top-k, renormalised
+ * weights; section "The central problem: load balancing": the aux loss, the
+ * router z-loss and the selection-only bias; llmdaily day-59 page, section
+ * "Replace one MLP with many experts": the eight-expert routing example).
+ * Router: logits = x W_r^T (+ b_router), softmax, top-k by logit (+ b_select
  * when given), routing weights, the aux loss and the router z-loss; with
  * MOE_CAPACITY_REROUTE also the rerouting of the overflow (one extra
  * single-workgroup kernel).
@@ -198,7 +210,11 @@ int moe_query_plan(const moe_desc* desc, moe_plan* plan);
 int moe_route(const moe_desc* desc, const void* x, const moe_weights* w, moe_routing* out,
               float* aux, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Dispatch: per-expert histogram of the assignments, prefix scan, capacity
+/* Dispatch (web page "Mixture of Experts: Scaling Parameters Without Scaling
+ * Compute", section "The MoE layer": each expert processes the tokens routed to
+ * it; section "The central problem: load balancing": expert capacity, overflow
+ * dropped; llmdaily day-59 page, section "Experts also have capacity limits").
+ * Dispatch: per-expert histogram of the assignments, prefix scan, capacity
  * (MOE_CAPACITY_DROP), stable ranks in token order, and the gather of token
  * rows into expert-contiguous rows.
  *   Reads r->topk_idx; ids outside [0, E) are dropped assignments.  Writes r->counts, r->offsets, r->dest, r->src (all
@@ -207,7 +223,11 @@ int moe_route(const moe_desc* desc, const void* x, const moe_weights* w, moe_rou
 int moe_permute(const moe_desc* desc, const void* x, moe_routing* r, void* x_perm,
                 void* workspace, size_t workspace_bytes, void* stream);
 
-/* First expert product with GELU fused into its epilogue:
+/* First expert product (web page "Mixture of Experts: Scaling Parameters
+ * Without Scaling Compute", section "The MoE layer": each expert is
+ * Linear(d -> d_ff), GELU, Linear(d_ff -> d); this is the first linear map and
+ * the GELU, erf form).
+ * First expert product with GELU fused into its epilogue:
  *   h[r] = GELU_erf(x_perm[r] W1_e^T + b1_e) for every row r of expert e's segment
  *   [offsets[e], offsets[e+1]).  x_perm [T*k][d] dtype; h is stored as the
  *   resolved h_mode says (plan.h_bytes bytes).  offsets is the device array
@@ -216,18 +236,24 @@ int moe_ffn_up(const moe_desc* desc, const void* x_perm, const int32_t* offsets,
                const moe_weights* w, void* h, void* workspace, size_t workspace_bytes,
                void* stream);
 
-/* Second expert product: o[r] = h[r] W2_e^T + b2_e, h as moe_ffn_up wrote it,
+/* Second expert product (same page and section: the expert's second linear
+ * map, Linear(d_ff -> d) with its bias).
+ * Second expert product: o[r] = h[r] W2_e^T + b2_e, h as moe_ffn_up wrote it,
  * o [T*k][d] fp32. */
 int moe_ffn_down(const moe_desc* desc, const void* h, const int32_t* offsets,
                  const moe_weights* w, float* o, void* workspace, size_t workspace_bytes,
                  void* stream);
 
-/* The grouped expert FFN: moe_ffn_up then moe_ffn_down on the same stream. */
+/* The grouped expert FFN (same page and section: every chosen expert's
+ * Linear-GELU-Linear on its own rows): moe_ffn_up then moe_ffn_down on the same
+ * stream. */
 int moe_grouped_ffn(const moe_desc* desc, const void* x_perm, const int32_t* offsets,
                     const moe_weights* w, void* h, float* o, void* workspace,
                     size_t workspace_bytes, void* stream);
 
-/* The shared expert on every token (desc->d_ff_shared > 0):
+/* The shared expert (web page "Mixture of Experts: Scaling Parameters Without
+ * Scaling Compute", section "Design variations": shared experts are always
+ * active), on every token (desc->d_ff_shared > 0):
  *   o_shared[t] = W2s GELU(W1s x[t] + b1s) + b2s.  x [T][d] dtype, o_shared [T][d]
  *   fp32.  Its hidden activations live in the workspace. */
 int moe_shared_ffn(const moe_desc* desc, const void* x, const moe_weights* w, float* o_shared,
@@ -243,7 +269,11 @@ int moe_shared_ffn(const moe_desc* desc, const void* x, const moe_weights* w, fl
 int moe_combine(const moe_desc* desc, const float* o, const int32_t* dest, const float* topk_w,
                 const float* o_shared, float* y, void* stream);
 
-/* The whole layer: route, permute, grouped FFN, the shared expert (if any),
+/* The whole layer (web page "Mixture of Experts: Scaling Parameters Without
+ * Scaling Compute", section "The MoE layer": the module's forward maps x to the
+ * weighted sum of the chosen experts' outputs and returns the aux loss beside
+ * it; llmdaily day-59 page, section "Replace one MLP with many experts").
+ * The whole layer: route, permute, grouped FFN, the shared expert (if any),
  * combine.  The first expert product reads each dispatched row's token
  * straight from x (through src), so no x_perm is materialised.
  *   x [T][d] dtype -> y [T][d] fp32 and *aux (device fp32 scalar, optional).

@@ -177,6 +177,99 @@ def _ptr(t) -> Optional[int]:
     return t.data_ptr()
 
 
+def _expected(desc: "Desc") -> dict:
+    """(dtype, element count) of every array the C ABI sizes from the descriptor,
+    by argument name (the same shapes the library's alias and bounds logic uses)."""
+    T, d, F, E, k, Fs = (desc.tokens, desc.d_model, desc.d_ff, desc.n_experts, desc.top_k,
+                         desc.d_ff_shared)
+    dt, f32, i32 = desc.torch_dtype, torch.float32, torch.int32
+    return {"x": (dt, T * d), "w_router": (dt, E * d), "b_router": (f32, E), "b_select": (f32, E),
+            "w1": (dt, E * F * d), "b1": (dt, E * F), "w2": (dt, E * d * F), "b2": (dt, E * d),
+            "w1_shared": (dt, Fs * d), "b1_shared": (dt, Fs), "w2_shared": (dt, d * Fs),
+            "b2_shared": (dt, d),
+            "topk_idx": (i32, T * k), "topk_w": (f32, T * k), "counts": (i32, E),
+            "offsets": (i32, E + 1), "dest": (i32, T * k), "src": (i32, T * k),
+            "top1_count": (i32, E), "prob_mean": (f32, E), "z_loss": (f32, 1),
+            "reroute_rounds": (i32, 1),
+            "x_perm": (dt, T * k * d), "o": (f32, T * k * d), "y": (f32, T * d),
+            "o_shared": (f32, T * d), "aux": (f32, 1)}
+
+
+def check_tensor(t, name: str, dtype, numel: int, device) -> None:
+    """Refuse, before any call into the library, a tensor the library would read or
+    write out of bounds or misinterpret: not on `device` (a GPU), wrong dtype, fewer
+    than `numel` elements, or not contiguous.  Raw integer pointers are the
+    caller's responsibility and pass unchecked."""
+    if t is None or isinstance(t, int):
+        return
+    if not isinstance(t, torch.Tensor):
+        raise MoeError(MOE_ERR_INVALID, f"{name} must be a torch tensor, an int pointer or None")
+    if (t.device != device) if device is not None else (t.device.type != "cuda"):
+        raise MoeError(MOE_ERR_INVALID, f"{name} is on {t.device}, expected {device or 'a GPU'}")
+    if dtype is not None and t.dtype != dtype:
+        raise MoeError(MOE_ERR_INVALID, f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.numel() < numel:
+        raise MoeError(MOE_ERR_INVALID, f"{name} has {t.numel()} elements, needs {numel}")
+    if not t.is_contiguous():
+        raise MoeError(MOE_ERR_INVALID, f"{name} must be contiguous")
+
+
+def _device_of(*ts):
+    for t in ts:
+        if isinstance(t, torch.Tensor):
+            return t.device
+    return None
+
+
+class _Args:
+    """Checks the tensors of one call against the descriptor (see check_tensor)."""
+
+    def __init__(self, desc: "Desc", *anchor):
+        self.desc = desc
+        self.want = _expected(desc)
+        self.device = _device_of(*anchor)
+        if self.device is not None and self.device.type != "cuda":
+            raise MoeError(MOE_ERR_INVALID, f"tensors are on {self.device}, expected a GPU")
+
+    def t(self, t, name, key=None):
+        dtype, n = self.want[key or name]
+        check_tensor(t, name, dtype, n, self.device)
+        return _ptr(t)
+
+    def weights(self, w: "Weights", router: bool, experts: bool):
+        names = (("w_router", "b_router", "b_select") if router else ()) + \
+                (("w1", "b1", "w2", "b2", "w1_shared", "b1_shared", "w2_shared", "b2_shared")
+                 if experts else ())
+        for n in names:
+            self.t(getattr(w, n), "weights." + n, n)
+        return ctypes.byref(w.to_c())
+
+    def routing(self, r: "Routing"):
+        for f in dataclasses.fields(r):
+            self.t(getattr(r, f.name), "routing." + f.name, f.name)
+        return ctypes.byref(r.to_c())
+
+    def h(self, t):
+        if t is None or isinstance(t, int):
+            return _ptr(t)
+        plan = moe_query_plan(self.desc)
+        check_tensor(t, "h", self.desc.torch_dtype, 0, self.device)
+        if t.numel() * t.element_size() < plan["h_bytes"]:
+            raise MoeError(MOE_ERR_INVALID, f"h has {t.numel() * t.element_size()} bytes, "
+                                            f"needs {plan['h_bytes']}")
+        return _ptr(t)
+
+    def ws(self, t):
+        """(pointer, bytes) of the workspace; None allocates one of the right size."""
+        if t is None:
+            t = alloc_workspace(self.desc, self.device)
+        if isinstance(t, int):
+            raise MoeError(MOE_ERR_INVALID, "pass the workspace as a tensor (its size is needed)")
+        check_tensor(t, "workspace", None, 0, self.device)
+        self._ws_keep = t
+        return _ptr(t), t.numel() * t.element_size()
+
+
 def _stream(stream) -> Optional[int]:
     if stream is None:
         return torch.cuda.current_stream().cuda_stream
@@ -219,55 +312,65 @@ def alloc_workspace(desc: Desc, device) -> torch.Tensor:
 
 
 def moe_route(desc, x, weights, routing, aux=None, workspace=None, stream=None):
-    ws = workspace if workspace is not None else alloc_workspace(desc, x.device)
-    _check(load_library().moe_route(ctypes.byref(desc.to_c()), _ptr(x), ctypes.byref(weights.to_c()),
-                                    ctypes.byref(routing.to_c()), _ptr(aux), _ptr(ws), ws.numel(),
-                                    _stream(stream)))
+    a = _Args(desc, x)
+    ws, nb = a.ws(workspace)
+    _check(load_library().moe_route(ctypes.byref(desc.to_c()), a.t(x, "x"), a.weights(weights, True, False),
+                                    a.routing(routing), a.t(aux, "aux"), ws, nb, _stream(stream)))
 
 
 def moe_permute(desc, x, routing, x_perm, workspace=None, stream=None):
-    ws = workspace if workspace is not None else alloc_workspace(desc, x.device)
-    _check(load_library().moe_permute(ctypes.byref(desc.to_c()), _ptr(x), ctypes.byref(routing.to_c()),
-                                      _ptr(x_perm), _ptr(ws), ws.numel(), _stream(stream)))
+    a = _Args(desc, x)
+    ws, nb = a.ws(workspace)
+    _check(load_library().moe_permute(ctypes.byref(desc.to_c()), a.t(x, "x"), a.routing(routing),
+                                      a.t(x_perm, "x_perm"), ws, nb, _stream(stream)))
 
 
 def moe_ffn_up(desc, x_perm, offsets, weights, h, workspace=None, stream=None):
-    ws = workspace if workspace is not None else alloc_workspace(desc, x_perm.device)
-    _check(load_library().moe_ffn_up(ctypes.byref(desc.to_c()), _ptr(x_perm), _ptr(offsets),
-                                     ctypes.byref(weights.to_c()), _ptr(h), _ptr(ws), ws.numel(),
-                                     _stream(stream)))
+    a = _Args(desc, x_perm)
+    ws, nb = a.ws(workspace)
+    _check(load_library().moe_ffn_up(ctypes.byref(desc.to_c()), a.t(x_perm, "x_perm"),
+                                     a.t(offsets, "offsets"), a.weights(weights, False, True), a.h(h),
+                                     ws, nb, _stream(stream)))
 
 
 def moe_ffn_down(desc, h, offsets, weights, o, workspace=None, stream=None):
-    ws = workspace if workspace is not None else alloc_workspace(desc, h.device)
-    _check(load_library().moe_ffn_down(ctypes.byref(desc.to_c()), _ptr(h), _ptr(offsets),
-                                       ctypes.byref(weights.to_c()), _ptr(o), _ptr(ws), ws.numel(),
+    a = _Args(desc, h)
+    ws, nb = a.ws(workspace)
+    _check(load_library().moe_ffn_down(ctypes.byref(desc.to_c()), a.h(h), a.t(offsets, "offsets"),
+                                       a.weights(weights, False, True), a.t(o, "o"), ws, nb,
                                        _stream(stream)))
 
 
 def moe_grouped_ffn(desc, x_perm, offsets, weights, h, o, workspace=None, stream=None):
-    ws = workspace if workspace is not None else alloc_workspace(desc, x_perm.device)
-    _check(load_library().moe_grouped_ffn(ctypes.byref(desc.to_c()), _ptr(x_perm), _ptr(offsets),
-                                          ctypes.byref(weights.to_c()), _ptr(h), _ptr(o), _ptr(ws),
-                                          ws.numel(), _stream(stream)))
+    a = _Args(desc, x_perm)
+    ws, nb = a.ws(workspace)
+    _check(load_library().moe_grouped_ffn(ctypes.byref(desc.to_c()), a.t(x_perm, "x_perm"),
+                                          a.t(offsets, "offsets"), a.weights(weights, False, True),
+                                          a.h(h), a.t(o, "o"), ws, nb, _stream(stream)))
 
 
 def moe_shared_ffn(desc, x, weights, o_shared, workspace=None, stream=None):
-    ws = workspace if workspace is not None else alloc_workspace(desc, x.device)
-    _check(load_library().moe_shared_ffn(ctypes.byref(desc.to_c()), _ptr(x), ctypes.byref(weights.to_c()),
-                                         _ptr(o_shared), _ptr(ws), ws.numel(), _stream(stream)))
+    a = _Args(desc, x)
+    ws, nb = a.ws(workspace)
+    _check(load_library().moe_shared_ffn(ctypes.byref(desc.to_c()), a.t(x, "x"),
+                                         a.weights(weights, False, True),
+                                         a.t(o_shared, "o_shared"), ws, nb, _stream(stream)))
 
 
 def moe_combine(desc, o, dest, topk_w, y, o_shared=None, stream=None):
-    _check(load_library().moe_combine(ctypes.byref(desc.to_c()), _ptr(o), _ptr(dest), _ptr(topk_w),
-                                      _ptr(o_shared), _ptr(y), _stream(stream)))
+    a = _Args(desc, o)
+    _check(load_library().moe_combine(ctypes.byref(desc.to_c()), a.t(o, "o"), a.t(dest, "dest"),
+                                      a.t(topk_w, "topk_w"), a.t(o_shared, "o_shared"), a.t(y, "y"),
+                                      _stream(stream)))
 
 
 def moe_forward(desc, x, weights, y, aux=None, routing=None, workspace=None, stream=None):
-    ws = workspace if workspace is not None else alloc_workspace(desc, x.device)
-    r = ctypes.byref(routing.to_c()) if routing is not None else None
-    _check(load_library().moe_forward(ctypes.byref(desc.to_c()), _ptr(x), ctypes.byref(weights.to_c()),
-                                      _ptr(y), _ptr(aux), r, _ptr(ws), ws.numel(), _stream(stream)))
+    a = _Args(desc, x)
+    ws, nb = a.ws(workspace)
+    r = a.routing(routing) if routing is not None else None
+    _check(load_library().moe_forward(ctypes.byref(desc.to_c()), a.t(x, "x"),
+                                      a.weights(weights, True, True), a.t(y, "y"), a.t(aux, "aux"), r,
+                                      ws, nb, _stream(stream)))
 
 
 def forward(x: torch.Tensor, weights: Weights, desc: Desc, workspace=None, stream=None):

@@ -157,6 +157,25 @@ def test_plan_resolution_of_the_named_workloads():
         assert p["workspace_bytes"] == moe.moe_workspace_size(d)
 
 
+def test_bf16_h_is_refused_for_top1_without_renorm():
+    """A top-1 layer without renormalisation cannot meet the 2e-2 bar on y with
+    bf16-rounded h: an explicit MOE_H_BF16 is refused, AUTO keeps two bf16 terms
+    even at prefill sizes, and the same layer with renormalisation or top-2 keeps
+    bf16 h."""
+    lib = moe.load_library()
+    n = ctypes.c_size_t(0)
+    for kw in (dict(capacity=160), dict(capacity=0)):
+        d = moe.Desc(8192, 2048, 8192, 64, 1, False, dtype="bf16", h_mode=B.MOE_H_BF16, **kw)
+        st = lib.moe_workspace_size(ctypes.byref(d.to_c()), ctypes.byref(n))
+        assert st == B.MOE_ERR_UNSUPPORTED and "MOE_H_BF16" in lib.moe_last_error().decode()
+    big = moe.Desc(65536, 2048, 8192, 8, 1, False)          # 8192 rows per expert, top-1
+    assert moe.moe_query_plan(big)["h_mode"] == B.MOE_H_SPLIT
+    for d in (moe.Desc(65536, 2048, 8192, 8, 1, True), moe.Desc(32768, 2048, 8192, 8, 2, False)):
+        assert moe.moe_query_plan(d)["h_mode"] == B.MOE_H_BF16
+        d.h_mode = B.MOE_H_BF16
+        assert moe.moe_workspace_size(d) > 0
+
+
 def test_shared_expert_flag_must_match_pointers():
     lib = moe.load_library()
     d = moe.Desc(64, 256, 512, 8, 2, has_expert_bias=False)
@@ -249,3 +268,41 @@ def test_disjoint_buffers_pass_the_alias_check():
     st = lib.moe_combine(ctypes.byref(_D.to_c()), 0x100000, 0x100000 + o_bytes,
                          0x100000 + o_bytes + 1024, None, 0x100000 + o_bytes + 2048, None)
     assert "overlaps" not in lib.moe_last_error().decode()
+
+
+# ---- the binding refuses tensors the library would misread, before any call ----
+
+def test_binding_refuses_host_tensors():
+    import torch
+    d = moe.Desc(4, 128, 128, 2, 1, dtype="f32")
+    o = torch.zeros(4, 128)
+    with pytest.raises(moe.MoeError, match="expected a GPU"):
+        moe.moe_combine(d, o, torch.zeros(4, 1, dtype=torch.int32), torch.zeros(4, 1), torch.zeros(4, 128))
+
+
+def test_binding_checks_dtype_size_and_device():
+    import torch
+    cpu = torch.device("cpu")
+    B.check_tensor(torch.zeros(8, dtype=torch.int32), "dest", torch.int32, 8, cpu)
+    with pytest.raises(moe.MoeError, match="dtype"):
+        B.check_tensor(torch.zeros(8, dtype=torch.float32), "x", torch.bfloat16, 8, cpu)
+    with pytest.raises(moe.MoeError, match="needs 9"):
+        B.check_tensor(torch.zeros(8, dtype=torch.int32), "offsets", torch.int32, 9, cpu)
+    with pytest.raises(moe.MoeError, match="expected"):
+        B.check_tensor(torch.zeros(8), "y", torch.float32, 8, torch.device("meta"))
+    with pytest.raises(moe.MoeError, match="contiguous"):
+        B.check_tensor(torch.zeros(4, 4).t(), "o", torch.float32, 16, cpu)
+    B.check_tensor(0x1000, "raw", torch.float32, 1 << 30, cpu)     # raw pointers pass unchecked
+
+
+def test_binding_sizes_follow_the_descriptor():
+    """The element counts the binding checks are the ones the C library sizes its
+    accesses from (bf16 layer with a shared expert)."""
+    import torch
+    d = moe.Desc(10, 256, 512, 4, 2, d_ff_shared=384)
+    e = B._expected(d)
+    assert e["x"] == (torch.bfloat16, 10 * 256)
+    assert e["w1"] == (torch.bfloat16, 4 * 512 * 256) and e["w2"] == (torch.bfloat16, 4 * 256 * 512)
+    assert e["o"] == (torch.float32, 20 * 256) and e["y"] == (torch.float32, 10 * 256)
+    assert e["offsets"] == (torch.int32, 5) and e["src"] == (torch.int32, 20)
+    assert e["w1_shared"] == (torch.bfloat16, 384 * 256) and e["b2_shared"] == (torch.bfloat16, 256)

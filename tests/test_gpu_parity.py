@@ -21,6 +21,9 @@ pytestmark = pytest.mark.gpu
 
 SMALL_NAMES = ["toy_fp32"] + list(SMALL)
 BF16_SMALL = [n for n in SMALL if SMALL[n].dtype == "bf16"]
+# bf16-rounded h is refused for top-1 layers without renormalisation (the ABI returns
+# MOE_ERR_UNSUPPORTED: y would miss the 2e-2 bar there); those shapes run split h only.
+BF16_H_OK = [n for n in BF16_SMALL if SMALL[n].top_k > 1 or SMALL[n].renormalize]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -122,9 +125,9 @@ def _ffn_inputs(spec, inp, ref):
 
 
 FFN_CASES = ([(n, moe.MOE_FFN_AUTO, moe.MOE_H_AUTO) for n in SMALL_NAMES] +
-             [(n, moe.MOE_FFN_TILED, moe.MOE_H_BF16) for n in BF16_SMALL] +
+             [(n, moe.MOE_FFN_TILED, moe.MOE_H_BF16) for n in BF16_H_OK] +
              [(n, moe.MOE_FFN_TILED, moe.MOE_H_SPLIT) for n in BF16_SMALL] +
-             [(n, moe.MOE_FFN_STREAM, moe.MOE_H_BF16) for n in BF16_SMALL] +
+             [(n, moe.MOE_FFN_STREAM, moe.MOE_H_BF16) for n in BF16_H_OK] +
              [(n, moe.MOE_FFN_STREAM, moe.MOE_H_SPLIT) for n in BF16_SMALL])
 
 
@@ -232,11 +235,9 @@ def test_forward_small(name):
     _check_forward(spec, inp, y, aux, r)
 
 
-@pytest.mark.parametrize("name", [n for n in BF16_SMALL if n != "switch_small_bf16"])
+@pytest.mark.parametrize("name", BF16_H_OK)
 def test_forward_small_bf16_h(name):
-    """bf16-rounded h on both kernels.  (The switch-style small shape is left out:
-    bf16 h alone puts its y at ~0.025 of RMS, reproduced by an fp64 emulation of
-    bf16 rounding; SPLIT h is what the library picks for it.)"""
+    """bf16-rounded h on both kernels, on every shape where the ABI accepts it."""
     spec, inp = inputs_for(name)
     for path in (moe.MOE_FFN_TILED, moe.MOE_FFN_STREAM):
         y, aux, r = _forward_gpu(spec, inp, path, moe.MOE_H_BF16)
