@@ -93,19 +93,48 @@ def _time_events(fn, reps, warmup=2):
 
 
 def cpu_baseline(spec, inp, sample_tokens):
-    """The fp64 oracle as it stands, on a bounded token sample of the same workload."""
+    """The fp64 oracle as it stands, on a bounded token sample of the same workload.
+    Returns the baseline record and the oracle's result on that sample."""
     from threadpoolctl import threadpool_info
     from oracle import moe_oracle as O
     rng = np.random.default_rng(0)
     toks = np.sort(rng.choice(spec.tokens, size=min(sample_tokens, spec.tokens), replace=False))
     t0 = time.perf_counter()
-    O.forward(inp, O.desc_of(spec), tokens=toks)
+    ref = O.forward(inp, O.desc_of(spec), tokens=toks)
     dt = time.perf_counter() - t0
     threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     return {"value": round(len(toks) / dt, 3), "unit": "tokens/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"{len(toks)} of {spec.tokens} tokens (routing of all tokens, expert FFNs of "
-                      f"the sampled tokens), fp64 NumPy/BLAS, {dt:.1f} s"}
+                      f"the sampled tokens), fp64 NumPy/BLAS, {dt:.1f} s"}, ref
+
+
+def parity_of(spec, ref, y, aux, routing):
+    """The timed run's outputs against the oracle's on the CPU-baseline sample: y's
+    max|err|/RMS over the sampled tokens, aux's relative error, routing exactness."""
+    toks = ref["tokens"]
+    yg = y.cpu().numpy().astype(np.float64)[toks]
+    yr = ref["y"]
+    rms = float(np.sqrt(np.mean(yr ** 2)))
+    idx = routing.topk_idx.cpu().numpy()
+    want = ref["topk_idx"] if spec.capacity_policy != "reroute" else np.where(ref["keep"], ref["topk_idx"], -1)
+    return {"tokens_compared": int(toks.size),
+            "y_max_err_over_rms": float(np.max(np.abs(yg - yr)) / rms),
+            "y_tol": 2e-2 if spec.dtype == "bf16" else 1e-4,
+            "aux_rel_err": abs(float(aux.item()) - ref["aux"]) / abs(ref["aux"]),
+            "routing_exact": bool(np.array_equal(idx, want)
+                                  and np.array_equal(routing.counts.cpu().numpy(), ref["counts"])
+                                  and np.array_equal(routing.dest.cpu().numpy(), ref["dest"]))}
+
+
+def stream_read_gbs(dev, mib=4096, reps=10):
+    """A plain streaming read of `mib` MiB (torch's sum over an fp32 buffer) on the
+    same GPU: the practical HBM read ceiling next to the 8 TB/s grade."""
+    import torch
+    buf = torch.ones(mib * (1 << 20) // 4, dtype=torch.float32, device=dev)
+    ms = _time_events(lambda: buf.sum(), reps)
+    del buf
+    return round(mib * (1 << 20) / (ms * 1e-3) / 1e9, 1)
 
 
 def kernel_bytes(spec, R, active, h_elem):
@@ -120,13 +149,15 @@ def kernel_bytes(spec, R, active, h_elem):
     return up, down
 
 
-def run(args):
+def measure(spec, args, dev, steps, with_cpu):
+    """One workload: moe_forward timed over `steps` steps, its expert products timed
+    alone in the launch configuration moe_forward uses, the roofline of the dominant
+    one, the routing's loads and drops, and (with_cpu) the oracle on a bounded sample
+    with the timed run's parity against it."""
     import torch
     import sparse_mixture_experts_49_amd as moe
     import synth
 
-    spec = synth.WORKLOADS[args.workload]
-    dev = "cuda:0"
     inp = synth.make_inputs(spec)
     desc = moe.Desc(spec.tokens, spec.d_model, spec.d_ff, spec.n_experts, spec.top_k,
                     spec.renormalize, spec.capacity, spec.dtype, spec.expert_bias,
@@ -148,39 +179,31 @@ def run(args):
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
-    for _ in range(args.steps):
+    for _ in range(steps):
         step()
     end.record()
     torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
+    ms = start.elapsed_time(end) / steps
+    y_out = y.clone()
+    aux_out = aux.clone()
 
-    # The expert kernels alone, same launch configuration as inside moe_forward.
+    # The expert products alone, as moe_forward launches them: the first reads each
+    # dispatched row's token from x through src, the second reads h.
     Tk = spec.tokens * spec.top_k
-    el = torch.bfloat16 if spec.dtype == "bf16" else torch.float32
-    x_perm = torch.empty(Tk, spec.d_model, dtype=el, device=dev)
     h = moe.alloc_h(desc, dev)
     o = torch.empty(Tk, spec.d_model, dtype=torch.float32, device=dev)
-    moe.moe_route(desc, x, w, routing, aux, ws)
-    moe.moe_permute(desc, x, routing, x_perm, ws)
-    torch.cuda.synchronize()
     R = int(routing.offsets[-1].item())
-    active = int((routing.counts > 0).sum().item())
-    up_ms = _time_events(lambda: moe.moe_ffn_up(desc, x_perm, routing.offsets, w, h, ws), args.kernel_reps)
+    counts = routing.counts.cpu().numpy()
+    active = int((counts > 0).sum())
+    up_ms = _time_events(lambda: moe.moe_ffn_up_gather(desc, x, routing.src, routing.offsets, w, h, ws),
+                         args.kernel_reps)
     down_ms = _time_events(lambda: moe.moe_ffn_down(desc, h, routing.offsets, w, o, ws), args.kernel_reps)
-    route_ms = _time_events(lambda: moe.moe_route(desc, x, w, routing, aux, ws), args.kernel_reps)
+    r2 = moe.Routing.allocate(desc, dev)
+    route_ms = _time_events(lambda: moe.moe_route(desc, x, w, r2, None, ws), args.kernel_reps)
     shared_ms = None
     if spec.d_ff_shared:
         o_sh = torch.empty(spec.tokens, spec.d_model, dtype=torch.float32, device=dev)
         shared_ms = _time_events(lambda: moe.moe_shared_ffn(desc, x, w, o_sh, ws), args.kernel_reps)
-
-    if args.copy_probe_mib:
-        # One plain copy of known size for scaling the HBM byte counters (see the module doc).
-        n = args.copy_probe_mib * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        torch.neg(src, out=dst)
-        torch.cuda.synchronize()
-        del src, dst
 
     plan = moe.moe_query_plan(desc)
     h_elem = h.element_size() * (2 if h.dim() == 3 else 1)
@@ -203,20 +226,15 @@ def run(args):
                 "frac": round(achieved / PEAK_HBM_GBS, 4)}
     roof.update({"traffic": traffic, "kernel": dom, "kernel_ms": round(dom_ms, 4),
                  "algorithmic_bytes": dom_bytes, "algorithmic_flops": flops_one})
-
+    # Every byte one step must move at least once: x, the router and the touched
+    # experts' weights and biases, y (fp32).
+    s_el = 2 if bf16 else 4
+    step_bytes = (spec.tokens * spec.d_model * s_el + spec.n_experts * spec.d_model * s_el
+                  + active * (2 * spec.d_ff * spec.d_model + (spec.d_ff + spec.d_model) * spec.expert_bias) * s_el
+                  + spec.tokens * spec.d_model * 4)
     out = {
-        "metric": METRIC,
-        "value": round(spec.tokens / (ms * 1e-3), 1),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": spec.dtype,
-        "data": "synthetic",
+        "tokens_per_s": round(spec.tokens / (ms * 1e-3), 1),
         "config": {"workload": spec.name, "tokens": spec.tokens, "d_model": spec.d_model,
                    "d_ff": spec.d_ff, "n_experts": spec.n_experts, "top_k": spec.top_k,
                    "capacity": spec.capacity, "capacity_policy": spec.capacity_policy,
@@ -229,15 +247,68 @@ def run(args):
                   "ffn_tflops": round(2 * flops_one / ((up_ms + down_ms) * 1e-3) / 1e12, 1),
                   "ffn_frac_peak": round(2 * flops_one / ((up_ms + down_ms) * 1e-3) / 1e12 / peak_flops, 4),
                   "ffn_gbs": round((up_bytes + down_bytes) / ((up_ms + down_ms) * 1e-3) / 1e9, 1),
-                  "step_gbs_weights_and_io": round(
-                      (up_bytes + down_bytes) / (ms * 1e-3) / 1e9, 1)},
+                  "step_min_bytes": int(step_bytes),
+                  "step_gbs": round(step_bytes / (ms * 1e-3) / 1e9, 1),
+                  "step_frac_hbm": round(step_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+        "loads": {"kept_per_expert": counts.tolist(), "dropped": int(Tk - R)},
     }
     if shared_ms is not None:
         sh_flops = 4.0 * spec.tokens * spec.d_model * spec.d_ff_shared
         out["layer"].update({"shared_ffn_ms": round(shared_ms, 4),
                              "shared_ffn_tflops": round(sh_flops / (shared_ms * 1e-3) / 1e12, 1)})
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(spec, inp, args.cpu_sample)
+    if with_cpu:
+        base, ref = cpu_baseline(spec, inp, args.cpu_sample)
+        out["cpu_baseline"] = base
+        out["parity"] = parity_of(spec, ref, y_out, aux_out, routing)
+    del x, w, ws, h, o
+    torch.cuda.empty_cache()
+    return out
+
+
+def run(args):
+    import synth
+
+    dev = "cuda:0"
+    if args.copy_probe_mib:
+        # One plain copy of known size for scaling the HBM byte counters (see the module doc).
+        import torch
+        n = args.copy_probe_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+    main = measure(synth.WORKLOADS[args.workload], args, dev, args.steps, not args.no_cpu_baseline)
+    out = {
+        "metric": METRIC,
+        "value": main["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": synth.WORKLOADS[args.workload].dtype,
+        "data": "synthetic",
+        "config": main["config"],
+        "roofline": main["roofline"],
+        "layer": main["layer"],
+        "loads": main["loads"],
+    }
+    for key in ("parity", "cpu_baseline"):
+        if key in main:
+            out[key] = main[key]
+    if args.decode_workload and args.decode_workload != args.workload:
+        # The decode half of the metric: the small-batch layer, HBM-bound, timed in the
+        # same run (more steps: one step is a few hundred microseconds).
+        dec = measure(synth.WORKLOADS[args.decode_workload], args, dev, args.decode_steps,
+                      not args.no_cpu_baseline)
+        out["decode"] = {k: dec[k] for k in ("ms_per_step", "tokens_per_s", "config", "roofline",
+                                            "layer", "loads", "parity", "cpu_baseline") if k in dec}
+        out["decode"]["steps"] = args.decode_steps
+    out["stream_read_gbs"] = stream_read_gbs(dev)
     print(json.dumps(out), flush=True)
 
 
@@ -339,6 +410,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="mixtral_prefill_bf16")
+    ap.add_argument("--decode-workload", default="decode_bf16",
+                    help="measured after the main workload, reported under 'decode' ('' to skip)")
+    ap.add_argument("--decode-steps", type=int, default=200)
     ap.add_argument("--kernel-reps", type=int, default=20)
     ap.add_argument("--cpu-sample", type=int, default=16384)
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -46,8 +46,9 @@
  * same inputs give bitwise-identical results.
  * Limits.  1 <= tokens; 1 <= n_experts <= 64; 1 <= top_k <= min(8, n_experts);
  * d_model, d_ff and d_ff_shared are multiples of 128; tokens * top_k *
- * max(d_model, d_ff) and tokens * d_ff_shared must fit in int32 (else
- * MOE_ERR_UNSUPPORTED).
+ * max(d_model, d_ff) and tokens * d_ff_shared must fit in int32, and one
+ * expert's weight matrix (d_model x max(d_ff, d_ff_shared) elements) must be
+ * under 4 GiB (else MOE_ERR_UNSUPPORTED).
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
@@ -235,6 +236,15 @@ int moe_permute(const moe_desc* desc, const void* x, moe_routing* r, void* x_per
 int moe_ffn_up(const moe_desc* desc, const void* x_perm, const int32_t* offsets,
                const moe_weights* w, void* h, void* workspace, size_t workspace_bytes,
                void* stream);
+
+/* The first expert product as moe_forward runs it (same page and section as
+ * moe_ffn_up): no x_perm is materialised; dispatched row r reads token
+ * src[r] / top_k of x straight from x [T][d] dtype.  src [T*k] and offsets
+ * [E+1] are moe_permute's outputs; h as moe_ffn_up writes it, bitwise equal to
+ * moe_ffn_up on the gathered rows. */
+int moe_ffn_up_gather(const moe_desc* desc, const void* x, const int32_t* src,
+                      const int32_t* offsets, const moe_weights* w, void* h, void* workspace,
+                      size_t workspace_bytes, void* stream);
 
 /* Second expert product (same page and section: the expert's second linear
  * map, Linear(d_ff -> d) with its bias).

@@ -22,7 +22,7 @@ MOE_CAPACITY_DROP, MOE_CAPACITY_REROUTE = 0, 1
 _POLICIES = {"drop": MOE_CAPACITY_DROP, "reroute": MOE_CAPACITY_REROUTE}
 
 ENTRY_POINTS = ("moe_status_string", "moe_last_error", "moe_workspace_size", "moe_query_plan",
-                "moe_route", "moe_permute", "moe_ffn_up", "moe_ffn_down", "moe_grouped_ffn",
+                "moe_route", "moe_permute", "moe_ffn_up", "moe_ffn_up_gather", "moe_ffn_down", "moe_grouped_ffn",
                 "moe_shared_ffn", "moe_combine", "moe_forward")
 
 
@@ -78,6 +78,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "moe_route": (I, [pd, P, pw, pr, P, P, S, P]),
         "moe_permute": (I, [pd, P, pr, P, P, S, P]),
         "moe_ffn_up": (I, [pd, P, P, pw, P, P, S, P]),
+        "moe_ffn_up_gather": (I, [pd, P, P, P, pw, P, P, S, P]),
         "moe_ffn_down": (I, [pd, P, P, pw, P, P, S, P]),
         "moe_grouped_ffn": (I, [pd, P, P, pw, P, P, P, S, P]),
         "moe_shared_ffn": (I, [pd, P, pw, P, P, S, P]),
@@ -331,6 +332,14 @@ def moe_ffn_up(desc, x_perm, offsets, weights, h, workspace=None, stream=None):
     _check(load_library().moe_ffn_up(ctypes.byref(desc.to_c()), a.t(x_perm, "x_perm"),
                                      a.t(offsets, "offsets"), a.weights(weights, False, True), a.h(h),
                                      ws, nb, _stream(stream)))
+
+
+def moe_ffn_up_gather(desc, x, src, offsets, weights, h, workspace=None, stream=None):
+    a = _Args(desc, x)
+    ws, nb = a.ws(workspace)
+    _check(load_library().moe_ffn_up_gather(ctypes.byref(desc.to_c()), a.t(x, "x"), a.t(src, "src"),
+                                            a.t(offsets, "offsets"), a.weights(weights, False, True),
+                                            a.h(h), ws, nb, _stream(stream)))
 
 
 def moe_ffn_down(desc, h, offsets, weights, o, workspace=None, stream=None):

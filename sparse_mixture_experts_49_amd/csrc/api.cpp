@@ -90,6 +90,11 @@ int validate_desc(const moe_desc* d) {
   const long long widest = d->d_model > d->d_ff ? d->d_model : d->d_ff;
   if (rows * widest > std::numeric_limits<int32_t>::max())
     return fail(MOE_ERR_UNSUPPORTED, "tokens * top_k * max(d_model, d_ff) exceeds int32");
+  // The tiled kernel addresses one expert's weight matrix with 32-bit byte offsets.
+  const long long wbytes = (long long)d->d_model * (d->d_ff > d->d_ff_shared ? d->d_ff : d->d_ff_shared) *
+                           (d->dtype == MOE_DTYPE_BF16 ? 2 : 4);
+  if (wbytes >= (1LL << 32))
+    return fail(MOE_ERR_UNSUPPORTED, "one expert's d_model x d_ff weight matrix must be under 4 GiB");
   if (d->d_ff_shared < 0) return fail(MOE_ERR_INVALID, "d_ff_shared must be >= 0");
   if (d->d_ff_shared % 128)
     return fail(MOE_ERR_UNSUPPORTED, "d_ff_shared (%d) must be a multiple of 128", d->d_ff_shared);
@@ -691,6 +696,32 @@ int moe_ffn_up(const moe_desc* desc, const void* x_perm, const int32_t* offsets,
     if (int st = check_alias(o, in)) return st;
   }
   return launch_one_ffn(desc, true, x_perm, offsets, w, h, ws, L, static_cast<hipStream_t>(stream));
+}
+
+int moe_ffn_up_gather(const moe_desc* desc, const void* x, const int32_t* src,
+                      const int32_t* offsets, const moe_weights* w, void* h, void* ws,
+                      size_t ws_bytes, void* stream) {
+  if (int st = validate_desc(desc)) return st;
+  MOE_REQUIRE_PTR(x, "x");
+  MOE_REQUIRE_PTR(src, "src");
+  MOE_REQUIRE_PTR(offsets, "offsets");
+  MOE_REQUIRE_PTR(h, "h");
+  if (int st = validate_weights(desc, w, false, true)) return st;
+  Layout L;
+  if (int st = check_ws(desc, ws, ws_bytes, L)) return st;
+  {
+    const Bytes b = bytes_of(desc);
+    Spans o, in;
+    o.add(h, b.h, "h");
+    o.add(ws, ws_bytes, "workspace");
+    in.add(x, b.x, "x");
+    in.add(src, b.tk, "src");
+    in.add(offsets, b.e1, "offsets");
+    add_weights(in, desc, w, false, true);
+    if (int st = check_alias(o, in)) return st;
+  }
+  return launch_one_ffn(desc, true, x, offsets, w, h, ws, L, static_cast<hipStream_t>(stream),
+                        src);
 }
 
 int moe_ffn_down(const moe_desc* desc, const void* h, const int32_t* offsets,

@@ -137,6 +137,13 @@ __device__ __forceinline__ void load_lds16_raw(const void* g, uint32_t lds_addr)
 }
 
 // s_waitcnt immediate (gfx9 encoding) waiting for vmcnt <= vm, other counters untouched.
+// The same load with a uniform 64-bit base in SGPRs and a 32-bit per-lane byte
+// offset in a VGPR (global "saddr" form): no per-lane 64-bit address arithmetic.
+__device__ __forceinline__ void load_lds16_sv(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(sbase), "s"(lds_addr) : "memory", "m0");
+}
+
 constexpr int waitcnt_vm(int vm) { return (vm & 0xF) | ((vm >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 constexpr int kWaitLgkm0 = 0xC07F;   // lgkmcnt(0), others untouched
 // vmcnt <= vm and lgkmcnt(0).
@@ -282,29 +289,32 @@ __global__ __launch_bounds__(256, OCC) void ffn_tiled_kernel(
   // the stage (A: plane p's row r is LDS row p*BM + r), physical chunk lane%8,
   // i.e. logical chunk (lane%8) ^ ((row >> 1) & 7).  BM is a multiple of 16,
   // so a plane-1 row has the swizzle of its row within the plane.
-  const uint16_t* a_src[kAInst];
-  const uint16_t* b_src[kBInst];
+  // Per-lane byte offsets (32 bits: the descriptor limits keep every operand
+  // under 4 GiB) from uniform bases that advance by k.  A plane-1 row
+  // (instruction i >= BM / 32 of a split A) reads from A_lo.
+  uint32_t a_off[kAInst];
+  uint32_t b_off[kBInst];
   const uint16_t* Wexp = W + (size_t)e * N * K;
 #pragma unroll
   for (int i = 0; i < kAInst; ++i) {
     const int lrow = (i * NW + wave) * 8 + (lane >> 3);
-    const int plane = lrow / BM, row = lrow % BM;
+    const int row = lrow % BM;
     const int c = (lane & 7) ^ ((lrow >> 1) & 7);
-    a_src[i] = (plane ? A_lo : A) + (size_t)a_row(gather, gather_k, min(r0 + row, r1 - 1)) * K + c * 8;
+    a_off[i] = (uint32_t)(((size_t)a_row(gather, gather_k, min(r0 + row, r1 - 1)) * K + c * 8) * 2);
   }
 #pragma unroll
   for (int i = 0; i < kBInst; ++i) {
     const int row = (i * NW + wave) * 8 + (lane >> 3);
     const int c = (lane & 7) ^ ((row >> 1) & 7);
-    b_src[i] = Wexp + (size_t)min(n0 + row, N - 1) * K + c * 8;
+    b_off[i] = (uint32_t)(((size_t)min(n0 + row, N - 1) * K + c * 8) * 2);
   }
   const int nk_all = K / kTBK;
   const int ks0 = (int)((long)job.part * nk_all / job.parts);
   const int nk = (int)((long)(job.part + 1) * nk_all / job.parts) - ks0;
-#pragma unroll
-  for (int i = 0; i < kAInst; ++i) a_src[i] += ks0 * kTBK;
-#pragma unroll
-  for (int i = 0; i < kBInst; ++i) b_src[i] += ks0 * kTBK;
+  const uint16_t* a_base = A + ks0 * kTBK;
+  const uint16_t* a_lo_base = (kPl == 2 ? A_lo : A) + ks0 * kTBK;
+  const uint16_t* b_base = Wexp + ks0 * kTBK;
+  auto a_plane_base = [&](int i) { return (i * NW * 8) / BM ? a_lo_base : a_base; };
   // Steps past the last are clamped to it: those loads refill a free stage and
   // are never read, which keeps the loop body branch-free.
   const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
@@ -312,13 +322,13 @@ __global__ __launch_bounds__(256, OCC) void ffn_tiled_kernel(
     const uint32_t base = lds0 + stage * kAStage;
     const int k0 = min(step, nk - 1) * kTBK;
 #pragma unroll
-    for (int i = 0; i < kAInst; ++i) load_lds16_raw(a_src[i] + k0, base + (i * NW + wave) * 1024);
+    for (int i = 0; i < kAInst; ++i) load_lds16_sv(a_plane_base(i) + k0, a_off[i], base + (i * NW + wave) * 1024);
   };
   auto issue_b = [&](int stage, int step) {
     const uint32_t base = lds0 + kBBase + stage * kBStage;
     const int k0 = min(step, nk - 1) * kTBK;
 #pragma unroll
-    for (int i = 0; i < kBInst; ++i) load_lds16_raw(b_src[i] + k0, base + (i * NW + wave) * 1024);
+    for (int i = 0; i < kBInst; ++i) load_lds16_sv(b_base + k0, b_off[i], base + (i * NW + wave) * 1024);
   };
 
   // Main loop and epilogue for a wave whose rows of the tile fill kMA of its
@@ -416,12 +426,12 @@ __global__ __launch_bounds__(256, OCC) void ffn_tiled_kernel(
       const int sa1 = sa ^ 1, sb1 = sb == WS - 1 ? 0 : sb + 1, sbw = sb == 0 ? WS - 1 : sb - 1;
       const int kbw = min(kt + WS - 1, nk - 1) * kTBK, kba = min(kt + 2, nk - 1) * kTBK;
       half_step(xa, xb, ya, yb, sa, sb, 1,
-                [&](int i) { load_lds16_raw(b_src[i] + kbw, lds0 + kBBase + sbw * kBStage + (i * NW + wave) * 1024); },
+                [&](int i) { load_lds16_sv(b_base + kbw, b_off[i], lds0 + kBBase + sbw * kBStage + (i * NW + wave) * 1024); },
                 LoadsB{});
       __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kBInst));
       __syncthreads();
       half_step(ya, yb, xa, xb, sa1, sb1, 0,
-                [&](int i) { load_lds16_raw(a_src[i] + kba, lds0 + sa * kAStage + (i * NW + wave) * 1024); },
+                [&](int i) { load_lds16_sv(a_plane_base(i) + kba, a_off[i], lds0 + sa * kAStage + (i * NW + wave) * 1024); },
                 LoadsA{});
       sa = sa1;
       sb = sb1;

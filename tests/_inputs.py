@@ -68,15 +68,32 @@ SMALL = {
                                      "bf16", capacity_policy="reroute"),
     "batch64_top1_bf16": Workload("batch64_top1_bf16", 64, 384, 640, 16, 1, False, 0, False,
                                   "bf16"),
+    # every token's first choice is one expert (a logit bias of +6 on it): that expert's
+    # segment holds all T rows -- the longest run of m-tiles the tile schedule sees --
+    # on the stream path (fp32), the 128-row tiled path (top-1) and the 256-row tiled
+    # path (top-2, 275 rows per expert on average)
+    "one_expert_fp32": Workload("one_expert_fp32", 300, 128, 256, 4, 1, True, 0, True, "f32",
+                                router_bias=True),
+    "one_expert_top1_bf16": Workload("one_expert_top1_bf16", 700, 256, 512, 8, 1, True, 0, True,
+                                     "bf16", router_bias=True),
+    "one_expert_top2_bf16": Workload("one_expert_top2_bf16", 1100, 256, 384, 8, 2, True, 0, False,
+                                     "bf16", router_bias=True),
     # the mid-size layer's shapes (4096 tokens, 16 experts) with a selection bias
     "mid_select_bias_bf16": Workload("mid_select_bias_bf16", 4096, 1024, 4096, 16, 2, True, 0, True,
                                      "bf16", selection_bias=True),
 }
 
 
+ONE_EXPERT_HOT = 5     # the expert every token of the one_expert_* shapes picks first
+
+
 def small_router_bias(spec):
     """A fixed skew for the small skewed shapes (no calibration needed)."""
     E = spec.n_experts
+    if spec.name.startswith("one_expert"):
+        b = np.zeros(E, np.float32)
+        b[ONE_EXPERT_HOT % E] = 6.0
+        return b
     if spec.top_k == 1:                     # hot experts: every 8th
         b = np.zeros(E, np.float32)
         b[::8] = 1.0

@@ -78,6 +78,8 @@ def test_workspace_size_grows_with_shape():
     (dict(d_ff_shared=-128), B.MOE_ERR_INVALID),
     (dict(d_ff_shared=100), B.MOE_ERR_UNSUPPORTED),
     (dict(tokens=1 << 20, d_ff_shared=4096, top_k=1), B.MOE_ERR_UNSUPPORTED),
+    (dict(tokens=16, d_model=32768, d_ff=65536), B.MOE_ERR_UNSUPPORTED),
+    (dict(tokens=16, d_model=65536, d_ff=128, d_ff_shared=32768), B.MOE_ERR_UNSUPPORTED),
 ])
 def test_invalid_descriptors(kw, status):
     base = dict(tokens=64, d_model=256, d_ff=512, n_experts=8, top_k=2)
