@@ -291,6 +291,20 @@ int moe_combine(const moe_desc* desc, const float* o, const int32_t* dest, const
 int moe_forward(const moe_desc* desc, const void* x, const moe_weights* w, float* y, float* aux,
                 moe_routing* routing, void* workspace, size_t workspace_bytes, void* stream);
 
+/* moe_forward without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  The call allocates nothing: it runs moe_forward on a
+ * 32 MiB device array the library holds on each GPU it runs on until the
+ * process ends (enough for a decode batch of a Mixtral-shaped layer: 32
+ * tokens of d_model 4096, d_ff 14336, 8 experts, top-2 need 8.5 MiB).
+ * Layers whose moe_workspace_size() exceeds 32 MiB return MOE_ERR_UNSUPPORTED
+ * before anything is enqueued.  Arguments, results and errors are those of
+ * moe_forward.  Every call on one GPU uses the same array, which keeps the
+ * last call's contents: calls that overlap on one GPU (two streams, two
+ * threads) race on it and must be serialised by the caller. */
+int moe_forward_noalloc(const moe_desc* desc, const void* x, const moe_weights* w, float* y,
+                        float* aux, moe_routing* routing, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -23,7 +23,7 @@ _POLICIES = {"drop": MOE_CAPACITY_DROP, "reroute": MOE_CAPACITY_REROUTE}
 
 ENTRY_POINTS = ("moe_status_string", "moe_last_error", "moe_workspace_size", "moe_query_plan",
                 "moe_route", "moe_permute", "moe_ffn_up", "moe_ffn_up_gather", "moe_ffn_down", "moe_grouped_ffn",
-                "moe_shared_ffn", "moe_combine", "moe_forward")
+                "moe_shared_ffn", "moe_combine", "moe_forward", "moe_forward_noalloc")
 
 
 class MoeError(RuntimeError):
@@ -84,6 +84,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "moe_shared_ffn": (I, [pd, P, pw, P, P, S, P]),
         "moe_combine": (I, [pd, P, P, P, P, P, P]),
         "moe_forward": (I, [pd, P, pw, P, P, pr, P, S, P]),
+        "moe_forward_noalloc": (I, [pd, P, pw, P, P, pr, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -380,6 +381,15 @@ def moe_forward(desc, x, weights, y, aux=None, routing=None, workspace=None, str
     _check(load_library().moe_forward(ctypes.byref(desc.to_c()), a.t(x, "x"),
                                       a.weights(weights, True, True), a.t(y, "y"), a.t(aux, "aux"), r,
                                       ws, nb, _stream(stream)))
+
+
+def moe_forward_noalloc(desc, x, weights, y, aux=None, routing=None, stream=None):
+    """moe_forward on the library's own device scratch (no workspace, no allocation)."""
+    a = _Args(desc, x)
+    r = a.routing(routing) if routing is not None else None
+    _check(load_library().moe_forward_noalloc(ctypes.byref(desc.to_c()), a.t(x, "x"),
+                                              a.weights(weights, True, True), a.t(y, "y"),
+                                              a.t(aux, "aux"), r, _stream(stream)))
 
 
 def forward(x: torch.Tensor, weights: Weights, desc: Desc, workspace=None, stream=None):

@@ -7,6 +7,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <limits>
+#include <mutex>
 
 #include "../../include/moe_mi355x.h"
 #include "kernels.h"
@@ -886,3 +887,55 @@ int moe_forward(const moe_desc* desc, const void* x, const moe_weights* w, float
 }
 
 }  // extern "C"
+
+// ---- the allocation-free layer call ------------------------------------------
+// moe_forward_noalloc runs moe_forward on a workspace the library owns: a
+// file-scope device array of kScratchBytes.  Each device holds its own copy;
+// its address is looked up once per device (with that device current) and the
+// kernels get that address, never the array's host-side name.  Every kernel of
+// the layer writes each workspace region before reading it, so nothing needs
+// clearing between calls.
+namespace {
+constexpr size_t kScratchBytes = size_t(32) << 20;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+int scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MOE_ERR_UNSUPPORTED, "device index %d is past the %d devices the scratch table holds",
+                dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(MOE_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+}  // namespace
+
+extern "C" int moe_forward_noalloc(const moe_desc* desc, const void* x, const moe_weights* w,
+                                   float* y, float* aux, moe_routing* routing, void* stream) {
+  if (int st = validate_desc(desc)) return st;
+  const size_t need = layout_of(desc).total;
+  if (need > kScratchBytes)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "moe_forward_noalloc: the layer needs %zu bytes of workspace, the library's scratch "
+                "holds %zu; use moe_forward with a caller workspace",
+                need, kScratchBytes);
+  void* ws = nullptr;
+  if (int st = scratch_of_current_device(&ws)) return st;
+  return moe_forward(desc, x, w, y, aux, routing, ws, kScratchBytes, stream);
+}

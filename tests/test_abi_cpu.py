@@ -308,3 +308,15 @@ def test_binding_sizes_follow_the_descriptor():
     assert e["o"] == (torch.float32, 20 * 256) and e["y"] == (torch.float32, 10 * 256)
     assert e["offsets"] == (torch.int32, 5) and e["src"] == (torch.int32, 20)
     assert e["w1_shared"] == (torch.bfloat16, 384 * 256) and e["b2_shared"] == (torch.bfloat16, 256)
+
+
+def test_noalloc_refuses_layers_past_its_scratch():
+    """The allocation-free call serves layers whose workspace fits its 32 MiB device
+    scratch and refuses larger ones before any HIP call (no GPU needed)."""
+    lib = moe.load_library()
+    w = B.CWeights(0x10000, None, 0x4000000, None, 0x6000000, None)
+    big = moe.Desc(16384, 4096, 14336, 8, 2, has_expert_bias=False)
+    st = lib.moe_forward_noalloc(ctypes.byref(big.to_c()), 0x1000000, ctypes.byref(w), 0x2000000,
+                                 None, None, None)
+    assert st == B.MOE_ERR_UNSUPPORTED and "scratch" in lib.moe_last_error().decode()
+    assert moe.moe_workspace_size(moe.Desc(32, 4096, 14336, 8, 2)) <= 32 << 20
