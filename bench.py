@@ -127,12 +127,15 @@ def parity_of(spec, ref, y, aux, routing):
                                   and np.array_equal(routing.dest.cpu().numpy(), ref["dest"]))}
 
 
-def stream_read_gbs(dev, mib=4096, reps=10):
-    """A plain streaming read of `mib` MiB (torch's sum over an fp32 buffer) on the
-    same GPU: the practical HBM read ceiling next to the 8 TB/s grade."""
+def stream_read_gbs(dev, mib=1792, reps=20):
+    """The library's plain streaming-read probe over `mib` MiB (about the decode
+    layer's expert bank) on the same GPU: the practical HBM read ceiling next to
+    the 8 TB/s grade."""
     import torch
+    import sparse_mixture_experts_49_amd as moe
     buf = torch.ones(mib * (1 << 20) // 4, dtype=torch.float32, device=dev)
-    ms = _time_events(lambda: buf.sum(), reps)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    ms = _time_events(lambda: moe.moe_read_probe(buf, sink), reps)
     del buf
     return round(mib * (1 << 20) / (ms * 1e-3) / 1e9, 1)
 

@@ -291,6 +291,13 @@ int moe_combine(const moe_desc* desc, const float* o, const int32_t* dest, const
 int moe_forward(const moe_desc* desc, const void* x, const moe_weights* w, float* y, float* aux,
                 moe_routing* routing, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Measurement aid, not part of the layer: one plain streaming read of `bytes`
+ * bytes of device memory at buf (each wave reads its own contiguous 16 KiB),
+ * the practical HBM read ceiling that the weight-bound kernels are compared
+ * with.  bytes must be a positive multiple of 65536 (else MOE_ERR_INVALID);
+ * sink is a device uint32 the kernel may write (never read back). */
+int moe_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+
 /* moe_forward without a workspace argument, for callers that cannot allocate
  * device memory: code under HIP graph capture, tight serving loops, harnesses
  * that forbid allocation.  The call allocates nothing: it runs moe_forward on a

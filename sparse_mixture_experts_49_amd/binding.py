@@ -23,7 +23,8 @@ _POLICIES = {"drop": MOE_CAPACITY_DROP, "reroute": MOE_CAPACITY_REROUTE}
 
 ENTRY_POINTS = ("moe_status_string", "moe_last_error", "moe_workspace_size", "moe_query_plan",
                 "moe_route", "moe_permute", "moe_ffn_up", "moe_ffn_up_gather", "moe_ffn_down", "moe_grouped_ffn",
-                "moe_shared_ffn", "moe_combine", "moe_forward", "moe_forward_noalloc")
+                "moe_shared_ffn", "moe_combine", "moe_forward", "moe_forward_noalloc",
+                "moe_read_probe")
 
 
 class MoeError(RuntimeError):
@@ -85,6 +86,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "moe_combine": (I, [pd, P, P, P, P, P, P]),
         "moe_forward": (I, [pd, P, pw, P, P, pr, P, S, P]),
         "moe_forward_noalloc": (I, [pd, P, pw, P, P, pr, P]),
+        "moe_read_probe": (I, [P, S, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -390,6 +392,14 @@ def moe_forward_noalloc(desc, x, weights, y, aux=None, routing=None, stream=None
     _check(load_library().moe_forward_noalloc(ctypes.byref(desc.to_c()), a.t(x, "x"),
                                               a.weights(weights, True, True), a.t(y, "y"),
                                               a.t(aux, "aux"), r, _stream(stream)))
+
+
+def moe_read_probe(buf: torch.Tensor, sink: torch.Tensor, stream=None):
+    """One plain streaming read of buf (a measurement aid, not part of the layer)."""
+    check_tensor(buf, "buf", None, 0, None)
+    check_tensor(sink, "sink", torch.int32, 1, buf.device)
+    _check(load_library().moe_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                         _stream(stream)))
 
 
 def forward(x: torch.Tensor, weights: Weights, desc: Desc, workspace=None, stream=None):

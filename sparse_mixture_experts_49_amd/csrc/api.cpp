@@ -888,6 +888,17 @@ int moe_forward(const moe_desc* desc, const void* x, const moe_weights* w, float
 
 }  // extern "C"
 
+extern "C" int moe_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  MOE_REQUIRE_PTR(buf, "buf");
+  MOE_REQUIRE_PTR(sink, "sink");
+  const size_t g = moe::read_probe_granule();
+  if (bytes == 0 || bytes % g)
+    return fail(MOE_ERR_INVALID, "bytes must be a positive multiple of %zu", g);
+  if (bytes / g > 0x7fffffffu) return fail(MOE_ERR_UNSUPPORTED, "bytes too large");
+  return hip_status(moe::launch_read_probe(buf, bytes, sink, static_cast<hipStream_t>(stream)),
+                    "read probe launch");
+}
+
 // ---- the allocation-free layer call ------------------------------------------
 // moe_forward_noalloc runs moe_forward on a workspace the library owns: a
 // file-scope device array of kScratchBytes.  Each device holds its own copy;

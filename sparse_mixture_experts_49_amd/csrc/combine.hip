@@ -39,12 +39,22 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   }
   f32x4 ov[8];
   if (partial) {
+    // Up to kMaxParts split parts per slot are loaded before any is added, so
+    // all of a thread's loads are in flight together; the sum runs in part order.
+    constexpr int kMaxParts = 8;
 #pragma unroll
     for (int s = 0; s < 8; ++s)
       if (dst[s] >= 0) {
         const float* p = partial + (size_t)dst[s] * d + (size_t)v * 4;
-        ov[s] = *reinterpret_cast<const f32x4*>(p);
-        for (int sp = 1; sp < splits; ++sp)
+        f32x4 part[kMaxParts];
+#pragma unroll
+        for (int sp = 0; sp < kMaxParts; ++sp)
+          if (sp < splits) part[sp] = *reinterpret_cast<const f32x4*>(p + (size_t)sp * rows_cap * d);
+        ov[s] = part[0];
+#pragma unroll
+        for (int sp = 1; sp < kMaxParts; ++sp)
+          if (sp < splits) ov[s] += part[sp];
+        for (int sp = kMaxParts; sp < splits; ++sp)
           ov[s] += *reinterpret_cast<const f32x4*>(p + (size_t)sp * rows_cap * d);
       }
   } else {

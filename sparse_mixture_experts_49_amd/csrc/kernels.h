@@ -112,4 +112,9 @@ struct CombineArgs {
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 
+// Streaming-read probe (measurement aid): reads `bytes` (a multiple of
+// read_probe_granule()) of device memory once.
+size_t read_probe_granule();
+hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t s);
+
 }  // namespace moe

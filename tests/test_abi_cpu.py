@@ -320,3 +320,10 @@ def test_noalloc_refuses_layers_past_its_scratch():
                                  None, None, None)
     assert st == B.MOE_ERR_UNSUPPORTED and "scratch" in lib.moe_last_error().decode()
     assert moe.moe_workspace_size(moe.Desc(32, 4096, 14336, 8, 2)) <= 32 << 20
+
+
+def test_read_probe_checks_its_size():
+    lib = moe.load_library()
+    assert lib.moe_read_probe(0x100000, 65536 + 16, 0x200000, None) == B.MOE_ERR_INVALID
+    assert lib.moe_read_probe(0x100000, 0, 0x200000, None) == B.MOE_ERR_INVALID
+    assert lib.moe_read_probe(None, 65536, 0x200000, None) == B.MOE_ERR_INVALID

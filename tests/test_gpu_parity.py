@@ -418,3 +418,14 @@ def test_reroute_moves_overflow_within_capacity():
     assert counts.max() <= spec.capacity and np.array_equal(counts, ref["counts"])
     assert r.reroute_rounds.item() == ref["reroute_rounds"] > 1
     assert G.rel_err(r.topk_w.cpu().numpy(), wt) <= G.TOL_W
+
+
+def test_read_probe_reads_without_writing():
+    """The streaming-read probe (a measurement aid) runs over a buffer and leaves it
+    as it was; its sink is written only for one impossible XOR value."""
+    buf = torch.arange(1 << 20, dtype=torch.int32, device=G.DEV)      # 4 MiB
+    ref = buf.clone()
+    sink = torch.zeros(1, dtype=torch.int32, device=G.DEV)
+    moe.moe_read_probe(buf, sink)
+    torch.cuda.synchronize()
+    assert torch.equal(buf, ref)

@@ -127,9 +127,9 @@ MUTATIONS = [
     ("routing_weights", _no_renorm, [P.test_eight_expert_example_top2]),
     ("topk_by_logit", _ties_to_higher, [P.test_exact_ties_go_to_lower_index]),
     ("capacity_keep", _keep_last, [P.test_capacity_hand_case]),
-    ("aux_loss", _aux_all_slots, [P.test_oracle_matches_listing_structure_toy]),
+    ("aux_loss", _aux_all_slots, [P.test_oracle_matches_the_definition_token_by_token]),
     ("expert_ffn", _ffn_no_out_bias, [P.test_single_expert_reduces_to_dense_mlp]),
-    ("expert_ffn", _ffn_transposed, [P.test_oracle_matches_listing_structure_toy]),
+    ("expert_ffn", _ffn_transposed, [P.test_oracle_matches_the_definition_token_by_token]),
     ("router_z_loss", _z_no_square, [functools.partial(RX.test_z_loss_of_equal_logits_is_log_E_squared, 8),
                                      RX.test_z_loss_of_one_hot_logits]),
     ("selection_scores", _selection_ignores_bias,

@@ -70,20 +70,21 @@ def test_three_score_example():
     np.testing.assert_allclose(r3["topk_w"][0], [0.75, 0.15], atol=1e-12)
 
 
-def test_run_it_demo_semantics():
-    """The aiinbed demo: seed 7, Gaussian scores for 8 experts and 4 tokens, softmax,
-    stable descending sort, top-2, shares renormalised over the two picks."""
+def test_topk_on_gaussian_scores_by_definition():
+    """Seeded Gaussian scores for 8 experts (the shape of the aiinbed page's router
+    demo): every chosen expert's probability is at least every unchosen one's, the
+    choices come in descending order, and the renormalised weights are the chosen
+    probabilities scaled to sum to 1."""
     rng = random.Random(7)
-    scores = [[rng.gauss(0, 1) for _ in range(8)] for _ in range(4)]
+    scores = np.array([[rng.gauss(0, 1) for _ in range(8)] for _ in range(64)])
     r = _route_logits(scores, 2)
-    for t, sc in enumerate(scores):
-        ex = [math.exp(s) for s in sc]
-        tot = sum(ex)
-        probs = [e / tot for e in ex]
-        best = sorted(range(8), key=lambda i: probs[i], reverse=True)[:2]
-        assert r["topk_idx"][t].tolist() == best
-        share = sum(probs[i] for i in best)
-        np.testing.assert_allclose(r["topk_w"][t], [probs[i] / share for i in best], rtol=1e-12)
+    p = O.softmax(scores)
+    for t in range(scores.shape[0]):
+        c = r["topk_idx"][t]
+        rest = np.setdiff1d(np.arange(8), c)
+        assert p[t, c[0]] >= p[t, c[1]] >= p[t, rest].max()
+        np.testing.assert_allclose(r["topk_w"][t], p[t, c] / p[t, c].sum(), rtol=1e-12)
+        np.testing.assert_allclose(r["topk_w"][t].sum(), 1.0, rtol=1e-15)
 
 
 def test_exact_ties_go_to_lower_index():
@@ -289,44 +290,35 @@ def test_oracle_equals_scalar_loops(k, renorm, cap):
     assert r["topk_idx"][:, 0].tolist() == lp["top1"]
 
 
-class _ListingStyleMoE(torch.nn.Module):
-    """The layer as the lecture-hall page's PyTorch listing structures it (router
-    Linear without bias, per-expert Linear-GELU-Linear, loop over experts with a
-    mask of the chosen tokens, Switch aux loss), written here in fp64 with torch's
-    own softmax, topk and exact GELU."""
-
-    def __init__(self, inp, E):
-        super().__init__()
-        t = lambda a: torch.from_numpy(O.widen(a))
-        self.wr = t(inp["w_router"])
-        self.w1, self.w2 = t(inp["w1"]), t(inp["w2"])
-        self.b1, self.b2 = t(inp["b1"]), t(inp["b2"])
-        self.E = E
-
-    def forward(self, x, k):
-        probs = torch.softmax(x @ self.wr.T, dim=-1)
-        topv, topi = probs.topk(k, dim=-1)
-        topv = topv / topv.sum(-1, keepdim=True)
-        out = torch.zeros_like(x)
-        for e in range(self.E):
-            sel = topi == e
-            rows = sel.any(-1).nonzero(as_tuple=True)[0]
-            if rows.numel() == 0:
-                continue
-            w = (topv * sel)[rows].sum(-1, keepdim=True)
-            h = F.gelu(x[rows] @ self.w1[e].T + self.b1[e])
-            out[rows] += w * (h @ self.w2[e].T + self.b2[e])
-        frac = F.one_hot(topi[:, 0], self.E).double().mean(0)
-        aux = self.E * (frac * probs.mean(0)).sum()
-        return out, aux, topi
+def _layer_by_definition(inp, E, k):
+    """The layer written straight from its definition, token by token, in torch fp64:
+    p = softmax(W_r x); the k largest p (torch.topk); weights p_i / sum of the chosen
+    p; y = sum over the chosen experts of w_i (W2_i GELU(W1_i x + b1_i) + b2_i) with
+    the exact erf GELU; aux = E * sum_i f_i P_i with f_i the share of tokens whose
+    first choice is i and P_i the mean of p_i."""
+    t = lambda a: torch.from_numpy(O.widen(a))
+    x, wr = t(inp["x"]), t(inp["w_router"])
+    w1, w2, b1, b2 = t(inp["w1"]), t(inp["w2"]), t(inp["b1"]), t(inp["b2"])
+    T = x.shape[0]
+    p = torch.softmax(x @ wr.T, dim=-1)
+    y = torch.zeros_like(x)
+    chosen = []
+    for tok in range(T):
+        pv, idx = torch.topk(p[tok], k)
+        chosen.append(idx.tolist())
+        for wgt, e in zip((pv / pv.sum()).tolist(), idx.tolist()):
+            y[tok] += wgt * (w2[e] @ F.gelu(w1[e] @ x[tok] + b1[e]) + b2[e])
+    f = torch.bincount(torch.tensor([c[0] for c in chosen]), minlength=E).double() / T
+    aux = E * torch.dot(f, p.mean(0))
+    return y, aux, np.array(chosen)
 
 
-def test_oracle_matches_listing_structure_toy():
+def test_oracle_matches_the_definition_token_by_token():
     spec, inp = inputs_for("toy_fp32")
     desc = O.desc_of(spec)
     r = O.forward(inp, desc)
-    y, aux, topi = _ListingStyleMoE(inp, spec.n_experts)(torch.from_numpy(O.widen(inp["x"])), spec.top_k)
-    assert np.array_equal(topi.numpy(), r["topk_idx"])
+    y, aux, chosen = _layer_by_definition(inp, spec.n_experts, spec.top_k)
+    assert np.array_equal(chosen, r["topk_idx"])
     np.testing.assert_allclose(r["y"], y.numpy(), rtol=1e-12, atol=1e-13)
     assert abs(r["aux"] - aux.item()) < 1e-12
 
