@@ -20,6 +20,7 @@ namespace moe {
 // Thread (blockIdx.y * 256 + threadIdx.x) of block row t sums four adjacent
 // columns of token t: its k expert-output loads are independent, so they are
 // all in flight at once, and a few tokens (decode) still spread over many waves.
+template <bool PARTIAL>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ o,
                                                       const int32_t* __restrict__ dest,
                                                       const float* __restrict__ topk_w,
@@ -37,10 +38,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     dst[s] = (s < k) ? dest[(size_t)t * k + s] : -1;
     w[s] = (s < k) ? topk_w[(size_t)t * k + s] : 0.f;
   }
-  f32x4 ov[8];
-  if (partial) {
-    // Up to kMaxParts split parts per slot are loaded before any is added, so
-    // all of a thread's loads are in flight together; the sum runs in part order.
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (PARTIAL) {
+    // Deferred split-k sums (few tokens): per slot, its parts (up to kMaxParts)
+    // are loaded before any is added, so they are in flight together; the sum
+    // runs in part order, then the slot is weighted in slot order.
     constexpr int kMaxParts = 8;
 #pragma unroll
     for (int s = 0; s < 8; ++s)
@@ -50,32 +52,40 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 #pragma unroll
         for (int sp = 0; sp < kMaxParts; ++sp)
           if (sp < splits) part[sp] = *reinterpret_cast<const f32x4*>(p + (size_t)sp * rows_cap * d);
-        ov[s] = part[0];
+        f32x4 ov = part[0];
 #pragma unroll
         for (int sp = 1; sp < kMaxParts; ++sp)
-          if (sp < splits) ov[s] += part[sp];
+          if (sp < splits) ov += part[sp];
         for (int sp = kMaxParts; sp < splits; ++sp)
-          ov[s] += *reinterpret_cast<const f32x4*>(p + (size_t)sp * rows_cap * d);
+          ov += *reinterpret_cast<const f32x4*>(p + (size_t)sp * rows_cap * d);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = fmaf(w[s], ov[i], acc[i]);
       }
   } else {
+    f32x4 ov[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s)
       if (dst[s] >= 0) ov[s] = *reinterpret_cast<const f32x4*>(o + (size_t)dst[s] * d + (size_t)v * 4);
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      if (dst[s] >= 0)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = fmaf(w[s], ov[s][i], acc[i]);
   }
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int s = 0; s < 8; ++s)
-    if (dst[s] >= 0)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] = fmaf(w[s], ov[s][i], acc[i]);
   if (shared) acc += *reinterpret_cast<const f32x4*>(shared + (size_t)t * d + (size_t)v * 4);
   *reinterpret_cast<f32x4*>(y + (size_t)t * d + (size_t)v * 4) = acc;
 }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
   const dim3 grid(a.T, (a.d / 4 + 255) / 256);
-  combine_kernel<<<grid, 256, 0, s>>>(a.o, a.dest, a.topk_w, a.shared, a.T, a.d, a.k, a.y,
-                                      a.partial, a.splits, a.rows_cap);
+  // Two instances: with deferred split-k parts (the loads of every part of every
+  // slot in flight at once; few tokens) and without (few registers, many waves).
+  if (a.partial)
+    combine_kernel<true><<<grid, 256, 0, s>>>(a.o, a.dest, a.topk_w, a.shared, a.T, a.d, a.k, a.y,
+                                              a.partial, a.splits, a.rows_cap);
+  else
+    combine_kernel<false><<<grid, 256, 0, s>>>(a.o, a.dest, a.topk_w, a.shared, a.T, a.d, a.k, a.y,
+                                               a.partial, a.splits, a.rows_cap);
   return hipGetLastError();
 }
 

@@ -579,28 +579,49 @@ __global__ __launch_bounds__(256) void ffn_tile_reduce(
   const float* p0 = partial + (size_t)(job.slot - job.part) * kPartialTileFloats;
   const uint16_t* bexp = bias ? bias + (size_t)e * N + n0 : nullptr;
   constexpr int kQuads = BN / 4;
-  for (int q = ra * kQuads + threadIdx.x; q < rb * kQuads; q += 256) {
-    const int r = q / kQuads, c = (q % kQuads) * 4;
-    if (n0 + c >= N) continue;                      // past the last column
-    f32x4 v = *reinterpret_cast<const f32x4*>(p0 + (size_t)r * BN + c);
-    for (int sp = 1; sp < job.parts; ++sp)
-      v += *reinterpret_cast<const f32x4*>(p0 + sp * kPartialTileFloats + (size_t)r * BN + c);
-    if (bexp) {
-      const uint2 braw = *reinterpret_cast<const uint2*>(bexp + c);
-      v[0] += __uint_as_float(braw.x << 16);
-      v[1] += __uint_as_float(braw.x & 0xffff0000u);
-      v[2] += __uint_as_float(braw.y << 16);
-      v[3] += __uint_as_float(braw.y & 0xffff0000u);
-    }
-    const size_t idx = (size_t)(r0 + r) * N + n0 + c;
-    if constexpr (UP && SPLIT) {
+  // kU quads per thread per pass, all of their parts loaded before any is
+  // summed, so a pass keeps kU * parts loads in flight; parts add in part order.
+  constexpr int kU = 4;
+  const int q0 = ra * kQuads, q1 = rb * kQuads;
+  for (int qb = q0 + threadIdx.x; qb < q1; qb += 256 * kU) {
+    f32x4 part[kU][kMaxSplit];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) emit<uint16_t, true, true>(out, out_plane, idx + u, v[u]);
-    } else if constexpr (UP) {
-      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + idx) =
-          make_uint2(pack_bf16x2(gelu_erf(v[0]), gelu_erf(v[1])), pack_bf16x2(gelu_erf(v[2]), gelu_erf(v[3])));
-    } else {
-      *reinterpret_cast<f32x4*>(static_cast<float*>(out) + idx) = v;
+    for (int u = 0; u < kU; ++u) {
+      const int q = qb + u * 256;
+      const int r = q / kQuads, c = (q % kQuads) * 4;
+      if (q < q1 && n0 + c < N) {
+        const float* src = p0 + (size_t)r * BN + c;
+#pragma unroll
+        for (int sp = 0; sp < kMaxSplit; ++sp)
+          if (sp < job.parts) part[u][sp] = *reinterpret_cast<const f32x4*>(src + sp * kPartialTileFloats);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int q = qb + u * 256;
+      const int r = q / kQuads, c = (q % kQuads) * 4;
+      if (q >= q1 || n0 + c >= N) continue;          // past the range or the last column
+      f32x4 v = part[u][0];
+#pragma unroll
+      for (int sp = 1; sp < kMaxSplit; ++sp)
+        if (sp < job.parts) v += part[u][sp];
+      if (bexp) {
+        const uint2 braw = *reinterpret_cast<const uint2*>(bexp + c);
+        v[0] += __uint_as_float(braw.x << 16);
+        v[1] += __uint_as_float(braw.x & 0xffff0000u);
+        v[2] += __uint_as_float(braw.y << 16);
+        v[3] += __uint_as_float(braw.y & 0xffff0000u);
+      }
+      const size_t idx = (size_t)(r0 + r) * N + n0 + c;
+      if constexpr (UP && SPLIT) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) emit<uint16_t, true, true>(out, out_plane, idx + w, v[w]);
+      } else if constexpr (UP) {
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + idx) =
+            make_uint2(pack_bf16x2(gelu_erf(v[0]), gelu_erf(v[1])), pack_bf16x2(gelu_erf(v[2]), gelu_erf(v[3])));
+      } else {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(out) + idx) = v;
+      }
     }
   }
 }

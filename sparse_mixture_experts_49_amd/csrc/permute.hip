@@ -47,23 +47,38 @@ __global__ __launch_bounds__(256) void perm_hist_kernel(const int32_t* __restric
   if (threadIdx.x < E) blk_hist[(size_t)blockIdx.x * E + threadIdx.x] = h[threadIdx.x];
 }
 
-__global__ __launch_bounds__(64) void perm_scan_kernel(const int32_t* __restrict__ blk_hist,
-                                                       int nblk, int E, int capacity,
-                                                       int32_t* __restrict__ blk_base,
-                                                       int32_t* __restrict__ counts,
-                                                       int32_t* __restrict__ offsets) {
+// The block counts are first copied to LDS by all threads (coalesced, loads in
+// flight together) when they fit; expert e's thread then walks its column in
+// block order.
+constexpr int kScanThreads = 1024;
+constexpr int kScanLds = 16384;     // block-count entries staged in LDS (64 KiB)
+
+__global__ __launch_bounds__(kScanThreads) void perm_scan_kernel(const int32_t* __restrict__ blk_hist,
+                                                                 int nblk, int E, int capacity,
+                                                                 int32_t* __restrict__ blk_base,
+                                                                 int32_t* __restrict__ counts,
+                                                                 int32_t* __restrict__ offsets) {
+  __shared__ int hs[kScanLds];
   __shared__ int kept[64];
-  const int e = threadIdx.x;
-  int run = 0;
-  if (e < E) {
-    for (int b = 0; b < nblk; ++b) {
-      blk_base[(size_t)b * E + e] = run;
-      run += blk_hist[(size_t)b * E + e];
-    }
-  }
-  kept[e] = (e < E) ? ((capacity > 0) ? min(run, capacity) : run) : 0;
+  const int tid = threadIdx.x;
+  const int n = nblk * E;
+  const bool staged = n <= kScanLds;
+  if (staged)
+    for (int i = tid; i < n; i += kScanThreads) hs[i] = blk_hist[i];
   __syncthreads();
-  if (e == 0) {
+  if (tid < 64) {
+    const int e = tid;
+    int run = 0;
+    if (e < E) {
+      for (int b = 0; b < nblk; ++b) {
+        blk_base[(size_t)b * E + e] = run;
+        run += staged ? hs[b * E + e] : blk_hist[(size_t)b * E + e];
+      }
+    }
+    kept[e] = (e < E) ? ((capacity > 0) ? min(run, capacity) : run) : 0;
+  }
+  __syncthreads();
+  if (tid == 0) {
     int acc = 0;
     for (int i = 0; i < E; ++i) {
       offsets[i] = acc;
@@ -75,9 +90,11 @@ __global__ __launch_bounds__(64) void perm_scan_kernel(const int32_t* __restrict
 }
 
 // Wave w of block b ranks assignments [b*1024 + w*256, +256) in four batches
-// of 64 lanes.  In a batch, lanes that share an expert are grouped with
-// ballots; a lane's rank is the number of earlier lanes of its group plus the
-// wave's running count for that expert (held by lane e of the wave).
+// of 64 lanes.  In a batch, the lanes that share an expert are matched with one
+// ballot per bit of the expert id (wave_rank); a lane's rank is the number of
+// earlier lanes of its group plus the wave's running count for that expert,
+// which the group's first lane then advances (LDS, this wave's row only, so the
+// wave's own program order keeps reads and updates in sequence).
 __global__ __launch_bounds__(256) void perm_rank_kernel(const int32_t* __restrict__ topk_idx,
                                                         int A, int E, int capacity,
                                                         const int32_t* __restrict__ blk_base,
@@ -88,27 +105,20 @@ __global__ __launch_bounds__(256) void perm_rank_kernel(const int32_t* __restric
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int base = blockIdx.x * kPermChunk + wave * 256;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  int cnt = 0;
+  wcount[wave][lane] = 0;
   int ex[4], rk[4];
 #pragma unroll
   for (int bt = 0; bt < 4; ++bt) {
     const int a = base + bt * 64 + lane;
     int e = (a < A) ? topk_idx[a] : -1;
     if (e < 0 || e >= E) e = -1;
+    int grp;
+    const int within = wave_rank(e, lt_mask, grp);
+    const int before = e >= 0 ? wcount[wave][e] : 0;
     ex[bt] = e;
-    rk[bt] = 0;
-    uint64_t remaining = __ballot(e >= 0);
-    while (remaining) {
-      const int leader = __ffsll((unsigned long long)remaining) - 1;
-      const int ee = __shfl(e, leader);
-      const uint64_t m = __ballot(e == ee);
-      const int before = __shfl(cnt, ee);
-      if (e == ee) rk[bt] = before + __popcll(m & lt_mask);
-      if (lane == ee) cnt += __popcll(m);
-      remaining &= ~m;
-    }
+    rk[bt] = before + within;
+    if (e >= 0 && within == 0) wcount[wave][e] = before + grp;
   }
-  wcount[wave][lane] = cnt;
   __syncthreads();
 #pragma unroll
   for (int bt = 0; bt < 4; ++bt) {
@@ -193,7 +203,7 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t s) {
   }
   const int nblk = permute_blocks(A);
   perm_hist_kernel<<<nblk, 256, 0, s>>>(a.topk_idx, A, a.E, a.blk_hist);
-  perm_scan_kernel<<<1, 64, 0, s>>>(a.blk_hist, nblk, a.E, a.capacity, a.blk_base, a.counts,
+  perm_scan_kernel<<<1, kScanThreads, 0, s>>>(a.blk_hist, nblk, a.E, a.capacity, a.blk_base, a.counts,
                                     a.offsets);
   perm_rank_kernel<<<nblk, 256, 0, s>>>(a.topk_idx, A, a.E, a.capacity, a.blk_base, a.offsets,
                                         a.dest, a.src);
