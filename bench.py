@@ -372,6 +372,37 @@ def summarize(args):
                          f"{float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
                          f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
         lines.append("")
+    if args.mfma_csv:
+        # Per kernel name, averaged over its dispatches: shader clock from the
+        # GPU-busy cycle count (summed over the 8 XCDs) over the dispatch's duration,
+        # and the share of those cycles each SIMD's matrix unit was busy.
+        xcds, simds = 8, 1024
+        per = {}
+        for r in _rows(args.mfma_csv):
+            k = r["Kernel_Name"]
+            if _entry_of(k) is None:
+                continue
+            d = per.setdefault(k, {}).setdefault(r["Dispatch_Id"], {})
+            d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+            d["_ns"] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+        lines += ["## MFMA utilisation and shader clock (`--pmc GRBM_GUI_ACTIVE SQ_BUSY_CYCLES "
+                  "SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA`)", "",
+                  "Clock = GRBM_GUI_ACTIVE / 8 XCDs / dispatch duration (this counter run's own "
+                  "timestamps); MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs / (GRBM_GUI_ACTIVE / 8).",
+                  "", "| kernel | entry point | dispatches | clock GHz | MFMA busy | MFMA instructions |",
+                  "|---|---|---|---|---|---|"]
+        for k, ds in sorted(per.items()):
+            vals = [v for v in ds.values() if v.get("GRBM_GUI_ACTIVE") and v["_ns"] > 0]
+            if not vals:
+                continue
+            clk = sum(v["GRBM_GUI_ACTIVE"] / xcds / v["_ns"] for v in vals) / len(vals)
+            busy = sum(v.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / simds / (v["GRBM_GUI_ACTIVE"] / xcds)
+                       for v in vals) / len(vals)
+            mi = sum(v.get("SQ_INSTS_MFMA", 0.0) for v in vals) / len(vals)
+            if mi == 0:
+                continue
+            lines.append(f"| `{_short(k)}` | {_entry_of(k)} | {len(vals)} | {clk:.2f} | {busy:.1%} | {mi:.4g} |")
+        lines.append("")
     if args.fetch_csv and args.write_csv:
         fetch = _counter_avgs(args.fetch_csv, "FETCH_SIZE")
         write = _counter_avgs(args.write_csv, "WRITE_SIZE")
@@ -424,6 +455,7 @@ def main():
     ap.add_argument("--stats-csv")
     ap.add_argument("--fetch-csv")
     ap.add_argument("--write-csv")
+    ap.add_argument("--mfma-csv")
     ap.add_argument("--command", action="append")
     args = ap.parse_args()
     if args.summarize:
