@@ -209,7 +209,7 @@ struct Layout {
   size_t topk_idx, topk_w, counts, offsets, dest, src, top1, prob_mean;
   size_t h, o, partial;
   size_t sh_offsets, h_sh, o_sh;   // shared expert (d_ff_shared > 0)
-  size_t rr_score, rr_wt, rr_list;   // reroute policy
+  size_t rr_rank, rr_list;   // reroute policy
   size_t total;
 };
 
@@ -264,9 +264,8 @@ Layout layout_of(const moe_desc* d) {
   }
   L.partial = take(part);
   if (d->capacity_policy == MOE_CAPACITY_REROUTE) {
-    L.rr_score = take(T * 64 * sizeof(float));
-    L.rr_wt = take(T * E * sizeof(float));
-    L.rr_list = take(4 * A * sizeof(int32_t));
+    L.rr_rank = take(T * 64 * 2 * sizeof(int32_t));
+    L.rr_list = take(4 * T * sizeof(int32_t));
   }
   L.total = p;
   return L;
@@ -431,8 +430,7 @@ int launch_route(const moe_desc* d, const void* x, const moe_weights* w, int32_t
   a.prob_mean = pmean;
   a.aux = aux;
   a.z_loss = zl;
-  a.rr_score = rr ? at<float>(ws, L.rr_score) : nullptr;
-  a.rr_wt = rr ? at<float>(ws, L.rr_wt) : nullptr;
+  a.rr_rank = rr ? at<int32_t>(ws, L.rr_rank) : nullptr;
   a.rounds_zero = rr ? nullptr : rounds;
   if (layout) {
     a.perm = true;
@@ -445,8 +443,7 @@ int launch_route(const moe_desc* d, const void* x, const moe_weights* w, int32_t
   if (int st = hip_status(moe::launch_router(a, s), "router launch")) return st;
   if (!rr) return MOE_OK;
   moe::RerouteArgs b{};
-  b.score = a.rr_score;
-  b.wt = a.rr_wt;
+  b.rank = a.rr_rank;
   b.T = d->tokens;
   b.k = d->top_k;
   b.E = d->n_experts;

@@ -22,8 +22,8 @@ struct RouterArgs {
   float* prob_mean;        // optional
   float* aux;              // optional
   float* z_loss;           // optional
-  float* rr_score;         // [T][64] selection scores for the reroute policy (-inf past E), or null
-  float* rr_wt;            // [T][E] the weight each expert would get (prob / denominator), or null
+  int32_t* rr_rank;        // reroute policy, else null: [T][64][2], position p of token t holds
+                           // {expert of rank p, bits of the weight it would get} for p < E
   int32_t* rounds_zero;    // optional: set to 0 (no reroute runs)
   // Optional dispatch layout of a small layer (T*k <= 1024, drop policy), computed by
   // the aux reduction block right after the router: counts, offsets, dest and src as
@@ -41,13 +41,12 @@ int router_blocks(int T);
 hipError_t launch_router(const RouterArgs& a, hipStream_t s);
 
 struct RerouteArgs {
-  const float* score;      // [T][64] from the router (RouterArgs::rr_score)
-  const float* wt;         // [T][E] from the router (RouterArgs::rr_wt)
+  const int32_t* rank;     // [T][64][2] from the router (RouterArgs::rr_rank)
   int T, k, E, capacity;
   int32_t* topk_idx;       // in: router choices; out: serving expert or -1 if dropped
   float* topk_w;           // out: weight of the serving expert, 0 if dropped
-  int32_t* lists;          // [4][T*k] scratch: two lists (used in turn) of rejected slots:
-                           // token ids and requests (expert | cursor << 8 | slot << 16)
+  int32_t* lists;          // [4][T] scratch: two lists (used in turn) of tokens with rejected
+                           // slots: token ids and (cursor + 1) | pending slots << 8
   int32_t* rounds;         // optional: number of acceptance rounds
 };
 hipError_t launch_reroute(const RerouteArgs& a, hipStream_t s);

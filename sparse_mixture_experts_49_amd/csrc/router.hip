@@ -19,106 +19,120 @@
 
 namespace moe {
 
-constexpr int kRouterTokens = 16;   // tokens per block (one MFMA row tile)
+constexpr int kRouterTile = 16;     // tokens per MFMA row tile
 constexpr int kAuxThreads = 1024;   // threads of the single aux-reduction block
 constexpr int kRouterWaves = 8;     // the block's waves split d between them
 
-// LDS of one token tile: the waves' partial logits, then each token's
-// probabilities, first choice and log-sum-exp for the aux and z-loss sums.
-template <int WAVES>
+// LDS of a block of MT token tiles: the waves' partial logits, then each
+// token's probabilities, first choice and log-sum-exp for the aux and z-loss
+// sums, and (reroute policy) its ranking scores and weights.
+template <int WAVES, int MT>
 struct RouterTileLds {
-  float red[WAVES][kRouterTokens][65];
-  float prob[kRouterTokens][64];
-  int top1[kRouterTokens];
-  float lse[kRouterTokens];
+  float red[WAVES][kRouterTile * MT][65];
+  float prob[kRouterTile * MT][64];
+  float rsc[kRouterTile * MT][64];
+  float rwt[kRouterTile * MT][64];
+  int top1[kRouterTile * MT];
+  float lse[kRouterTile * MT];
 };
 
-// Tokens t0 .. t0+15 of the router: logits on MFMA (the WAVES waves split d),
-// softmax, top-k and the routing weights; fills sm.prob / top1 / lse.  Ends
-// with a barrier.  Wave w accumulates the k-chunks w, w+WAVES, ... of the
-// d-long dot products; the partial logit tiles are summed in wave order
-// through LDS, so the result does not depend on scheduling.
+// Tokens t0 .. t0 + 16*MT - 1 of the router: logits on MFMA (the WAVES waves
+// split d), softmax, top-k and the routing weights; fills sm.prob / top1 / lse
+// (and, with `rr`, sm.rsc / rwt).  Ends with a barrier.  Wave w accumulates
+// the k-chunks w, w+WAVES, ... of the d-long dot products; the partial logit
+// tiles are summed in wave order through LDS, so the result does not depend on
+// scheduling.
 //
 // Lane layout of the loads: lane l reads row (l % 16) -- a token of x, or an
-// expert row of W_r -- and 64 contiguous bytes starting at k-chunk offset
-// (l / 16) * 64 B, so each row's 256 B per chunk come from 4 lanes.  MFMA j of
-// the chunk consumes the lane's j-th 16-byte piece; A and B use the same map.
-template <typename T, int NT, int WAVES>
+// expert row of W_r -- and in load q of a chunk the 16 bytes at offset
+// q * 64 + (l / 16) * 16 of the row's 256-byte chunk, so the four lanes of a
+// row cover 64 contiguous bytes (half a cache line) per instruction.  MFMA q of
+// the chunk consumes load q; A and B use the same map, so each MFMA sums 32
+// (bf16) or 16 (fp32, four MFMAs) consecutive k.
+template <typename T, int NT, int WAVES, int MT>
 __device__ __forceinline__ void route_tile(
     const T* __restrict__ x, const T* __restrict__ wr, const float* __restrict__ br,
-    const float* __restrict__ bsel, int T_, int d, int E, int k, int renorm, int t0,
-    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, float* __restrict__ rr_score,
-    float* __restrict__ rr_wt, RouterTileLds<WAVES>& sm) {
-  constexpr int kPerLane = 64 / sizeof(T);          // elements per lane per chunk
-  constexpr int kChunk = 4 * kPerLane;              // 128 bf16 or 64 fp32
-  constexpr int kPerVec = 16 / sizeof(T);
+    const float* __restrict__ bsel, int T_, int d, int E, int k, int renorm, int t0, bool rr,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, RouterTileLds<WAVES, MT>& sm) {
+  constexpr int kPerVec = 16 / sizeof(T);           // elements per 16-byte piece
+  constexpr int kChunk = 16 * kPerVec;              // 128 bf16 or 64 fp32 = 256 bytes
   auto& red = sm.red;
-  auto& prob = sm.prob;
-  auto& top1 = sm.top1;
-  auto& lse = sm.lse;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, c = lane >> 4;
-  const T* xrow = x + (size_t)min(t0 + r, T_ - 1) * d + c * kPerLane;
+  const T* xrow[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+    xrow[m] = x + (size_t)min(t0 + 16 * m + r, T_ - 1) * d + c * kPerVec;
   const T* wrow[NT];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) wrow[nt] = wr + (size_t)min(nt * 16 + r, E - 1) * d + c * kPerLane;
+  for (int nt = 0; nt < NT; ++nt) wrow[nt] = wr + (size_t)min(nt * 16 + r, E - 1) * d + c * kPerVec;
 
-  f32x4 acc[NT];
+  f32x4 acc[MT][NT];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[m][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nch = d / kChunk;
-  auto load_chunk = [&](int ch, u32x4 (&a)[4], u32x4 (&b)[NT][4]) {
+  auto load_chunk = [&](int ch, u32x4 (&a)[MT][4], u32x4 (&b)[NT][4]) {
     const int kk = ch * kChunk;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) a[q] = ld16(xrow + kk + q * kPerVec);
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) a[m][q] = ld16(xrow[m] + kk + q * 4 * kPerVec);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) b[nt][q] = ld16(wrow[nt] + kk + q * kPerVec);
+      for (int q = 0; q < 4; ++q) b[nt][q] = ld16(wrow[nt] + kk + q * 4 * kPerVec);
   };
-  auto mma_chunk = [&](const u32x4 (&a)[4], const u32x4 (&b)[NT][4]) {
+  auto mma_chunk = [&](const u32x4 (&a)[MT][4], const u32x4 (&b)[NT][4]) {
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      if constexpr (sizeof(T) == 2) {
+    for (int m = 0; m < MT; ++m)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[nt] = mfma_bf16(a[q], b[nt][q], acc[nt]);
-      } else {
+      for (int nt = 0; nt < NT; ++nt) {
+        if constexpr (sizeof(T) == 2) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+          for (int q = 0; q < 4; ++q) acc[m][nt] = mfma_bf16(a[m][q], b[nt][q], acc[m][nt]);
+        } else {
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            acc[nt] = mfma_f32(__uint_as_float(a[q][i]), __uint_as_float(b[nt][q][i]), acc[nt]);
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              acc[m][nt] = mfma_f32(__uint_as_float(a[m][q][i]), __uint_as_float(b[nt][q][i]), acc[m][nt]);
+        }
       }
-    }
   };
   // Two chunks per iteration, both loaded before either is multiplied: with
   // few tokens (decode) the loop is bound by load latency.  The chunks are
   // accumulated in order ch = wave, wave + WAVES, ... either way.
   int ch = wave;
   for (; ch + WAVES < nch; ch += 2 * WAVES) {
-    u32x4 a0[4], b0[NT][4], a1[4], b1[NT][4];
+    u32x4 a0[MT][4], b0[NT][4], a1[MT][4], b1[NT][4];
     load_chunk(ch, a0, b0);
     load_chunk(ch + WAVES, a1, b1);
     mma_chunk(a0, b0);
     mma_chunk(a1, b1);
   }
   if (ch < nch) {
-    u32x4 a0[4], b0[NT][4];
+    u32x4 a0[MT][4], b0[NT][4];
     load_chunk(ch, a0, b0);
     mma_chunk(a0, b0);
   }
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
+  for (int m = 0; m < MT; ++m)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) red[wave][4 * c + i][nt * 16 + r] = acc[nt][i];
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[wave][16 * m + 4 * c + i][nt * 16 + r] = acc[m][nt][i];
   __syncthreads();
 
-  if (wave == 0) {
-    // Four lanes per token: lane quarter q holds experts q, q+4, q+8, ...
+  if (wave < MT) {
+    // Wave w finishes token tile w.  Four lanes per token: lane quarter q holds
+    // experts q, q+4, q+8, ...
     const int tq = lane >> 2, q = lane & 3;
-    const int t = t0 + tq;
+    const int tr = 16 * wave + tq;                   // token row of the block
+    const int t = t0 + tr;
     constexpr int kMaxPer = 16;
     float g[kMaxPer], p[kMaxPer], sc[kMaxPer];
     float m = -INFINITY;
@@ -127,9 +141,9 @@ __device__ __forceinline__ void route_tile(
       const int e = q + 4 * j;
       g[j] = -INFINITY;
       if (e < E) {
-        g[j] = red[0][tq][e];
+        g[j] = red[0][tr][e];
 #pragma unroll
-        for (int w = 1; w < WAVES; ++w) g[j] += red[w][tq][e];   // in wave order
+        for (int w = 1; w < WAVES; ++w) g[j] += red[w][tr][e];   // in wave order
         if (br) g[j] += br[e];
         m = fmaxf(m, g[j]);
       }
@@ -151,7 +165,7 @@ __device__ __forceinline__ void route_tile(
       const int e = q + 4 * j;
       sc[j] = (bsel && e < E) ? g[j] + bsel[e] : g[j];   // ranking scores
     }
-    if (q == 0) lse[tq] = m + logf(s);
+    if (q == 0) sm.lse[tr] = m + logf(s);
 
     // top-k: k rounds of a quad-wide argmax over the unselected logits.
     uint32_t taken = 0;
@@ -203,37 +217,39 @@ __device__ __forceinline__ void route_tile(
         }
       }
     }
-    if (rr_score && t < T_) {                       // inputs of the reroute policy
+    if (rr) {                                        // inputs of the expert ranking
 #pragma unroll
       for (int j = 0; j < kMaxPer; ++j) {
-        const int e = q + 4 * j;                     // rows of 64 scores, -inf past E
-        rr_score[(size_t)t * 64 + e] = e < E ? sc[j] : -INFINITY;
-        if (e < E) rr_wt[(size_t)t * E + e] = renorm ? p[j] * winv : p[j];
+        const int e = q + 4 * j;                     // rows of 64, -inf past E
+        sm.rsc[tr][e] = e < E ? sc[j] : -INFINITY;
+        sm.rwt[tr][e] = renorm ? p[j] * winv : p[j];
       }
     }
 #pragma unroll
     for (int j = 0; j < kMaxPer; ++j) {
       const int e = q + 4 * j;
-      if (e < E) prob[tq][e] = (t < T_) ? p[j] : 0.f;
+      if (e < E) sm.prob[tr][e] = (t < T_) ? p[j] : 0.f;
     }
-    if (q == 0) top1[tq] = (t < T_) ? sel_e[0] : -1;
+    if (q == 0) sm.top1[tr] = (t < T_) ? sel_e[0] : -1;
   }
   __syncthreads();
 }
 
-// One block = 16 tokens x all experts, 8 waves splitting d.  The block then
-// writes its partial sums of the aux loss and z-loss for aux_finalize_kernel.
-template <typename T, int NT>
+// One block = 16*MT tokens x all experts, 8 waves splitting d.  The block then
+// writes its partial sums of the aux loss and z-loss for aux_finalize_kernel
+// and, for the reroute policy, every token's experts in ranking order.
+template <typename T, int NT, int MT>
 __global__ __launch_bounds__(kRouterWaves * 64) void router_kernel(
     const T* __restrict__ x, const T* __restrict__ wr, const float* __restrict__ br,
     const float* __restrict__ bsel, int T_, int d, int E, int k, int renorm,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
     double* __restrict__ part_psum, int32_t* __restrict__ part_top1, double* __restrict__ part_z,
-    float* __restrict__ rr_score, float* __restrict__ rr_wt) {
-  __shared__ RouterTileLds<kRouterWaves> sm;
-  const int t0 = blockIdx.x * kRouterTokens;
-  route_tile<T, NT, kRouterWaves>(x, wr, br, bsel, T_, d, E, k, renorm, t0, topk_idx, topk_w,
-                                  rr_score, rr_wt, sm);
+    int32_t* __restrict__ rr_rank) {
+  __shared__ RouterTileLds<kRouterWaves, MT> sm;
+  constexpr int kTok = kRouterTile * MT;
+  const int t0 = blockIdx.x * kTok;
+  route_tile<T, NT, kRouterWaves, MT>(x, wr, br, bsel, T_, d, E, k, renorm, t0, rr_rank != nullptr,
+                                      topk_idx, topk_w, sm);
   auto& prob = sm.prob;
   auto& top1 = sm.top1;
   auto& lse = sm.lse;
@@ -243,7 +259,7 @@ __global__ __launch_bounds__(kRouterWaves * 64) void router_kernel(
     double ps = 0.0;
     int cnt = 0;
 #pragma unroll
-    for (int i = 0; i < kRouterTokens; ++i) {
+    for (int i = 0; i < kTok; ++i) {
       ps += (double)prob[i][e];
       cnt += (top1[i] == e);
     }
@@ -252,8 +268,30 @@ __global__ __launch_bounds__(kRouterWaves * 64) void router_kernel(
   }
   if (threadIdx.x == 64) {                           // z-loss partial, token order
     double z = 0.0;
-    for (int i = 0; i < kRouterTokens && t0 + i < T_; ++i) z += (double)lse[i] * (double)lse[i];
+    for (int i = 0; i < kTok && t0 + i < T_; ++i) z += (double)lse[i] * (double)lse[i];
     part_z[blockIdx.x] = z;
+  }
+  if (rr_rank) {
+    // The token's experts in ranking order (higher score first, equal scores
+    // by lower index): expert e goes to position = the number of experts
+    // ranked above it, as {e, weight bits}.  Lanes of a wave take the 64
+    // experts of one token, so the score reads are LDS broadcasts.
+#pragma unroll 1
+    for (int idx = threadIdx.x; idx < kTok * 64; idx += kRouterWaves * 64) {
+      const int tr = idx >> 6, e = idx & 63, t = t0 + tr;
+      if (e >= E || t >= T_) continue;
+      const float s = sm.rsc[tr][e];
+      int pos = 0;
+#pragma unroll
+      for (int j = 0; j < 64; j += 4) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(&sm.rsc[tr][j]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) pos += (int)(v[u] > s) + (int)((v[u] == s) & (j + u < e));
+      }
+      typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
+      *reinterpret_cast<i32x2*>(rr_rank + ((size_t)t * 64 + pos) * 2) =
+          i32x2{e, (int32_t)__float_as_uint(sm.rwt[tr][e])};
+    }
   }
 }
 
@@ -329,23 +367,32 @@ __global__ __launch_bounds__(kAuxThreads) void aux_finalize_kernel(
 
 bool router_can_permute(int assignments) { return assignments <= kPermChunk; }
 
+// Two token tiles per block when the expert rows are many (E > 16) and the
+// tokens fill the chip with one block per CU: each W_r fragment loaded then
+// serves 32 tokens, halving the re-reads of W_r.
+static int router_tiles(int T, int E) { return (E > 16 && T >= 256 * 2 * kRouterTile) ? 2 : 1; }
+
 template <typename T>
 static hipError_t launch_router_t(const RouterArgs& a, hipStream_t s) {
-  const int nblk = (a.T + kRouterTokens - 1) / kRouterTokens;
   const int nt = (a.E + 15) / 16;
+  const int mt = router_tiles(a.T, a.E);
+  const int nblk = (a.T + kRouterTile * mt - 1) / (kRouterTile * mt);
   const T* x = static_cast<const T*>(a.x);
   const T* wr = static_cast<const T*>(a.w_router);
-#define MOE_ROUTER_CASE(NT)                                                                   \
-  case NT:                                                                                  \
-    router_kernel<T, NT><<<nblk, kRouterWaves * 64, 0, s>>>(                                  \
+#define MOE_ROUTER_CASE(NT, MT)                                                               \
+  case NT * 4 + MT:                                                                         \
+    router_kernel<T, NT, MT><<<nblk, kRouterWaves * 64, 0, s>>>(                              \
         x, wr, a.b_router, a.b_select, a.T, a.d, a.E, a.k, a.renorm, a.topk_idx, a.topk_w,   \
-        a.part_psum, a.part_top1, a.part_z, a.rr_score, a.rr_wt);                             \
+        a.part_psum, a.part_top1, a.part_z, a.rr_rank);                                       \
     break;
-  switch (nt) {
-    MOE_ROUTER_CASE(1)
-    MOE_ROUTER_CASE(2)
-    MOE_ROUTER_CASE(3)
-    MOE_ROUTER_CASE(4)
+  switch (nt * 4 + mt) {
+    MOE_ROUTER_CASE(1, 1)
+    MOE_ROUTER_CASE(2, 1)
+    MOE_ROUTER_CASE(3, 1)
+    MOE_ROUTER_CASE(4, 1)
+    MOE_ROUTER_CASE(2, 2)
+    MOE_ROUTER_CASE(3, 2)
+    MOE_ROUTER_CASE(4, 2)
     default: return hipErrorInvalidValue;
   }
 #undef MOE_ROUTER_CASE
@@ -359,7 +406,8 @@ static hipError_t launch_router_t(const RouterArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-int router_blocks(int T) { return (T + kRouterTokens - 1) / kRouterTokens; }
+// Upper bound of the blocks a router launch uses (sizes the partial-sum buffers).
+int router_blocks(int T) { return (T + kRouterTile - 1) / kRouterTile; }
 
 hipError_t launch_router(const RouterArgs& a, hipStream_t s) {
   return a.bf16 ? launch_router_t<uint16_t>(a, s) : launch_router_t<float>(a, s);
