@@ -452,6 +452,14 @@ int launch_route(const moe_desc* d, const void* x, const moe_weights* w, int32_t
   b.topk_w = wt;
   b.lists = at<int32_t>(ws, L.rr_list);
   b.rounds = rounds;
+  b.part_psum = a.part_psum;
+  b.part_top1 = a.part_top1;
+  b.part_z = a.part_z;
+  b.nblk = moe::router_launch_blocks(d->tokens, d->n_experts);
+  b.top1_count = top1;
+  b.prob_mean = pmean;
+  b.aux = aux;
+  b.z_loss = zl;
   return hip_status(moe::launch_reroute(b, s), "reroute launch");
 }
 

@@ -23,7 +23,8 @@ struct RouterArgs {
   float* aux;              // optional
   float* z_loss;           // optional
   int32_t* rr_rank;        // reroute policy, else null: [T][64][2], position p of token t holds
-                           // {expert of rank p, bits of the weight it would get} for p < E
+                           // {expert of rank p, bits of the weight it would get} for p < E;
+                           // the partials are then reduced by launch_reroute
   int32_t* rounds_zero;    // optional: set to 0 (no reroute runs)
   // Optional dispatch layout of a small layer (T*k <= 1024, drop policy), computed by
   // the aux reduction block right after the router: counts, offsets, dest and src as
@@ -38,6 +39,8 @@ struct RouterArgs {
 // Whether RouterArgs::perm may be used for T*k assignments.
 bool router_can_permute(int assignments);
 int router_blocks(int T);
+// Blocks (partial-sum rows) a router launch for T tokens and E experts uses.
+int router_launch_blocks(int T, int E);
 hipError_t launch_router(const RouterArgs& a, hipStream_t s);
 
 struct RerouteArgs {
@@ -48,6 +51,16 @@ struct RerouteArgs {
   int32_t* lists;          // [4][T] scratch: two lists (used in turn) of tokens with rejected
                            // slots: token ids and (cursor + 1) | pending slots << 8
   int32_t* rounds;         // optional: number of acceptance rounds
+  // The router's partials (RouterArgs; nblk = router_launch_blocks) and the
+  // optional aux outputs: a second block of the launch reduces them.
+  const double* part_psum;
+  const int32_t* part_top1;
+  const double* part_z;
+  int nblk;
+  int32_t* top1_count;
+  float* prob_mean;
+  float* aux;
+  float* z_loss;
 };
 hipError_t launch_reroute(const RerouteArgs& a, hipStream_t s);
 

@@ -42,6 +42,7 @@
 // writes its expert and weight at once; a rejected slot past the last
 // position is dropped at once (expert -1, weight 0); a token with slots still
 // asking is appended to the other list in the same order.
+#include "aux_reduce.h"
 #include "device_common.h"
 #include "kernels.h"
 
@@ -85,11 +86,22 @@ __device__ __forceinline__ void wave_rank_cols(const int (&ev)[KMAX], uint64_t l
   }
 }
 
+// Block 0 reroutes; block 1 reduces the router's aux partials (aux_reduce),
+// which the rerouting does not read, so the two run side by side.
 template <int KMAX, int SUB, int THREADS>
 __global__ __launch_bounds__(THREADS) void reroute_kernel(
     const int32_t* __restrict__ rank_rec, int T, int k, int E, int capacity,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int32_t* __restrict__ lists,
-    int32_t* __restrict__ rounds_out) {
+    int32_t* __restrict__ rounds_out, const double* __restrict__ part_psum,
+    const int32_t* __restrict__ part_top1, const double* __restrict__ part_z, int nblk,
+    int32_t* __restrict__ top1_count, float* __restrict__ prob_mean, float* __restrict__ aux,
+    float* __restrict__ z_loss) {
+  if (blockIdx.x == 1) {
+    __shared__ AuxLds<THREADS> ared;
+    aux_reduce<THREADS>(part_psum, part_top1, part_z, nblk, T, E, top1_count, prob_mean, aux,
+                        z_loss, ared);
+    return;
+  }
   constexpr int kWaves = THREADS / 64;
   constexpr int kGroups = SUB * kWaves;             // (sub-chunk, wave) groups, list order
   constexpr int kChunk = SUB * THREADS;
@@ -98,7 +110,7 @@ __global__ __launch_bounds__(THREADS) void reroute_kernel(
   __shared__ int room[kGroups][64];   // room expert x has for group g's requests
   __shared__ int wapp[kGroups];       // tokens appended per group in the chunk
   __shared__ int lst_t[2][kLdsList];  // list heads: token ids
-  __shared__ int lst_m[2][kLdsList];  // list heads: (cursor + 1) | asking slots << 8
+  __shared__ int lst_m[2][kLdsList];  // list heads: words
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   int left = capacity;                // wave 0, lane x: capacity expert x has left
@@ -107,7 +119,11 @@ __global__ __launch_bounds__(THREADS) void reroute_kernel(
   int rounds = 0;
   // Entry i of list l: LDS below kLdsList, workspace above (lists holds the
   // token ids of list 0, words of list 0, token ids of list 1, words of list 1).
+  // Word: bits 0..7 cursor + 1, bits 8..15 the slots asking this round.
   auto gidx = [&](int l, int field, int i) -> size_t { return (size_t)(2 * l + field) * T + i; };
+  auto rec = [&](int t, int pos, int field) -> int32_t {
+    return rank_rec[((size_t)t * 64 + pos) * 2 + field];
+  };
   for (;;) {
     ++rounds;
     const bool first = rounds == 1;
@@ -115,10 +131,10 @@ __global__ __launch_bounds__(THREADS) void reroute_kernel(
     // to ask (unreachable; bounds the loop).
     const bool last = rounds > E;
     int napp = 0;                     // entries appended so far this round (same in every wave)
-    for (int base = 0; base < n; base += kChunk) {
-      int tok[SUB], cpos[SUB], ask[SUB], ev[SUB][KMAX];
-      float wv[SUB][KMAX];
-      // Entries and their requests.
+    // Entries base + u * THREADS + tid: token, cursor, asking slots, and the
+    // experts and weights the slots ask for.
+    auto load_chunk = [&](int base, int (&tok)[SUB], int (&cpos)[SUB], int (&ask)[SUB],
+                          int (&ev)[SUB][KMAX], float (&wv)[SUB][KMAX]) {
 #pragma unroll
       for (int u = 0; u < SUB; ++u) {
         const int i = base + u * THREADS + tid;
@@ -147,16 +163,14 @@ __global__ __launch_bounds__(THREADS) void reroute_kernel(
             m = lists[gidx(cur, 1, i)];
           }
           cpos[u] = (m & 0xff) - 1;
-          ask[u] = m >> 8;
-          int before = 0;
+          ask[u] = (m >> 8) & 0xff;
+          int j = 0;
 #pragma unroll
           for (int s = 0; s < KMAX; ++s)
             if ((ask[u] >> s) & 1) {
-              const i32x2 r = *reinterpret_cast<const i32x2*>(
-                  rank_rec + ((size_t)tok[u] * 64 + cpos[u] + 1 + before) * 2);
-              ev[u][s] = r[0];
-              wv[u][s] = __int_as_float(r[1]);
-              ++before;
+              ev[u][s] = rec(tok[u], cpos[u] + 1 + j, 0);
+              wv[u][s] = __int_as_float(rec(tok[u], cpos[u] + 1 + j, 1));
+              ++j;
             }
         }
         // An id outside [0, E) (not produced by the router) is dropped.
@@ -169,6 +183,15 @@ __global__ __launch_bounds__(THREADS) void reroute_kernel(
             ev[u][s] = -1;
           }
       }
+    };
+    int tok[SUB], cpos[SUB], ask[SUB], ev[SUB][KMAX];
+    float wv[SUB][KMAX];
+    load_chunk(0, tok, cpos, ask, ev, wv);
+    for (int base = 0; base < n; base += kChunk) {
+      // The next chunk's loads go out before this chunk's decisions.
+      int ntok[SUB], ncpos[SUB], nask[SUB], nev[SUB][KMAX];
+      float nwv[SUB][KMAX];
+      load_chunk(base + kChunk, ntok, ncpos, nask, nev, nwv);
       // Ranks inside each wave and the per-group counts.
       int rk[SUB][KMAX];
 #pragma unroll
@@ -183,9 +206,12 @@ __global__ __launch_bounds__(THREADS) void reroute_kernel(
       }
       __syncthreads();
       if (wave == 0) {
+        // Group g holds entries base + 64 g .. base + 64 g + 63, so the groups
+        // with entries are a prefix.
+        const int ng = min(kGroups, (n - base + 63) >> 6);
         int r = left;
-#pragma unroll 8
-        for (int g = 0; g < kGroups; ++g) {
+#pragma unroll 4
+        for (int g = 0; g < ng; ++g) {
           const int c = wcnt[g][lane];
           room[g][lane] = r;
           r -= c;
@@ -257,6 +283,17 @@ __global__ __launch_bounds__(THREADS) void reroute_kernel(
         }
       }
       napp += total;
+#pragma unroll
+      for (int u = 0; u < SUB; ++u) {
+        tok[u] = ntok[u];
+        cpos[u] = ncpos[u];
+        ask[u] = nask[u];
+#pragma unroll
+        for (int s = 0; s < KMAX; ++s) {
+          ev[u][s] = nev[u][s];
+          wv[u][s] = nwv[u][s];
+        }
+      }
     }
     if (wave == 0) left = max(left, 0);
     __syncthreads();
@@ -270,14 +307,15 @@ __global__ __launch_bounds__(THREADS) void reroute_kernel(
 
 hipError_t launch_reroute(const RerouteArgs& a, hipStream_t s) {
 #define MOE_REROUTE(KMAX, SUB, THREADS)                                                      \
-  reroute_kernel<KMAX, SUB, THREADS><<<1, THREADS, 0, s>>>(a.rank, a.T, a.k, a.E, a.capacity,  \
-                                                          a.topk_idx, a.topk_w, a.lists, a.rounds)
+  reroute_kernel<KMAX, SUB, THREADS><<<2, THREADS, 0, s>>>(                                    \
+      a.rank, a.T, a.k, a.E, a.capacity, a.topk_idx, a.topk_w, a.lists, a.rounds, a.part_psum, \
+      a.part_top1, a.part_z, a.nblk, a.top1_count, a.prob_mean, a.aux, a.z_loss)
   // Entries per thread and chunk shrink as the slots per token grow, and past
   // two slots the block halves, so that the requests stay in registers.
   if (a.k == 1)
     MOE_REROUTE(1, 4, 1024);
   else if (a.k == 2)
-    MOE_REROUTE(2, 4, 1024);
+    MOE_REROUTE(2, 2, 1024);
   else if (a.k <= 4)
     MOE_REROUTE(4, 4, 512);
   else if (a.k <= 8)

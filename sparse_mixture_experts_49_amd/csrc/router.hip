@@ -15,6 +15,7 @@
 // squared log-sum-exp of the logits (same section: router z-loss).
 #include "device_common.h"
 #include "kernels.h"
+#include "aux_reduce.h"
 #include "perm_small.h"
 
 namespace moe {
@@ -25,12 +26,22 @@ constexpr int kRouterWaves = 8;     // the block's waves split d between them
 
 // LDS of a block of MT token tiles: the waves' partial logits, then each
 // token's probabilities, first choice and log-sum-exp for the aux and z-loss
-// sums, and (reroute policy) its ranking scores and weights.
+// sums, and (reroute policy) its ranking keys and weights.
+// A token's ranking as one unsigned compare: the score's bits mapped to an
+// integer of the same order (-0 taken as +0, as the float compare does) above,
+// 63 - e below, so the larger key is the higher score, or the lower index on
+// equal scores.  Valid keys are > 0.
+__device__ __forceinline__ uint64_t rank_key(float s, int e) {
+  const uint32_t b = __float_as_uint(s == 0.f ? 0.f : s);
+  const uint32_t ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((uint64_t)ord << 32) | (uint32_t)(63 - e);
+}
+
 template <int WAVES, int MT>
 struct RouterTileLds {
   float red[WAVES][kRouterTile * MT][65];
   float prob[kRouterTile * MT][64];
-  float rsc[kRouterTile * MT][64];
+  uint64_t rkey[kRouterTile * MT][64];
   float rwt[kRouterTile * MT][64];
   int top1[kRouterTile * MT];
   float lse[kRouterTile * MT];
@@ -38,7 +49,7 @@ struct RouterTileLds {
 
 // Tokens t0 .. t0 + 16*MT - 1 of the router: logits on MFMA (the WAVES waves
 // split d), softmax, top-k and the routing weights; fills sm.prob / top1 / lse
-// (and, with `rr`, sm.rsc / rwt).  Ends with a barrier.  Wave w accumulates
+// (and, with `rr`, sm.rkey / rwt).  Ends with a barrier.  Wave w accumulates
 // the k-chunks w, w+WAVES, ... of the d-long dot products; the partial logit
 // tiles are summed in wave order through LDS, so the result does not depend on
 // scheduling.
@@ -220,8 +231,8 @@ __device__ __forceinline__ void route_tile(
     if (rr) {                                        // inputs of the expert ranking
 #pragma unroll
       for (int j = 0; j < kMaxPer; ++j) {
-        const int e = q + 4 * j;                     // rows of 64, -inf past E
-        sm.rsc[tr][e] = e < E ? sc[j] : -INFINITY;
+        const int e = q + 4 * j;                     // rows of 64, key 0 past E
+        sm.rkey[tr][e] = e < E ? rank_key(sc[j], e) : 0ull;
         sm.rwt[tr][e] = renorm ? p[j] * winv : p[j];
       }
     }
@@ -280,14 +291,10 @@ __global__ __launch_bounds__(kRouterWaves * 64) void router_kernel(
     for (int idx = threadIdx.x; idx < kTok * 64; idx += kRouterWaves * 64) {
       const int tr = idx >> 6, e = idx & 63, t = t0 + tr;
       if (e >= E || t >= T_) continue;
-      const float s = sm.rsc[tr][e];
+      const uint64_t key = sm.rkey[tr][e];
       int pos = 0;
 #pragma unroll
-      for (int j = 0; j < 64; j += 4) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(&sm.rsc[tr][j]);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) pos += (int)(v[u] > s) + (int)((v[u] == s) & (j + u < e));
-      }
+      for (int j = 0; j < 64; ++j) pos += (int)(sm.rkey[tr][j] > key);
       typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
       *reinterpret_cast<i32x2*>(rr_rank + ((size_t)t * 64 + pos) * 2) =
           i32x2{e, (int32_t)__float_as_uint(sm.rwt[tr][e])};
@@ -295,9 +302,8 @@ __global__ __launch_bounds__(kRouterWaves * 64) void router_kernel(
   }
 }
 
-// Fixed-order reduction of the router partials: f, P and aux (web page
-// "Mixture of Experts: Scaling Parameters Without Scaling Compute", section
-// "The central problem: load balancing").
+// The router partials reduced in a fixed order (aux_reduce), then the small
+// layers' dispatch layout.
 __global__ __launch_bounds__(kAuxThreads) void aux_finalize_kernel(
     const double* __restrict__ part_psum, const int32_t* __restrict__ part_top1,
     const double* __restrict__ part_z, int nblk, int T_, int E, int32_t* __restrict__ top1_count,
@@ -305,62 +311,11 @@ __global__ __launch_bounds__(kAuxThreads) void aux_finalize_kernel(
     int32_t* __restrict__ rounds_zero, const int32_t* __restrict__ topk_idx, int k, bool perm,
     int capacity, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ dest, int32_t* __restrict__ src) {
-  // The partials are [nblk][E] laid out flat.  Thread t < stride (a multiple of
-  // E) sums entries t, t + stride, ... (all of expert t % E, coalesced across
-  // the block); expert e's per-thread sums are then added in thread order.
-  // The grouping depends only on (nblk, E), so the result is deterministic.
-  __shared__ double ps[kAuxThreads];
-  __shared__ long long pc[kAuxThreads];
-  __shared__ double fP[64];
-  __shared__ double wz[kAuxThreads / 64];
+  __shared__ AuxLds<kAuxThreads> ared;
   __shared__ PermSmallLds psm;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int stride = (kAuxThreads / E) * E;
-  const long n = (long)nblk * E;
-  double sum = 0.0;
-  long long cnt = 0;
-  if (t < stride) {
-    // Unrolled so that several loads are in flight; the sum still runs in i order.
-#pragma unroll 8
-    for (long i = t; i < n; i += stride) {
-      sum += part_psum[i];
-      cnt += part_top1[i];
-    }
-  }
-  ps[t] = sum;
-  pc[t] = cnt;
-  double zs = 0.0;                                   // z-loss: block partials t, t + threads, ...
-#pragma unroll 4
-  for (int b = t; b < nblk; b += kAuxThreads) zs += part_z[b];
-  // Fixed shuffle tree per wave, then the waves in order.
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) zs += __shfl_down(zs, off);
-  if (lane == 0) wz[wave] = zs;
-  __syncthreads();
-  if (t < E) {
-    double S = 0.0;
-    long long C = 0;
-    for (int u = t; u < stride; u += E) {
-      S += ps[u];
-      C += pc[u];
-    }
-    const double P = S / (double)T_, f = (double)C / (double)T_;
-    fP[t] = f * P;
-    if (top1_count) top1_count[t] = (int32_t)C;
-    if (prob_mean) prob_mean[t] = (float)P;
-  }
-  __syncthreads();
-  if (t == 0 && aux) {
-    double acc = 0.0;
-    for (int i = 0; i < E; ++i) acc += fP[i];
-    *aux = (float)((double)E * acc);
-  }
-  if (t == 128 && rounds_zero) *rounds_zero = 0;
-  if (t == 64 && z_loss) {
-    double zt = 0.0;
-    for (int w = 0; w < kAuxThreads / 64; ++w) zt += wz[w];
-    *z_loss = (float)(zt / (double)T_);
-  }
+  aux_reduce<kAuxThreads>(part_psum, part_top1, part_z, nblk, T_, E, top1_count, prob_mean, aux,
+                          z_loss, ared);
+  if (threadIdx.x == 128 && rounds_zero) *rounds_zero = 0;
   // Small layers: the dispatch layout too, saving the permute's own launch.
   if (perm) perm_small_layout(topk_idx, T_, k, E, capacity, true, counts, offsets, dest, src, psm);
 }
@@ -372,11 +327,16 @@ bool router_can_permute(int assignments) { return assignments <= kPermChunk; }
 // serves 32 tokens, halving the re-reads of W_r.
 static int router_tiles(int T, int E) { return (E > 16 && T >= 256 * 2 * kRouterTile) ? 2 : 1; }
 
+int router_launch_blocks(int T, int E) {
+  const int mt = router_tiles(T, E);
+  return (T + kRouterTile * mt - 1) / (kRouterTile * mt);
+}
+
 template <typename T>
 static hipError_t launch_router_t(const RouterArgs& a, hipStream_t s) {
   const int nt = (a.E + 15) / 16;
   const int mt = router_tiles(a.T, a.E);
-  const int nblk = (a.T + kRouterTile * mt - 1) / (kRouterTile * mt);
+  const int nblk = router_launch_blocks(a.T, a.E);
   const T* x = static_cast<const T*>(a.x);
   const T* wr = static_cast<const T*>(a.w_router);
 #define MOE_ROUTER_CASE(NT, MT)                                                               \
@@ -398,6 +358,7 @@ static hipError_t launch_router_t(const RouterArgs& a, hipStream_t s) {
 #undef MOE_ROUTER_CASE
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
+  if (a.rr_rank) return hipSuccess;                   // reduced by the reroute launch
   if (a.perm && !router_can_permute(a.T * a.k)) return hipErrorInvalidValue;
   aux_finalize_kernel<<<1, kAuxThreads, 0, s>>>(a.part_psum, a.part_top1, a.part_z, nblk, a.T, a.E,
                                                 a.top1_count, a.prob_mean, a.aux, a.z_loss,
