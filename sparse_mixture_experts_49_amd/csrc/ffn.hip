@@ -160,13 +160,20 @@ constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 0xF) | ((vm >> 4) << 14) |
 // past the last full group are dealt round-robin over the XCDs.
 //
 // Tail.  An XCD's list is cut into rounds of kCusPerXcd tiles.  If the last,
-// partial round has at most half a round of tiles, each of them is split into
+// partial round has at most half a round of tiles and the k range has at
+// least kSplitMinSteps steps, each of them is split into
 // S = min(kMaxSplit, kCusPerXcd / tail) parts of its k range, run by S blocks
 // that store fp32 partial tiles into workspace slot x * kCusPerXcd + j; the
 // reduce kernel then sums the parts in order.  Otherwise the last round's
-// tiles stay whole.
+// tiles stay whole.  The split saves a share of one tile's time, which grows
+// with k, and costs the partial tiles' round trip, which does not: measured
+// on MI355X it pays for k = 8192 and 14336 (second products of the Switch-style
+// and prefill layers, 7% and 2% of the product) and loses for k = 1024 and
+// 2048 (first products of the mid-size, fine-grained and Switch-style layers,
+// 1-15%).
 constexpr int kCusPerXcd = 32;
 constexpr int kMaxSplit = 8;
+constexpr int kSplitMinSteps = 64;   // k >= 4096
 constexpr int kPartialSlots = kXcds * kCusPerXcd;
 constexpr size_t kPartialTileFloats = (size_t)kTBM * 256;
 
@@ -189,7 +196,9 @@ __device__ __forceinline__ bool tile_job(const int32_t* __restrict__ offsets, in
   const int left = lm * ntn;                         // leftover tiles, dealt round-robin
   const int cnt = full + (left > x ? (left - x + kXcds - 1) / kXcds : 0);
   const int rounds = cnt / kCusPerXcd, tail = cnt - rounds * kCusPerXcd;
-  const int S = (tail > 0 && 2 * tail <= kCusPerXcd) ? min(min(kMaxSplit, nk), kCusPerXcd / tail) : 1;
+  const int S = (tail > 0 && 2 * tail <= kCusPerXcd && nk >= kSplitMinSteps)
+                    ? min(min(kMaxSplit, nk), kCusPerXcd / tail)
+                    : 1;
   int entry = i;
   job.part = 0;
   job.parts = 1;

@@ -78,6 +78,16 @@ SMALL = {
                                      "bf16", router_bias=True),
     "one_expert_top2_bf16": Workload("one_expert_top2_bf16", 1100, 256, 384, 8, 2, True, 0, False,
                                      "bf16", router_bias=True),
+    # k ranges of 4096 (d_model for the first product, d_ff for the second): the
+    # tiled kernel's last round is split along k and finished by its reduction, for
+    # bf16 h (top-2, 256-row tiles) and split h (top-1 without renormalisation,
+    # 128-row tiles), first and second product
+    "long_d_bf16": Workload("long_d_bf16", 512, 4096, 512, 4, 2, True, 0, True, "bf16"),
+    "long_f_bf16": Workload("long_f_bf16", 512, 256, 4096, 4, 2, True, 0, True, "bf16"),
+    "long_d_top1_bf16": Workload("long_d_top1_bf16", 600, 4096, 512, 8, 1, False, 0, True,
+                                 "bf16"),
+    "long_f_top1_bf16": Workload("long_f_top1_bf16", 600, 512, 4096, 8, 1, False, 0, True,
+                                 "bf16"),
     # the mid-size layer's shapes (4096 tokens, 16 experts) with a selection bias
     "mid_select_bias_bf16": Workload("mid_select_bias_bf16", 4096, 1024, 4096, 16, 2, True, 0, True,
                                      "bf16", selection_bias=True),
