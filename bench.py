@@ -332,7 +332,7 @@ def _entry_of(kernel_name: str):
     if base.startswith("ffn_"):
         up = re.search(r"\b(true|false)\b", m.group(2)).group(1) == "true"
         return "moe_ffn_up" if up else "moe_ffn_down"
-    if base.startswith(("router", "aux")):
+    if base.startswith(("router", "aux", "reroute")):
         return "moe_route"
     if base.startswith("perm"):
         return "moe_permute"
