@@ -51,11 +51,20 @@ __device__ __forceinline__ bool find_mtile(const int32_t* __restrict__ offsets, 
   return false;
 }
 
-// Row of A holding dispatched row r: r itself, or -- when the first product
-// reads the tokens straight from x -- the token of assignment gather[r]
-// (gather = the dispatch's src array, gather_k = top_k).
-__device__ __forceinline__ int a_row(const int32_t* __restrict__ gather, int gather_k, int r) {
-  return gather ? gather[r] / gather_k : r;
+// Rows of A holding dispatched rows r[0..n): r itself, or -- when the first
+// product reads the tokens straight from x -- the token of assignment
+// gather[r] (gather = the dispatch's src array, gather_k = top_k).  Every
+// index load is issued before any is used (one wait, not one per row; the
+// null test is uniform), and the division is unsigned (indices are >= 0).
+template <int n>
+__device__ __forceinline__ void a_rows(const int32_t* __restrict__ gather, int gather_k, int (&r)[n]) {
+  if (!gather) return;
+  int32_t g[n];
+#pragma unroll
+  for (int i = 0; i < n; ++i) g[i] = gather[r[i]];
+  const uint32_t k = (uint32_t)gather_k;
+#pragma unroll
+  for (int i = 0; i < n; ++i) r[i] = (int)((uint32_t)g[i] / k);
 }
 
 template <typename T, bool UP>
@@ -304,12 +313,24 @@ __global__ __launch_bounds__(256, OCC) void ffn_tiled_kernel(
   uint32_t a_off[kAInst];
   uint32_t b_off[kBInst];
   const uint16_t* Wexp = W + (size_t)e * N * K;
+  if constexpr (UP) {                                 // only the first product gathers
+    int arow[kAInst];
 #pragma unroll
-  for (int i = 0; i < kAInst; ++i) {
-    const int lrow = (i * NW + wave) * 8 + (lane >> 3);
-    const int row = lrow % BM;
-    const int c = (lane & 7) ^ ((lrow >> 1) & 7);
-    a_off[i] = (uint32_t)(((size_t)a_row(gather, gather_k, min(r0 + row, r1 - 1)) * K + c * 8) * 2);
+    for (int i = 0; i < kAInst; ++i) arow[i] = min(r0 + ((i * NW + wave) * 8 + (lane >> 3)) % BM, r1 - 1);
+    a_rows<kAInst>(gather, gather_k, arow);
+#pragma unroll
+    for (int i = 0; i < kAInst; ++i) {
+      const int lrow = (i * NW + wave) * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ ((lrow >> 1) & 7);
+      a_off[i] = (uint32_t)(((size_t)arow[i] * K + c * 8) * 2);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kAInst; ++i) {
+      const int lrow = (i * NW + wave) * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ ((lrow >> 1) & 7);
+      a_off[i] = (uint32_t)(((size_t)min(r0 + lrow % BM, r1 - 1) * K + c * 8) * 2);
+    }
   }
 #pragma unroll
   for (int i = 0; i < kBInst; ++i) {
@@ -705,6 +726,11 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(
   // (L % kPieces) ^ swz(row).  Rows past the block's last are clamped (their
   // data is never used).
   const T* a_src[kAInst];
+  int arow[kAInst];
+#pragma unroll
+  for (int i = 0; i < kAInst; ++i)
+    arow[i] = min(r0 + (((i * 4 + wave) * 1024 + lane * 16) % kPlaneBytes) / kRowBytes, r1 - 1);
+  if constexpr (UP) a_rows<kAInst>(gather, gather_k, arow);   // only the first product gathers
 #pragma unroll
   for (int i = 0; i < kAInst; ++i) {
     const int byte = (i * 4 + wave) * 1024 + lane * 16;
@@ -712,7 +738,7 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(
     const int row = (byte % kPlaneBytes) / kRowBytes;
     const int logical = ((byte % kRowBytes) / 16) ^ swz(row);
     const T* base = (kTwoA && plane) ? A_lo : A;
-    a_src[i] = base + (size_t)a_row(gather, gather_k, min(r0 + row, r1 - 1)) * K + logical * kPerVec;
+    a_src[i] = base + (size_t)arow[i] * K + logical * kPerVec;
   }
   const T* w_src[NWN];
   const T* Wexp = W + (size_t)e * N * K;
