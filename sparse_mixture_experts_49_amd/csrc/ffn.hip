@@ -30,25 +30,45 @@
 
 namespace moe {
 
-// Find the expert owning global m-tile `mt` when every expert's rows are cut
-// into ceil(count/bm) tiles laid end to end.  Returns false past the last tile.
-__device__ __forceinline__ bool find_mtile(const int32_t* __restrict__ offsets, int E, int bm,
-                                           int mt, int& e_out, int& r0, int& r1) {
-  int cum = 0;
-  int lo = offsets[0];
-  for (int e = 0; e < E; ++e) {
-    const int hi = offsets[e + 1];
-    const int nt = (hi - lo + bm - 1) / bm;
-    if (mt < cum + nt) {
-      e_out = e;
-      r0 = lo + (mt - cum) * bm;
-      r1 = min(hi, r0 + bm);
-      return true;
-    }
-    cum += nt;
-    lo = hi;
+// Every expert's rows cut into ceil(count/BM) m-tiles laid end to end, one
+// expert per lane (E <= 64): lane e holds its rows [lo, hi), its m-tile count
+// and the index of its first m-tile; `total` (uniform) counts them all.  One
+// vector load per lane and a wave-wide prefix sum, not a loop of dependent
+// loads over the experts.  Every lane of the wave must take part.
+struct MTiles {
+  int lo, hi, nt, first;   // this lane's expert (0 past E)
+  int total;               // m-tiles over all experts
+};
+
+template <int BM>
+__device__ __forceinline__ MTiles mtiles(const int32_t* __restrict__ offsets, int E) {
+  const int lane = __lane_id();
+  MTiles m;
+  m.lo = lane < E ? offsets[lane] : 0;
+  m.hi = lane < E ? offsets[lane + 1] : 0;
+  m.nt = (m.hi - m.lo + BM - 1) / BM;
+  int incl = m.nt;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
   }
-  return false;
+  m.first = incl - m.nt;
+  m.total = __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
+  return m;
+}
+
+// The expert owning global m-tile `mt` (uniform) and the tile's rows: the lane
+// whose range of m-tiles holds it.  Returns false past the last tile.
+template <int BM>
+__device__ __forceinline__ bool find_mtile(const MTiles& m, int mt, int& e_out, int& r0, int& r1) {
+  const uint64_t own = __ballot(mt >= m.first && mt < m.first + m.nt);
+  if (!own) return false;
+  const int e = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)own) - 1);
+  e_out = e;
+  r0 = __builtin_amdgcn_readfirstlane(__shfl(m.lo + (mt - m.first) * BM, e));
+  r1 = min(__builtin_amdgcn_readfirstlane(__shfl(m.hi, e)), r0 + BM);
+  return true;
 }
 
 // Rows of A holding dispatched rows r[0..n): r itself, or -- when the first
@@ -192,11 +212,7 @@ struct TileJob {
   int slot;        // partial-tile slot when parts > 1
 };
 
-template <int BM>
-__device__ __forceinline__ bool tile_job(const int32_t* __restrict__ offsets, int E, int ntn, int nk,
-                                         int b, TileJob& job) {
-  int total_mt = 0;
-  for (int e = 0; e < E; ++e) total_mt += (offsets[e + 1] - offsets[e] + BM - 1) / BM;
+__device__ __forceinline__ bool tile_job(int total_mt, int ntn, int nk, int b, TileJob& job) {
   constexpr int kGroupM = kXcds * kBandM;
   const int x = b % kXcds, i = b / kXcds;
   const int G = total_mt / kGroupM;
@@ -234,10 +250,7 @@ __device__ __forceinline__ bool tile_job(const int32_t* __restrict__ offsets, in
 }
 
 // First entry of XCD x's tail (its last, partial round) in tile_job's order.
-template <int BM>
-__device__ __forceinline__ int tail_start(const int32_t* __restrict__ offsets, int E, int ntn, int x) {
-  int total_mt = 0;
-  for (int e = 0; e < E; ++e) total_mt += (offsets[e + 1] - offsets[e] + BM - 1) / BM;
+__device__ __forceinline__ int tail_start(int total_mt, int ntn, int x) {
   constexpr int kGroupM = kXcds * kBandM;
   const int G = total_mt / kGroupM;
   const int left = (total_mt - G * kGroupM) * ntn;
@@ -292,10 +305,11 @@ __global__ __launch_bounds__(256, OCC) void ffn_tiled_kernel(
   // columns past N load the last W row and are not stored)
   const int ntn = (N + BN - 1) / BN;
   TileJob job;
-  if (!tile_job<BM>(offsets, E, ntn, K / kTBK, blockIdx.x, job)) return;
+  const MTiles mts = mtiles<BM>(offsets, E);
+  if (!tile_job(mts.total, ntn, K / kTBK, blockIdx.x, job)) return;
   const int mt = job.mt, nt = job.nt;
   int e, r0, r1;
-  if (!find_mtile(offsets, E, BM, mt, e, r0, r1)) return;
+  if (!find_mtile<BM>(mts, mt, e, r0, r1)) return;
   const int n0 = nt * BN;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -598,11 +612,12 @@ __global__ __launch_bounds__(256) void ffn_tile_reduce(
     size_t out_plane, int E, int N, int K, const float* __restrict__ partial) {
   const int ntn = (N + BN - 1) / BN, x = blockIdx.x % kXcds, j = blockIdx.x / kXcds;
   TileJob job;
-  if (!tile_job<BM>(offsets, E, ntn, K / kTBK, x + kXcds * (tail_start<BM>(offsets, E, ntn, x) + j), job) ||
+  const MTiles mts = mtiles<BM>(offsets, E);
+  if (!tile_job(mts.total, ntn, K / kTBK, x + kXcds * (tail_start(mts.total, ntn, x) + j), job) ||
       job.parts == 1)
     return;
   int e, r0, r1;
-  if (!find_mtile(offsets, E, BM, job.mt, e, r0, r1)) return;
+  if (!find_mtile<BM>(mts, job.mt, e, r0, r1)) return;
   const int n0 = job.nt * BN;
   const int ra = job.part * BM / job.parts;
   const int rb = min(r1 - r0, (job.part + 1) * BM / job.parts);
