@@ -26,7 +26,7 @@ struct RouterArgs {
                            // {expert of rank p, bits of the weight it would get} for p < E;
                            // the partials are then reduced by launch_reroute
   int32_t* rounds_zero;    // optional: set to 0 (no reroute runs)
-  // Optional dispatch layout of a small layer (T*k <= 1024, drop policy), computed by
+  // Optional dispatch layout of a small layer (T*k <= 8192, drop policy), computed by
   // the aux reduction block right after the router: counts, offsets, dest and src as
   // the permute writes them, with `capacity` (0 = none).
   bool perm;

@@ -1,46 +1,56 @@
-// The dispatch layout of at most kPermChunk assignments, computed by one
-// block (web page "Mixture of Experts: Scaling Parameters Without Scaling
-// Compute", section "The MoE layer": rows grouped by expert, in token order;
-// section "The central problem: load balancing": expert capacity).  Shared by
-// the single-launch permute and by the aux-loss reduction, which runs it for
-// the whole layer when the layer is small.
+// The dispatch layout of a layer small enough for one block (web page
+// "Mixture of Experts: Scaling Parameters Without Scaling Compute", section
+// "The MoE layer": rows grouped by expert, in token order; section "The central
+// problem: load balancing": expert capacity).  Used by the single-launch
+// permute (up to kPermChunk assignments) and by the aux-loss reduction block,
+// which runs it for the whole layer (up to kPermWide assignments) so that
+// moe_forward needs no permute launch.
 #pragma once
 
 #include "device_common.h"
 
 namespace moe {
 
-constexpr int kPermChunk = 1024;   // assignments per block (4 waves x 4 batches x 64)
+constexpr int kPermChunk = 1024;   // assignments per block of the multi-block permute
+constexpr int kPermWide = 8192;    // assignments the aux block lays out (16 waves x 8 batches x 64)
 
-struct PermSmallLds {
-  int wcount[4][64];
+template <int WAVES, int BATCHES, bool KEEP>
+struct PermLayoutLds {
+  int pre[WAVES][64];     // wave w's count of expert e, then the count in waves before w
   int s_off[65];
-  int s_dest[kPermChunk];
+  int s_dest[KEEP ? WAVES * BATCHES * 64 : 1];
 };
 
-// Called by every thread of the block (it holds barriers); threads 0..255 do
-// the work.  Wave w ranks assignments w*256 .. +255 in four batches of 64
-// (lane e of the wave keeps its running count of expert e); the per-wave
-// counts give each expert's total, the capacity clamp (capacity > 0) and the
-// offsets; then every assignment gets its row (-1 if dropped or if its expert
-// is outside [0, E)), kept in sm.s_dest.  With `write`, counts, offsets, dest
-// and src are written to global memory too.
-__device__ __forceinline__ void perm_small_layout(const int32_t* __restrict__ topk_idx, int T,
-                                                  int k, int E, int capacity, bool write,
-                                                  int32_t* __restrict__ counts,
-                                                  int32_t* __restrict__ offsets,
-                                                  int32_t* __restrict__ dest,
-                                                  int32_t* __restrict__ src, PermSmallLds& sm) {
-  const bool worker = threadIdx.x < 256;
+// Called by every thread of the block (it holds barriers); the first WAVES
+// waves do the work.  Wave w ranks assignments w*BATCHES*64 .. in BATCHES
+// batches of 64 (lane e of the wave keeps its running count of expert e).
+// Wave 0 then takes one expert per lane: the waves' counts give the number of
+// each expert's requests in the waves before each wave, its total, the
+// capacity clamp (capacity > 0) and, by a wave-wide scan, the offsets.  Every
+// assignment then gets its row (-1 if dropped or if its expert is outside
+// [0, E)), kept in sm.s_dest with KEEP.  With `write`, counts, offsets, dest and
+// src are written to global memory too.
+template <int WAVES, int BATCHES, bool KEEP>
+__device__ __forceinline__ void perm_layout(const int32_t* __restrict__ topk_idx, int T, int k,
+                                            int E, int capacity, bool write,
+                                            int32_t* __restrict__ counts,
+                                            int32_t* __restrict__ offsets,
+                                            int32_t* __restrict__ dest, int32_t* __restrict__ src,
+                                            PermLayoutLds<WAVES, BATCHES, KEEP>& sm) {
+  const bool worker = threadIdx.x < WAVES * 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int A = T * k;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  int ex[4], rk[4], run = 0;
+  int ex[BATCHES], rk[BATCHES], run = 0;
   if (worker) {
 #pragma unroll
-    for (int bt = 0; bt < 4; ++bt) {
-      const int a = wave * 256 + bt * 64 + lane;
-      int e = (a < A) ? topk_idx[a] : -1;
+    for (int bt = 0; bt < BATCHES; ++bt) {         // every load in flight before any is used
+      const int a = (wave * BATCHES + bt) * 64 + lane;
+      ex[bt] = (a < A) ? topk_idx[a] : -1;
+    }
+#pragma unroll
+    for (int bt = 0; bt < BATCHES; ++bt) {
+      int e = ex[bt];
       if (e < 0 || e >= E) e = -1;
       int cnt;
       const int r = wave_rank(e, lt_mask, cnt);
@@ -48,38 +58,50 @@ __device__ __forceinline__ void perm_small_layout(const int32_t* __restrict__ to
       rk[bt] = __shfl(run, e >= 0 ? e : 0) + r;   // this wave's earlier batches + rank in this one
       run += wave_count_of_lane(e, lane);         // lane x: requests for expert x in this batch
     }
-    sm.wcount[wave][lane] = run;
+    sm.pre[wave][lane] = run;
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int acc = 0;
-    for (int e = 0; e < E; ++e) {
-      const int tot = sm.wcount[0][e] + sm.wcount[1][e] + sm.wcount[2][e] + sm.wcount[3][e];
-      const int kept = capacity > 0 ? min(tot, capacity) : tot;
-      sm.s_off[e] = acc;
+  if (threadIdx.x < 64) {
+    const int e = threadIdx.x;
+    int tot = 0;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) {
+      const int c = sm.pre[w][e];
+      sm.pre[w][e] = tot;
+      tot += c;
+    }
+    const int kept = e < E ? (capacity > 0 ? min(tot, capacity) : tot) : 0;
+    int incl = kept;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int o = __shfl_up(incl, off);
+      if (lane >= off) incl += o;
+    }
+    if (e < E) {
+      sm.s_off[e] = incl - kept;
       if (write) {
-        offsets[e] = acc;
+        offsets[e] = incl - kept;
         counts[e] = kept;
       }
-      acc += kept;
     }
-    sm.s_off[E] = acc;
-    if (write) offsets[E] = acc;
+    if (e == E - 1) {
+      sm.s_off[E] = incl;
+      if (write) offsets[E] = incl;
+    }
   }
   __syncthreads();
   if (worker) {
 #pragma unroll
-    for (int bt = 0; bt < 4; ++bt) {
-      const int a = wave * 256 + bt * 64 + lane;
+    for (int bt = 0; bt < BATCHES; ++bt) {
+      const int a = (wave * BATCHES + bt) * 64 + lane;
       if (a >= A) continue;
       const int e = ex[bt];
       int row = -1;
       if (e >= 0) {
-        int r = rk[bt];
-        for (int w = 0; w < wave; ++w) r += sm.wcount[w][e];
+        const int r = rk[bt] + sm.pre[wave][e];
         if (capacity <= 0 || r < capacity) row = sm.s_off[e] + r;
       }
-      sm.s_dest[a] = row;
+      if constexpr (KEEP) sm.s_dest[a] = row;
       if (write) {
         dest[a] = row;
         if (row >= 0) src[row] = a;

@@ -165,15 +165,16 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(const uint8_t* __rest
 }
 
 // All four steps for A <= kPermChunk assignments: every block builds the
-// layout in LDS (perm_small_layout), block 0 writes it out, and block b
-// scatters tokens 4b .. 4b+3, one wave each.
+// layout in LDS (perm_layout), block 0 writes it out, and block b scatters
+// tokens 4b .. 4b+3, one wave each.
 __global__ __launch_bounds__(256) void perm_small_kernel(
     const int32_t* __restrict__ topk_idx, int T, int k, int E, int capacity,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ dest,
     int32_t* __restrict__ src, const uint8_t* __restrict__ x, int row_bytes,
     uint8_t* __restrict__ x_perm) {
-  __shared__ PermSmallLds sm;
-  perm_small_layout(topk_idx, T, k, E, capacity, blockIdx.x == 0, counts, offsets, dest, src, sm);
+  __shared__ PermLayoutLds<4, kPermChunk / 256, true> sm;
+  perm_layout<4, kPermChunk / 256, true>(topk_idx, T, k, E, capacity, blockIdx.x == 0, counts,
+                                         offsets, dest, src, sm);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + wave;
   if (t >= T || !x_perm) return;

@@ -312,15 +312,17 @@ __global__ __launch_bounds__(kAuxThreads) void aux_finalize_kernel(
     int capacity, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ dest, int32_t* __restrict__ src) {
   __shared__ AuxLds<kAuxThreads> ared;
-  __shared__ PermSmallLds psm;
+  __shared__ PermLayoutLds<kAuxThreads / 64, kPermWide / kAuxThreads, false> psm;
   aux_reduce<kAuxThreads>(part_psum, part_top1, part_z, nblk, T_, E, top1_count, prob_mean, aux,
                           z_loss, ared);
   if (threadIdx.x == 128 && rounds_zero) *rounds_zero = 0;
   // Small layers: the dispatch layout too, saving the permute's own launch.
-  if (perm) perm_small_layout(topk_idx, T_, k, E, capacity, true, counts, offsets, dest, src, psm);
+  if (perm)
+    perm_layout<kAuxThreads / 64, kPermWide / kAuxThreads, false>(topk_idx, T_, k, E, capacity, true,
+                                                                  counts, offsets, dest, src, psm);
 }
 
-bool router_can_permute(int assignments) { return assignments <= kPermChunk; }
+bool router_can_permute(int assignments) { return assignments <= kPermWide; }
 
 // Two token tiles per block when the expert rows are many (E > 16) and the
 // tokens fill the chip with one block per CU: each W_r fragment loaded then
