@@ -495,13 +495,25 @@ __global__ __launch_bounds__(256, OCC) void ffn_tiled_kernel(
     // the other modes stage fp32 (kOutGeluSplit converts to hi + lo on the way
     // out, the lo plane out_plane elements after the hi plane).
     const uint16_t* bexp = bias ? bias + (size_t)e * N : nullptr;
+    // The lane's bias words (four bf16 columns per (jn, g), the same in every
+    // pass): loaded once per tile, all in flight before any is used -- one at a
+    // time they cost a round trip each.
+    uint2 braw[kNT][4];
+    auto load_bias = [&](bool with_bias) {
+#pragma unroll
+      for (int jn = 0; jn < kNT; ++jn)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int col = n0 + wn * kWN + jn * 32 + 8 * g + 4 * fc;
+          braw[jn][g] = (with_bias && col < N) ? *reinterpret_cast<const uint2*>(bexp + col)
+                                               : make_uint2(0u, 0u);
+        }
+    };
     auto bias4 = [&](int jn, int g, float (&bv)[4]) {
-      const int col = n0 + wn * kWN + jn * 32 + 8 * g + 4 * fc;
-      const uint2 braw = col < N ? *reinterpret_cast<const uint2*>(bexp + col) : make_uint2(0u, 0u);
-      bv[0] = __uint_as_float(braw.x << 16);
-      bv[1] = __uint_as_float(braw.x & 0xffff0000u);
-      bv[2] = __uint_as_float(braw.y << 16);
-      bv[3] = __uint_as_float(braw.y & 0xffff0000u);
+      bv[0] = __uint_as_float(braw[jn][g].x << 16);
+      bv[1] = __uint_as_float(braw[jn][g].x & 0xffff0000u);
+      bv[2] = __uint_as_float(braw[jn][g].y << 16);
+      bv[3] = __uint_as_float(braw[jn][g].y & 0xffff0000u);
     };
     auto store_tile = [&](auto mode_tag, uint8_t* dst, size_t row_stride, int row_lim, int col_lim,
                           bool with_bias) {
@@ -513,6 +525,7 @@ __global__ __launch_bounds__(256, OCC) void ffn_tiled_kernel(
       constexpr int kPasses = kWM / kPassRows;
       constexpr int kRowsPerInst = 64 / kChunks;
       uint8_t* my = lds + wave * (kPassRows * kRowB);
+      if (with_bias) load_bias(true);
 #pragma unroll
       for (int pass = 0; pass < kPasses; ++pass) {
         if (pass * kPassRows >= kMA * 32) continue;    // rows past the active subtiles
