@@ -21,9 +21,24 @@ struct PermLayoutLds {
   int s_dest[KEEP ? WAVES * BATCHES * 64 : 1];
 };
 
-// Called by every thread of the block (it holds barriers); the first WAVES
-// waves do the work.  Wave w ranks assignments w*BATCHES*64 .. in BATCHES
-// batches of 64 (lane e of the wave keeps its running count of expert e).
+// The expert of each assignment the thread lays out (-1 past the end), loaded
+// before any is used; a caller may issue these loads early, ahead of other work,
+// and pass them to perm_layout.
+template <int WAVES, int BATCHES>
+__device__ __forceinline__ void perm_load(const int32_t* __restrict__ topk_idx, int A,
+                                          int (&ex)[BATCHES]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int bt = 0; bt < BATCHES; ++bt) {
+    const int a = (wave * BATCHES + bt) * 64 + lane;
+    ex[bt] = (threadIdx.x < WAVES * 64 && a < A) ? topk_idx[a] : -1;
+  }
+}
+
+// Called by every thread of the block (it holds barriers), with ex from
+// perm_load; the first WAVES waves do the work.  Wave w ranks assignments
+// w*BATCHES*64 .. in BATCHES batches of 64 (lane e of the wave keeps its running
+// count of expert e).
 // Wave 0 then takes one expert per lane: the waves' counts give the number of
 // each expert's requests in the waves before each wave, its total, the
 // capacity clamp (capacity > 0) and, by a wave-wide scan, the offsets.  Every
@@ -31,7 +46,7 @@ struct PermLayoutLds {
 // [0, E)), kept in sm.s_dest with KEEP.  With `write`, counts, offsets, dest and
 // src are written to global memory too.
 template <int WAVES, int BATCHES, bool KEEP>
-__device__ __forceinline__ void perm_layout(const int32_t* __restrict__ topk_idx, int T, int k,
+__device__ __forceinline__ void perm_layout(int (&ex)[BATCHES], int T, int k,
                                             int E, int capacity, bool write,
                                             int32_t* __restrict__ counts,
                                             int32_t* __restrict__ offsets,
@@ -41,20 +56,17 @@ __device__ __forceinline__ void perm_layout(const int32_t* __restrict__ topk_idx
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int A = T * k;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  int ex[BATCHES], rk[BATCHES], run = 0;
+  int rk[BATCHES], run = 0;
   if (worker) {
-#pragma unroll
-    for (int bt = 0; bt < BATCHES; ++bt) {         // every load in flight before any is used
-      const int a = (wave * BATCHES + bt) * 64 + lane;
-      ex[bt] = (a < A) ? topk_idx[a] : -1;
-    }
 #pragma unroll
     for (int bt = 0; bt < BATCHES; ++bt) {
       int e = ex[bt];
       if (e < 0 || e >= E) e = -1;
+      ex[bt] = e;
+      rk[bt] = 0;
+      if (__ballot(e >= 0) == 0) continue;       // a batch with nothing to lay out (wave-uniform)
       int cnt;
       const int r = wave_rank(e, lt_mask, cnt);
-      ex[bt] = e;
       rk[bt] = __shfl(run, e >= 0 ? e : 0) + r;   // this wave's earlier batches + rank in this one
       run += wave_count_of_lane(e, lane);         // lane x: requests for expert x in this batch
     }

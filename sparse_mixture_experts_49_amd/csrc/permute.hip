@@ -173,8 +173,10 @@ __global__ __launch_bounds__(256) void perm_small_kernel(
     int32_t* __restrict__ src, const uint8_t* __restrict__ x, int row_bytes,
     uint8_t* __restrict__ x_perm) {
   __shared__ PermLayoutLds<4, kPermChunk / 256, true> sm;
-  perm_layout<4, kPermChunk / 256, true>(topk_idx, T, k, E, capacity, blockIdx.x == 0, counts,
-                                         offsets, dest, src, sm);
+  int ex[kPermChunk / 256];
+  perm_load<4, kPermChunk / 256>(topk_idx, T * k, ex);
+  perm_layout<4, kPermChunk / 256, true>(ex, T, k, E, capacity, blockIdx.x == 0, counts, offsets,
+                                         dest, src, sm);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + wave;
   if (t >= T || !x_perm) return;

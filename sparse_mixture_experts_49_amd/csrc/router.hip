@@ -136,6 +136,32 @@ __device__ __forceinline__ void route_tile(
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) red[wave][16 * m + 4 * c + i][nt * 16 + r] = acc[m][nt][i];
+
+  // The bias words of the lane's experts (quarter q of a quad holds experts q, q+4,
+  // ...), all issued before the barrier so that their latency overlaps it rather
+  // than adding one round trip per expert to the epilogue.
+  constexpr int kMaxPer = 16;
+  float bb[kMaxPer], bs[kMaxPer];
+  {
+    const int q = lane & 3;
+#pragma unroll
+    for (int j = 0; j < kMaxPer; ++j) {
+      bb[j] = 0.f;
+      bs[j] = 0.f;
+    }
+    if (wave < MT) {
+      if (br) {
+#pragma unroll
+        for (int j = 0; j < kMaxPer; ++j)
+          if (4 * j < E) bb[j] = br[min(q + 4 * j, E - 1)];
+      }
+      if (bsel) {
+#pragma unroll
+        for (int j = 0; j < kMaxPer; ++j)
+          if (4 * j < E) bs[j] = bsel[min(q + 4 * j, E - 1)];
+      }
+    }
+  }
   __syncthreads();
 
   if (wave < MT) {
@@ -144,7 +170,6 @@ __device__ __forceinline__ void route_tile(
     const int tq = lane >> 2, q = lane & 3;
     const int tr = 16 * wave + tq;                   // token row of the block
     const int t = t0 + tr;
-    constexpr int kMaxPer = 16;
     float g[kMaxPer], p[kMaxPer], sc[kMaxPer];
     float m = -INFINITY;
 #pragma unroll
@@ -155,7 +180,7 @@ __device__ __forceinline__ void route_tile(
         g[j] = red[0][tr][e];
 #pragma unroll
         for (int w = 1; w < WAVES; ++w) g[j] += red[w][tr][e];   // in wave order
-        if (br) g[j] += br[e];
+        if (br) g[j] += bb[j];
         m = fmaxf(m, g[j]);
       }
     }
@@ -174,7 +199,7 @@ __device__ __forceinline__ void route_tile(
     for (int j = 0; j < kMaxPer; ++j) {
       p[j] *= inv;
       const int e = q + 4 * j;
-      sc[j] = (bsel && e < E) ? g[j] + bsel[e] : g[j];   // ranking scores
+      sc[j] = (bsel && e < E) ? g[j] + bs[j] : g[j];     // ranking scores
     }
     if (q == 0) sm.lse[tr] = m + logf(s);
 
@@ -246,21 +271,21 @@ __device__ __forceinline__ void route_tile(
   __syncthreads();
 }
 
-// One block = 16*MT tokens x all experts, 8 waves splitting d.  The block then
+// One block = 16*MT tokens x all experts, W waves splitting d.  The block then
 // writes its partial sums of the aux loss and z-loss for aux_finalize_kernel
 // and, for the reroute policy, every token's experts in ranking order.
-template <typename T, int NT, int MT>
-__global__ __launch_bounds__(kRouterWaves * 64) void router_kernel(
+template <typename T, int NT, int MT, int W>
+__global__ __launch_bounds__(W * 64) void router_kernel(
     const T* __restrict__ x, const T* __restrict__ wr, const float* __restrict__ br,
     const float* __restrict__ bsel, int T_, int d, int E, int k, int renorm,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
     double* __restrict__ part_psum, int32_t* __restrict__ part_top1, double* __restrict__ part_z,
     int32_t* __restrict__ rr_rank) {
-  __shared__ RouterTileLds<kRouterWaves, MT> sm;
+  __shared__ RouterTileLds<W, MT> sm;
   constexpr int kTok = kRouterTile * MT;
   const int t0 = blockIdx.x * kTok;
-  route_tile<T, NT, kRouterWaves, MT>(x, wr, br, bsel, T_, d, E, k, renorm, t0, rr_rank != nullptr,
-                                      topk_idx, topk_w, sm);
+  route_tile<T, NT, W, MT>(x, wr, br, bsel, T_, d, E, k, renorm, t0, rr_rank != nullptr, topk_idx,
+                           topk_w, sm);
   auto& prob = sm.prob;
   auto& top1 = sm.top1;
   auto& lse = sm.lse;
@@ -288,7 +313,7 @@ __global__ __launch_bounds__(kRouterWaves * 64) void router_kernel(
     // ranked above it, as {e, weight bits}.  Lanes of a wave take the 64
     // experts of one token, so the score reads are LDS broadcasts.
 #pragma unroll 1
-    for (int idx = threadIdx.x; idx < kTok * 64; idx += kRouterWaves * 64) {
+    for (int idx = threadIdx.x; idx < kTok * 64; idx += W * 64) {
       const int tr = idx >> 6, e = idx & 63, t = t0 + tr;
       if (e >= E || t >= T_) continue;
       const uint64_t key = sm.rkey[tr][e];
@@ -312,14 +337,18 @@ __global__ __launch_bounds__(kAuxThreads) void aux_finalize_kernel(
     int capacity, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ dest, int32_t* __restrict__ src) {
   __shared__ AuxLds<kAuxThreads> ared;
-  __shared__ PermLayoutLds<kAuxThreads / 64, kPermWide / kAuxThreads, false> psm;
+  constexpr int kBatches = kPermWide / kAuxThreads;
+  __shared__ PermLayoutLds<kAuxThreads / 64, kBatches, false> psm;
+  // Small layers: the dispatch layout too, saving the permute's own launch.  Its
+  // loads are issued first, so that their latency overlaps the reduction's.
+  int ex[kBatches];
+  if (perm) perm_load<kAuxThreads / 64, kBatches>(topk_idx, T_ * k, ex);
   aux_reduce<kAuxThreads>(part_psum, part_top1, part_z, nblk, T_, E, top1_count, prob_mean, aux,
                           z_loss, ared);
   if (threadIdx.x == 128 && rounds_zero) *rounds_zero = 0;
-  // Small layers: the dispatch layout too, saving the permute's own launch.
   if (perm)
-    perm_layout<kAuxThreads / 64, kPermWide / kAuxThreads, false>(topk_idx, T_, k, E, capacity, true,
-                                                                  counts, offsets, dest, src, psm);
+    perm_layout<kAuxThreads / 64, kBatches, false>(ex, T_, k, E, capacity, true, counts, offsets,
+                                                   dest, src, psm);
 }
 
 bool router_can_permute(int assignments) { return assignments <= kPermWide; }
@@ -343,7 +372,7 @@ static hipError_t launch_router_t(const RouterArgs& a, hipStream_t s) {
   const T* wr = static_cast<const T*>(a.w_router);
 #define MOE_ROUTER_CASE(NT, MT)                                                               \
   case NT * 4 + MT:                                                                         \
-    router_kernel<T, NT, MT><<<nblk, kRouterWaves * 64, 0, s>>>(                              \
+    router_kernel<T, NT, MT, kRouterWaves><<<nblk, kRouterWaves * 64, 0, s>>>(                \
         x, wr, a.b_router, a.b_select, a.T, a.d, a.E, a.k, a.renorm, a.topk_idx, a.topk_w,   \
         a.part_psum, a.part_top1, a.part_z, a.rr_rank);                                       \
     break;
