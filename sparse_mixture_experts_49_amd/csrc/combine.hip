@@ -40,27 +40,42 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   }
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   if constexpr (PARTIAL) {
-    // Deferred split-k sums (few tokens): per slot, its parts (up to kMaxParts)
-    // are loaded before any is added, so they are in flight together; the sum
-    // runs in part order, then the slot is weighted in slot order.
+    // Deferred split-k sums (few tokens): two slots at a time, the parts of both
+    // (up to kMaxParts each) loaded before any is added, so they are in flight
+    // together; each slot's sum runs in part order, then the slots are weighted
+    // in slot order.
     constexpr int kMaxParts = 8;
 #pragma unroll
-    for (int s = 0; s < 8; ++s)
-      if (dst[s] >= 0) {
-        const float* p = partial + (size_t)dst[s] * d + (size_t)v * 4;
-        f32x4 part[kMaxParts];
+    for (int s0 = 0; s0 < 8; s0 += 2) {
+      if (s0 >= k) break;
+      f32x4 part[2][kMaxParts];
 #pragma unroll
-        for (int sp = 0; sp < kMaxParts; ++sp)
-          if (sp < splits) part[sp] = *reinterpret_cast<const f32x4*>(p + (size_t)sp * rows_cap * d);
-        f32x4 ov = part[0];
+      for (int u = 0; u < 2; ++u) {
+        const int s = s0 + u;
+        if (dst[s] >= 0) {
+          const float* p = partial + (size_t)dst[s] * d + (size_t)v * 4;
 #pragma unroll
-        for (int sp = 1; sp < kMaxParts; ++sp)
-          if (sp < splits) ov += part[sp];
-        for (int sp = kMaxParts; sp < splits; ++sp)
-          ov += *reinterpret_cast<const f32x4*>(p + (size_t)sp * rows_cap * d);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] = fmaf(w[s], ov[i], acc[i]);
+          for (int sp = 0; sp < kMaxParts; ++sp)
+            if (sp < splits)
+              part[u][sp] = *reinterpret_cast<const f32x4*>(p + (size_t)sp * rows_cap * d);
+        }
       }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int s = s0 + u;
+        if (dst[s] >= 0) {
+          f32x4 ov = part[u][0];
+#pragma unroll
+          for (int sp = 1; sp < kMaxParts; ++sp)
+            if (sp < splits) ov += part[u][sp];
+          const float* p = partial + (size_t)dst[s] * d + (size_t)v * 4;
+          for (int sp = kMaxParts; sp < splits; ++sp)
+            ov += *reinterpret_cast<const f32x4*>(p + (size_t)sp * rows_cap * d);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[i] = fmaf(w[s], ov[i], acc[i]);
+        }
+      }
+    }
   } else {
     f32x4 ov[8];
 #pragma unroll
@@ -78,8 +93,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
   const dim3 grid(a.T, (a.d / 4 + 255) / 256);
-  // Two instances: with deferred split-k parts (the loads of every part of every
-  // slot in flight at once; few tokens) and without (few registers, many waves).
+  // Two instances: with deferred split-k parts (the loads of every part of two
+  // slots in flight at once; few tokens) and without (few registers, many waves).
   if (a.partial)
     combine_kernel<true><<<grid, 256, 0, s>>>(a.o, a.dest, a.topk_w, a.shared, a.T, a.d, a.k, a.y,
                                               a.partial, a.splits, a.rows_cap);
