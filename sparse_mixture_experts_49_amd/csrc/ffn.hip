@@ -883,6 +883,163 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Weight-streaming kernel, first product (bf16), both operands through LDS.
+// Same block shape as ffn_stream_kernel with NWN = 1 (4 waves, wave w owns the
+// 16 output columns n0 + 16w + [0, 16); the block owns up to 16*NMT rows of
+// expert blockIdx.y, row group and k split in blockIdx.z), but the weights go
+// global -> LDS by DMA too, in stages of kLdsRun bytes of each of the block's
+// 64 weight rows (and of its A rows).  One DMA instruction then reads two whole
+// 512 B runs, where the register ring reads 64 B of each of 16 rows per
+// instruction: measured on MI355X with the decode layer's first product, the
+// register pattern streams its weights at ~5.2 TB/s whatever the A traffic
+// (the same kernel without its A loads is no faster), and DMA probes of
+// 512 B runs x 64 rows, A rows included, at 5.7-5.8 TB/s.
+//   - Stage s of the k range (kLdsStageK elements) sits in ring slot s % kLdsDepth
+//     of W (64 rows) and of A (16*NMT rows), rows of 512 B whose 16 B pieces
+//     sit at (piece ^ (row & 15)), so the fragment reads (16 rows, same piece)
+//     hit every bank once.  DMA instruction i of wave w writes 1 KB of a stage:
+//     rows 2g, 2g + 1 with g = 4i + w.
+//   - Per stage: wait for its loads, barrier (the slot of stage s - 1 is then
+//     free), issue stage s + kLdsDepth - 1 into that slot, then 8 MFMAs per
+//     active m-tile, lane (fr, fc) using piece 4q + fc of its A row and its W
+//     row for MFMA q.
+// Rows past the block's last are clamped (their data is never used); m-tiles
+// past it issue no MFMA.  Sum order is fixed per block (bitwise repeatable).
+// ---------------------------------------------------------------------------
+constexpr int kLdsRun = 512;                   // bytes of each row per stage
+constexpr int kLdsStageK = kLdsRun / 2;        // bf16 elements per stage
+constexpr int kLdsDepth = 3;
+
+template <bool SPLIT, int NMT>
+__global__ __launch_bounds__(256) void ffn_stream_lds_kernel(
+    const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets,
+    const uint16_t* __restrict__ W, const uint16_t* __restrict__ bias, void* __restrict__ out,
+    size_t out_plane, int E, int N, int K, int splits, float* __restrict__ partial, int rows_cap,
+    const int32_t* __restrict__ gather, int gather_k) {
+  constexpr int kMR = 16 * NMT;
+  constexpr int kWBytes = 64 * kLdsRun;          // W part of a stage: 32 KB
+  constexpr int kABytes = kMR * kLdsRun;         // A part: 8 KB per m-tile
+  constexpr int kWI = kWBytes / 4096;            // 1 KB DMA instructions per wave per stage
+  constexpr int kAI = kABytes / 4096;
+  constexpr int kPieces = kLdsRun / 16;
+  static_assert(kWI * 4096 == kWBytes && kAI * 4096 == kABytes, "DMA plan");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsDepth * (kWBytes + kABytes)];
+
+  const int e = blockIdx.y;
+  const int split = blockIdx.z % splits;
+  const int seg0 = offsets[e], seg1 = offsets[e + 1];
+  const int r0 = seg0 + (blockIdx.z / splits) * kMR;
+  if (r0 >= seg1) return;
+  const int r1 = min(seg1, r0 + kMR);
+  const int mt_active = (r1 - r0 + 15) >> 4;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int fr = lane & 15, fc = lane >> 4;
+  const int nb = blockIdx.x * 64;                // the block's first weight row
+  const int n0 = nb + wave * 16;
+
+  // DMA plan (see above): lane L of instruction i writes physical piece L % 32
+  // of row 2g + L / 32, i.e. loads logical piece (L % 32) ^ (row & 15).
+  uint32_t w_off[kWI];
+#pragma unroll
+  for (int i = 0; i < kWI; ++i) {
+    const int row = 2 * (i * 4 + wave) + (lane >> 5);
+    const int piece = (lane & 31) ^ (row & 15);
+    w_off[i] = (uint32_t)(((size_t)row * K + piece * 8) * 2);
+  }
+  int arow[kAI];
+#pragma unroll
+  for (int i = 0; i < kAI; ++i) arow[i] = min(r0 + 2 * (i * 4 + wave) + (lane >> 5), r1 - 1);
+  a_rows<kAI>(gather, gather_k, arow);
+  const uint16_t* a_src[kAI];
+#pragma unroll
+  for (int i = 0; i < kAI; ++i) {
+    const int row = 2 * (i * 4 + wave) + (lane >> 5);
+    a_src[i] = A + (size_t)arow[i] * K + (((lane & 31) ^ (row & 15)) * 8);
+  }
+  const uint16_t* w_base = W + ((size_t)e * N + nb) * K;
+
+  f32x4 acc[NMT];
+#pragma unroll
+  for (int i = 0; i < NMT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nst_all = K / kLdsStageK;
+  const int s0 = (int)((long)split * nst_all / splits);
+  const int nst = (int)((long)(split + 1) * nst_all / splits) - s0;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
+  auto issue = [&](int slot, int st) {
+    const int k0 = (s0 + st) * kLdsStageK;
+    const uint32_t wl = lds0 + slot * kWBytes, al = lds0 + kLdsDepth * kWBytes + slot * kABytes;
+#pragma unroll
+    for (int i = 0; i < kAI; ++i) load_lds16_raw(a_src[i] + k0, al + (i * 4 + wave) * 1024);
+    const uint16_t* wb = w_base + k0;
+#pragma unroll
+    for (int i = 0; i < kWI; ++i) load_lds16_sv(wb, w_off[i], wl + (i * 4 + wave) * 1024);
+  };
+  // Every fragment read of the stage is issued before its MFMAs; the active
+  // m-tile count picks one of two unrolled bodies (a uniform branch).
+  constexpr int kQ = kPieces / 4;                // MFMAs per m-tile per stage
+  auto compute = [&](int slot) {
+    const uint8_t* ws = lds + slot * kWBytes;
+    const uint8_t* as = lds + kLdsDepth * kWBytes + slot * kABytes;
+    const int wrow = wave * 16 + fr;
+    u32x4 wf[kQ];
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) wf[q] = ld16(ws + wrow * kLdsRun + (((q * 4 + fc) ^ (wrow & 15)) << 4));
+    auto tiles = [&](auto mt_c) {
+      constexpr int MT = decltype(mt_c)::value;
+      u32x4 af[MT][kQ];
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+        const int row = i * 16 + fr;
+#pragma unroll
+        for (int q = 0; q < kQ; ++q) af[i][q] = ld16(as + row * kLdsRun + (((q * 4 + fc) ^ (row & 15)) << 4));
+      }
+#pragma unroll
+      for (int q = 0; q < kQ; ++q)
+#pragma unroll
+        for (int i = 0; i < MT; ++i) acc[i] = mfma_bf16(af[i][q], wf[q], acc[i]);
+    };
+    if (NMT == 1 || mt_active == 1) tiles(std::integral_constant<int, 1>{});
+    else tiles(std::integral_constant<int, NMT>{});
+  };
+
+  // Loads complete in issue order: in steady state kLdsDepth - 2 stages were
+  // issued after stage s, so waiting for at most that many instructions lands
+  // it; near the end (fewer issued after it) wait for all.
+  constexpr int kSteadyWait = (kLdsDepth - 2) * (kWI + kAI);
+#pragma unroll
+  for (int d = 0; d < kLdsDepth - 1; ++d)
+    if (d < nst) issue(d, d);
+  for (int st = 0; st < nst; ++st) {
+    if (st + kLdsDepth - 2 < nst) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kSteadyWait));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+    __syncthreads();
+    if (st + kLdsDepth - 1 < nst) issue((st + kLdsDepth - 1) % kLdsDepth, st + kLdsDepth - 1);
+    compute(st % kLdsDepth);
+  }
+
+  // Epilogue, as ffn_stream_kernel's: lane (fr, fc) holds column n0 + fr of
+  // rows 4fc + v of each m-tile.
+  const int col = n0 + fr;
+  const float bv = (bias && split == 0) ? bf16_to_f32(bias[(size_t)e * N + col]) : 0.f;
+#pragma unroll
+  for (int i = 0; i < NMT; ++i) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int row = r0 + i * 16 + 4 * fc + v;
+      if (row < r1) {
+        if (splits > 1)
+          partial[((size_t)split * rows_cap + row) * N + col] = acc[i][v] + bv;
+        else
+          emit<uint16_t, true, SPLIT>(out, out_plane, (size_t)row * N + col, acc[i][v] + bv);
+      }
+    }
+  }
+}
+
 // Finish a split-k product: out[r][c] = epilogue(sum over splits s of
 // partial[s][r][c]), summed in split order; rows r < offsets[E] only.  Each
 // thread handles four consecutive columns.
@@ -906,6 +1063,7 @@ __global__ __launch_bounds__(256) void ffn_splitk_reduce(
 // descriptor alone (never from device data).
 struct StreamShape {
   int nmt, nwn, groups, splits;
+  bool lds;   // ffn_stream_lds_kernel (bf16 first product, at most 32 rows per block)
 };
 static StreamShape stream_shape(bool bf16, bool up, bool split, int E, int N, int K,
                                 int max_rows_per_expert) {
@@ -916,7 +1074,8 @@ static StreamShape stream_shape(bool bf16, bool up, bool split, int E, int N, in
   const int bound = max_rows_per_expert;
   sh.nmt = bound <= 16 ? 1 : bound <= 32 ? 2 : bound <= 64 ? 4 : 10;
   sh.groups = (bound + 16 * sh.nmt - 1) / (16 * sh.nmt);
-  sh.nwn = (sh.nmt < 10 && (long)E * (N / 128) >= 1024) ? 2 : 1;
+  sh.lds = bf16 && up && sh.nmt <= 2 && K % kLdsStageK == 0 && N % 64 == 0;
+  sh.nwn = (!sh.lds && sh.nmt < 10 && (long)E * (N / 128) >= 1024) ? 2 : 1;
   // Split the k range when the grid is too small to keep enough weight loads
   // in flight (fewer than kStreamMinBlocks / 2 blocks), up to about
   // kStreamMinBlocks blocks and keeping >= 8 chunks per split; the partial sums
@@ -963,9 +1122,30 @@ static void launch_stream_nmt(const FfnArgs& a, const StreamShape& sh, hipStream
   }
 }
 
+template <bool SPLIT, int NMT>
+static void launch_stream_lds(const FfnArgs& a, const StreamShape& sh, hipStream_t s) {
+  const dim3 grid(a.N / 64, a.E, sh.groups * sh.splits);
+  ffn_stream_lds_kernel<SPLIT, NMT><<<grid, 256, 0, s>>>(
+      static_cast<const uint16_t*>(a.a), a.offsets, static_cast<const uint16_t*>(a.w),
+      static_cast<const uint16_t*>(a.bias), a.out, a.plane, a.E, a.N, a.K, sh.splits, a.partial,
+      a.max_rows, a.gather, a.gather_k);
+  if (sh.splits > 1) {
+    const size_t quads = (size_t)a.max_rows * (a.N / 4);
+    ffn_splitk_reduce<uint16_t, true, SPLIT><<<(unsigned)((quads + 255) / 256), 256, 0, s>>>(
+        a.partial, a.offsets, a.E, a.N, sh.splits, a.max_rows, a.out, a.plane);
+  }
+}
+
 template <typename T, bool UP, bool SPLIT>
 static void launch_stream(const FfnArgs& a, hipStream_t s) {
   const StreamShape sh = stream_shape(a.bf16, UP, SPLIT, a.E, a.N, a.K, a.max_rows_per_expert);
+  if constexpr (std::is_same<T, uint16_t>::value && UP) {
+    if (sh.lds) {
+      if (sh.nmt == 1) launch_stream_lds<SPLIT, 1>(a, sh, s);
+      else launch_stream_lds<SPLIT, 2>(a, sh, s);
+      return;
+    }
+  }
   switch (sh.nmt) {
     case 1: launch_stream_nmt<T, UP, SPLIT, 1>(a, sh, s); break;
     case 2: launch_stream_nmt<T, UP, SPLIT, 2>(a, sh, s); break;

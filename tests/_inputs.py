@@ -88,6 +88,12 @@ SMALL = {
                                  "bf16"),
     "long_f_top1_bf16": Workload("long_f_top1_bf16", 600, 512, 4096, 8, 1, False, 0, True,
                                  "bf16"),
+    # few column blocks and d_model = 4096 on the weight-streaming path: the first
+    # product's k range is split over blocks and reduced (top-2 of 2 experts: both hold
+    # all 24 rows, two 16-row tiles; top-1 of 4: mostly one tile)
+    "split_k_bf16": Workload("split_k_bf16", 24, 4096, 256, 2, 2, True, 0, True, "bf16"),
+    "split_k_top1_bf16": Workload("split_k_top1_bf16", 20, 4096, 256, 4, 1, False, 0, True,
+                                  "bf16"),
     # the mid-size layer's shapes (4096 tokens, 16 experts) with a selection bias
     "mid_select_bias_bf16": Workload("mid_select_bias_bf16", 4096, 1024, 4096, 16, 2, True, 0, True,
                                      "bf16", selection_bias=True),
