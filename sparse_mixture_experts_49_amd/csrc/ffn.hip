@@ -7,7 +7,7 @@
 // one dense product out[seg] = A[seg] W_e^T (+ bias_e) with W_e stored
 // [N][K] (K contiguous, like A).  Experts with no rows do no work.
 //
-// Two kernels, chosen on the host from a bound on rows per expert (the
+// Three kernels, chosen on the host from a bound on rows per expert (the
 // device-side counts are never read back):
 //   * ffn_tiled_kernel  -- many rows per expert: 256 x 256 (or x 128) output
 //     tiles for prefill, 128-row tiles from 64 rows per expert; both
@@ -19,6 +19,9 @@
 //     registers in the MFMA operand layout, while the block's (at most
 //     16*NMT) rows of A are staged through LDS once per k-chunk and shared by
 //     the four waves.  Weight bytes are read once.
+//   * ffn_stream_lds_kernel -- the same blocks for a bf16 first product with at
+//     most 32 rows per block, both operands staged through LDS by DMA in whole
+//     512 B runs of each row.
 // The first product applies bias + exact-erf GELU in its epilogue and stores
 // dtype h; the second adds its bias and stores fp32 o.
 #include <algorithm>
