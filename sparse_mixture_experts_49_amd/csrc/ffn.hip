@@ -771,6 +771,24 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(
     const T* base = (kTwoA && plane) ? A_lo : A;
     a_src[i] = base + (size_t)arow[i] * K + logical * kPerVec;
   }
+  // Compact plan for a block whose rows fit one m-tile (NMT > 1): the first 16
+  // rows of every plane are 4 KB in all, one 1 KB instruction per wave, written
+  // where the full plan puts them (plane p at p * kPlaneBytes).  Halves (or
+  // better) the A loads of blocks with few rows, e.g. decode.
+  constexpr int kHalfPlane = 16 * kRowBytes;
+  const bool compact = NMT > 1 && mt_active == 1;
+  const T* a_src1 = nullptr;
+  uint32_t a_dst1 = 0;
+  if (compact) {
+    const int byte = wave * 1024 + lane * 16;
+    const int plane = byte / kHalfPlane, rem = byte % kHalfPlane;
+    const int row = rem / kRowBytes;
+    int ar[1] = {min(r0 + row, r1 - 1)};
+    if constexpr (UP) a_rows<1>(gather, gather_k, ar);
+    const int logical = ((rem % kRowBytes) / 16) ^ swz(row);
+    a_src1 = ((kTwoA && plane) ? A_lo : A) + (size_t)ar[0] * K + logical * kPerVec;
+    a_dst1 = (uint32_t)(((wave * 1024) / kHalfPlane) * kPlaneBytes + (wave * 1024) % kHalfPlane);
+  }
   const T* w_src[NWN];
   const T* Wexp = W + (size_t)e * N * K;
 #pragma unroll
@@ -797,9 +815,13 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(
     for (int j = 0; j < NWN; ++j)
 #pragma unroll
       for (int q = 0; q < kQ; ++q) wdst[j][q] = ld16(w_src[j] + k0 + q * 4 * kPerVec);
+    if (compact) {
+      load_lds16_raw(a_src1 + k0, lds0 + slot * kStageBytes + a_dst1);
+    } else {
 #pragma unroll
-    for (int i = 0; i < kAInst; ++i)
-      load_lds16_raw(a_src[i] + k0, lds0 + slot * kStageBytes + (i * 4 + wave) * 1024);
+      for (int i = 0; i < kAInst; ++i)
+        load_lds16_raw(a_src[i] + k0, lds0 + slot * kStageBytes + (i * 4 + wave) * 1024);
+    }
   };
   auto compute = [&](const u32x4 (&wc)[NWN][kQ], int slot) {
     const uint8_t* st = lds + slot * kStageBytes;
@@ -839,10 +861,15 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(
   // were issued after A of the next chunk, so waiting for at most that many
   // outstanding lands it; near the end (fewer loads issued) wait for all.
   constexpr int kSteadyWait = (kDepth - 2) * (kWInst + kAInst);
+  constexpr int kSteadyWait1 = (kDepth - 2) * (kWInst + 1);   // compact plan
+  auto steady_wait = [&]() {
+    if (compact) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kSteadyWait1));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kSteadyWait));
+  };
 #pragma unroll
   for (int d = 0; d < kDepth - 1; ++d)
     if (d < nch) issue(wbuf[d], d, d);
-  if (nch >= kDepth - 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kSteadyWait));
+  if (nch >= kDepth - 1) steady_wait();
   else __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
   __syncthreads();
   for (int ch0 = 0; ch0 < nch; ch0 += kDepth) {
@@ -854,7 +881,7 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(
         const bool steady = ch + kDepth - 1 < nch;
         if (steady) issue(wbuf[dn], dn, ch + kDepth - 1);
         compute(wbuf[d], d);
-        if (steady) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kSteadyWait));
+        if (steady) steady_wait();
         else __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
         __syncthreads();
       }
