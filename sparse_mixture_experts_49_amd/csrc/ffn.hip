@@ -926,34 +926,47 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(
 // (the same kernel without its A loads is no faster), and DMA probes of
 // 512 B runs x 64 rows, A rows included, at 5.7-5.8 TB/s.
 //   - Stage s of the k range (kLdsStageK elements) sits in ring slot s % kLdsDepth
-//     of W (64 rows) and of A (16*NMT rows), rows of 512 B whose 16 B pieces
-//     sit at (piece ^ (row & 15)), so the fragment reads (16 rows, same piece)
-//     hit every bank once.  DMA instruction i of wave w writes 1 KB of a stage:
-//     rows 2g, 2g + 1 with g = 4i + w.
+//     of W (64 rows) and of A (16*NMT rows), rows of kLdsRun bytes whose 16 B
+//     pieces sit at (piece ^ (row & 15)), so the fragment reads (16 rows, same
+//     piece) hit every bank once.  DMA instruction i of wave w writes 1 KB of a
+//     stage: the 1024 / kLdsRun whole rows from row (1024 / kLdsRun) * g on,
+//     g = 4i + w.
 //   - Per stage: wait for its loads, barrier (the slot of stage s - 1 is then
 //     free), issue stage s + kLdsDepth - 1 into that slot, then 8 MFMAs per
 //     active m-tile, lane (fr, fc) using piece 4q + fc of its A row and its W
 //     row for MFMA q.
 // Rows past the block's last are clamped (their data is never used); m-tiles
 // past it issue no MFMA.  Sum order is fixed per block (bitwise repeatable).
+//   - Persistent over column blocks: block x streams the `cpb` column blocks
+//     x*cpb .. of its expert one after the other (the host sizes the grid to
+//     one block per CU), and the stage sequence runs on across their
+//     boundaries, so the ring never drains and the block's set-up (offsets,
+//     gathered row indices: ~2.5 us measured) is paid once, not per 64
+//     columns.  Each column block keeps its own accumulators (cpb <=
+//     kLdsMaxCpb) and all results are stored after the last stage: a store
+//     in the loop would share the vmcnt counter with the DMA loads without
+//     completing in order with them, and the loop's wait counts assume
+//     loads only.
 // ---------------------------------------------------------------------------
 constexpr int kLdsRun = 512;                   // bytes of each row per stage
 constexpr int kLdsStageK = kLdsRun / 2;        // bf16 elements per stage
 constexpr int kLdsDepth = 3;
+constexpr int kLdsMaxCpb = 8;                  // column blocks per block, at most
 
 template <bool SPLIT, int NMT>
 __global__ __launch_bounds__(256) void ffn_stream_lds_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets,
     const uint16_t* __restrict__ W, const uint16_t* __restrict__ bias, void* __restrict__ out,
     size_t out_plane, int E, int N, int K, int splits, float* __restrict__ partial, int rows_cap,
-    const int32_t* __restrict__ gather, int gather_k) {
+    const int32_t* __restrict__ gather, int gather_k, int cpb) {
   constexpr int kMR = 16 * NMT;
   constexpr int kWBytes = 64 * kLdsRun;          // W part of a stage: 32 KB
   constexpr int kABytes = kMR * kLdsRun;         // A part: 8 KB per m-tile
   constexpr int kWI = kWBytes / 4096;            // 1 KB DMA instructions per wave per stage
   constexpr int kAI = kABytes / 4096;
   constexpr int kPieces = kLdsRun / 16;
-  static_assert(kWI * 4096 == kWBytes && kAI * 4096 == kABytes, "DMA plan");
+  static_assert(kWI * 4096 == kWBytes && kAI * 4096 == kABytes && kLdsRun <= 1024 &&
+                kPieces >= 16, "DMA plan");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsDepth * (kWBytes + kABytes)];
 
   const int e = blockIdx.y;
@@ -967,51 +980,57 @@ __global__ __launch_bounds__(256) void ffn_stream_lds_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int fr = lane & 15, fc = lane >> 4;
-  const int nb = blockIdx.x * 64;                // the block's first weight row
-  const int n0 = nb + wave * 16;
+  const int cb0 = blockIdx.x * cpb;              // the block's first column block
+  const int ncb = min(cpb, N / 64 - cb0);
+  if (ncb <= 0) return;
 
-  // DMA plan (see above): lane L of instruction i writes physical piece L % 32
-  // of row 2g + L / 32, i.e. loads logical piece (L % 32) ^ (row & 15).
+  // DMA plan (see above): with R = 1024 / kLdsRun rows per instruction, lane L
+  // of instruction i writes physical piece L % kPieces of row R*g + L / kPieces,
+  // i.e. loads logical piece (L % kPieces) ^ (row & 15).
+  constexpr int kRowsPerInst = 1024 / kLdsRun;
+  auto plan_row = [&](int i) { return kRowsPerInst * (i * 4 + wave) + lane / kPieces; };
+  const int piece = lane % kPieces;
   uint32_t w_off[kWI];
 #pragma unroll
   for (int i = 0; i < kWI; ++i) {
-    const int row = 2 * (i * 4 + wave) + (lane >> 5);
-    const int piece = (lane & 31) ^ (row & 15);
-    w_off[i] = (uint32_t)(((size_t)row * K + piece * 8) * 2);
+    const int row = plan_row(i);
+    w_off[i] = (uint32_t)(((size_t)row * K + (piece ^ (row & 15)) * 8) * 2);
   }
   int arow[kAI];
 #pragma unroll
-  for (int i = 0; i < kAI; ++i) arow[i] = min(r0 + 2 * (i * 4 + wave) + (lane >> 5), r1 - 1);
+  for (int i = 0; i < kAI; ++i) arow[i] = min(r0 + plan_row(i), r1 - 1);
   a_rows<kAI>(gather, gather_k, arow);
   const uint16_t* a_src[kAI];
 #pragma unroll
-  for (int i = 0; i < kAI; ++i) {
-    const int row = 2 * (i * 4 + wave) + (lane >> 5);
-    a_src[i] = A + (size_t)arow[i] * K + (((lane & 31) ^ (row & 15)) * 8);
-  }
-  const uint16_t* w_base = W + ((size_t)e * N + nb) * K;
+  for (int i = 0; i < kAI; ++i)
+    a_src[i] = A + (size_t)arow[i] * K + ((piece ^ (plan_row(i) & 15)) * 8);
+  const uint16_t* w_base = W + ((size_t)e * N + (size_t)cb0 * 64) * K;
 
-  f32x4 acc[NMT];
+  f32x4 acc[kLdsMaxCpb][NMT];
 #pragma unroll
-  for (int i = 0; i < NMT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < kLdsMaxCpb; ++j)
+#pragma unroll
+    for (int i = 0; i < NMT; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nst_all = K / kLdsStageK;
   const int s0 = (int)((long)split * nst_all / splits);
   const int nst = (int)((long)(split + 1) * nst_all / splits) - s0;
   const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
-  auto issue = [&](int slot, int st) {
+  // Stage t of the block's sequence: column block t / nst, k stage t % nst.
+  auto issue = [&](int slot, int t) {
+    const int j = t / nst, st = t - j * nst;
     const int k0 = (s0 + st) * kLdsStageK;
     const uint32_t wl = lds0 + slot * kWBytes, al = lds0 + kLdsDepth * kWBytes + slot * kABytes;
 #pragma unroll
     for (int i = 0; i < kAI; ++i) load_lds16_raw(a_src[i] + k0, al + (i * 4 + wave) * 1024);
-    const uint16_t* wb = w_base + k0;
+    const uint16_t* wb = w_base + (size_t)j * 64 * K + k0;
 #pragma unroll
     for (int i = 0; i < kWI; ++i) load_lds16_sv(wb, w_off[i], wl + (i * 4 + wave) * 1024);
   };
   // Every fragment read of the stage is issued before its MFMAs; the active
   // m-tile count picks one of two unrolled bodies (a uniform branch).
   constexpr int kQ = kPieces / 4;                // MFMAs per m-tile per stage
-  auto compute = [&](int slot) {
+  auto compute = [&](int slot, f32x4 (&acc_j)[NMT]) {
     const uint8_t* ws = lds + slot * kWBytes;
     const uint8_t* as = lds + kLdsDepth * kWBytes + slot * kABytes;
     const int wrow = wave * 16 + fr;
@@ -1030,41 +1049,67 @@ __global__ __launch_bounds__(256) void ffn_stream_lds_kernel(
 #pragma unroll
       for (int q = 0; q < kQ; ++q)
 #pragma unroll
-        for (int i = 0; i < MT; ++i) acc[i] = mfma_bf16(af[i][q], wf[q], acc[i]);
+        for (int i = 0; i < MT; ++i) acc_j[i] = mfma_bf16(af[i][q], wf[q], acc_j[i]);
     };
     if (NMT == 1 || mt_active == 1) tiles(std::integral_constant<int, 1>{});
     else tiles(std::integral_constant<int, NMT>{});
   };
 
   // Loads complete in issue order: in steady state kLdsDepth - 2 stages were
-  // issued after stage s, so waiting for at most that many instructions lands
-  // it; near the end (fewer issued after it) wait for all.
+  // issued after stage t, so waiting for at most that many instructions lands
+  // it; near the end (fewer issued after it) wait for all.  The column-block
+  // loop is unrolled so that each one's accumulators stay in registers.
   constexpr int kSteadyWait = (kLdsDepth - 2) * (kWI + kAI);
+  const int total = ncb * nst;
 #pragma unroll
   for (int d = 0; d < kLdsDepth - 1; ++d)
-    if (d < nst) issue(d, d);
-  for (int st = 0; st < nst; ++st) {
-    if (st + kLdsDepth - 2 < nst) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kSteadyWait));
-    else __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
-    __syncthreads();
-    if (st + kLdsDepth - 1 < nst) issue((st + kLdsDepth - 1) % kLdsDepth, st + kLdsDepth - 1);
-    compute(st % kLdsDepth);
+    if (d < total) issue(d, d);
+#pragma unroll
+  for (int j = 0; j < kLdsMaxCpb; ++j) {
+    if (j < ncb) {
+      for (int st = 0; st < nst; ++st) {
+        const int t = j * nst + st;
+        if (t + kLdsDepth - 2 < total) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kSteadyWait));
+        else __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+        __syncthreads();
+        if (t + kLdsDepth - 1 < total) issue((t + kLdsDepth - 1) % kLdsDepth, t + kLdsDepth - 1);
+        compute(t % kLdsDepth, acc[j]);
+      }
+    }
   }
 
-  // Epilogue, as ffn_stream_kernel's: lane (fr, fc) holds column n0 + fr of
-  // rows 4fc + v of each m-tile.
-  const int col = n0 + fr;
-  const float bv = (bias && split == 0) ? bf16_to_f32(bias[(size_t)e * N + col]) : 0.f;
+  // Epilogue, as ffn_stream_kernel's, per column block: lane (fr, fc) holds
+  // column 64 * (cb0 + j) + 16 * wave + fr of rows 4fc + v of each m-tile.  The
+  // bias words of every column block are loaded first (clamped indices, one
+  // wait), not one load and wait per column block behind the stores.
+  float bvs[kLdsMaxCpb];
 #pragma unroll
-  for (int i = 0; i < NMT; ++i) {
+  for (int j = 0; j < kLdsMaxCpb; ++j) bvs[j] = 0.f;
+  if (bias && split == 0) {
+    uint16_t braw[kLdsMaxCpb];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int row = r0 + i * 16 + 4 * fc + v;
-      if (row < r1) {
-        if (splits > 1)
-          partial[((size_t)split * rows_cap + row) * N + col] = acc[i][v] + bv;
-        else
-          emit<uint16_t, true, SPLIT>(out, out_plane, (size_t)row * N + col, acc[i][v] + bv);
+    for (int j = 0; j < kLdsMaxCpb; ++j)
+      braw[j] = bias[(size_t)e * N + (cb0 + min(j, ncb - 1)) * 64 + wave * 16 + fr];
+#pragma unroll
+    for (int j = 0; j < kLdsMaxCpb; ++j) bvs[j] = bf16_to_f32(braw[j]);
+  }
+#pragma unroll
+  for (int j = 0; j < kLdsMaxCpb; ++j) {
+    if (j < ncb) {
+      const int col = (cb0 + j) * 64 + wave * 16 + fr;
+      const float bv = bvs[j];
+#pragma unroll
+      for (int i = 0; i < NMT; ++i) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int row = r0 + i * 16 + 4 * fc + v;
+          if (row < r1) {
+            if (splits > 1)
+              partial[((size_t)split * rows_cap + row) * N + col] = acc[j][i][v] + bv;
+            else
+              emit<uint16_t, true, SPLIT>(out, out_plane, (size_t)row * N + col, acc[j][i][v] + bv);
+          }
+        }
       }
     }
   }
@@ -1154,11 +1199,17 @@ static void launch_stream_nmt(const FfnArgs& a, const StreamShape& sh, hipStream
 
 template <bool SPLIT, int NMT>
 static void launch_stream_lds(const FfnArgs& a, const StreamShape& sh, hipStream_t s) {
-  const dim3 grid(a.N / 64, a.E, sh.groups * sh.splits);
+  // One block per CU: each block streams cpb column blocks of its expert, cpb
+  // the smallest that brings the grid down to one block per CU (at most
+  // kLdsMaxCpb).
+  const long cbs = (long)(a.N / 64) * a.E * sh.groups * sh.splits;
+  const int cpb = (int)std::min<long>(kLdsMaxCpb, std::max<long>(1, (cbs + kXcds * kCusPerXcd - 1) /
+                                                                       (kXcds * kCusPerXcd)));
+  const dim3 grid((a.N / 64 + cpb - 1) / cpb, a.E, sh.groups * sh.splits);
   ffn_stream_lds_kernel<SPLIT, NMT><<<grid, 256, 0, s>>>(
       static_cast<const uint16_t*>(a.a), a.offsets, static_cast<const uint16_t*>(a.w),
       static_cast<const uint16_t*>(a.bias), a.out, a.plane, a.E, a.N, a.K, sh.splits, a.partial,
-      a.max_rows, a.gather, a.gather_k);
+      a.max_rows, a.gather, a.gather_k, cpb);
   if (sh.splits > 1) {
     const size_t quads = (size_t)a.max_rows * (a.N / 4);
     ffn_splitk_reduce<uint16_t, true, SPLIT><<<(unsigned)((quads + 255) / 256), 256, 0, s>>>(
