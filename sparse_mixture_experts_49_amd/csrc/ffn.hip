@@ -914,29 +914,27 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Weight-streaming kernel, first product (bf16), both operands through LDS.
-// Same block shape as ffn_stream_kernel with NWN = 1 (4 waves, wave w owns the
-// 16 output columns n0 + 16w + [0, 16); the block owns up to 16*NMT rows of
-// expert blockIdx.y, row group and k split in blockIdx.z), but the weights go
-// global -> LDS by DMA too, in stages of kLdsRun bytes of each of the block's
-// 64 weight rows (and of its A rows).  One DMA instruction then reads two whole
-// 512 B runs, where the register ring reads 64 B of each of 16 rows per
-// instruction: measured on MI355X with the decode layer's first product, the
-// register pattern streams its weights at ~5.2 TB/s whatever the A traffic
-// (the same kernel without its A loads is no faster), and DMA probes of
-// 512 B runs x 64 rows, A rows included, at 5.7-5.8 TB/s.
+// Weight-streaming kernel (bf16), both operands through LDS.  Same block shape
+// as ffn_stream_kernel with NWN = 1 (4 waves, wave w owns 16 output columns of
+// each 64-column block; the block owns up to 16*NMT rows of expert blockIdx.y
+// at a time), but the weights go global -> LDS by DMA too, in stages of
+// kLdsRun bytes of each of the block's 64 weight rows (and of its A rows, both
+// planes of a split h).  One DMA instruction then reads two whole 512 B runs,
+// where the register ring reads 64 B of each of 16 rows per instruction:
+// measured on MI355X with the decode layer's first product, the register
+// pattern streams its weights at ~5.2 TB/s whatever the A traffic (the same
+// kernel without its A loads is no faster), and DMA probes of 512 B runs x 64
+// rows, A rows included, at 5.7-5.8 TB/s.
 //   - Stage s of the k range (kLdsStageK elements) sits in ring slot s % kLdsDepth
-//     of W (64 rows) and of A (16*NMT rows), rows of kLdsRun bytes whose 16 B
-//     pieces sit at (piece ^ (row & 15)), so the fragment reads (16 rows, same
-//     piece) hit every bank once.  DMA instruction i of wave w writes 1 KB of a
-//     stage: the 1024 / kLdsRun whole rows from row (1024 / kLdsRun) * g on,
-//     g = 4i + w.
+//     of W (64 rows) and of A (16*NMT rows per plane), rows of kLdsRun bytes
+//     whose 16 B pieces sit at (piece ^ (row & 15)), so the fragment reads (16
+//     rows, same piece) hit every bank once.  DMA instruction i of wave w
+//     writes 1 KB of a stage part: the 1024 / kLdsRun whole rows from row
+//     (1024 / kLdsRun) * g on, g = 4i + w (A: plane 0's rows, then plane 1's).
 //   - Per stage: wait for its loads, barrier (the slot of stage s - 1 is then
-//     free), issue stage s + kLdsDepth - 1 into that slot, then 8 MFMAs per
-//     active m-tile, lane (fr, fc) using piece 4q + fc of its A row and its W
-//     row for MFMA q.
-// Rows past the block's last are clamped (their data is never used); m-tiles
-// past it issue no MFMA.  Sum order is fixed per block (bitwise repeatable).
+//     free), issue stage s + kLdsDepth - 1 into that slot, then the MFMAs of
+//     the active m-tiles (one per plane), lane (fr, fc) using piece 4q + fc of
+//     its A row and its W row for MFMA q.
 //   - Persistent over column blocks: block x streams the `cpb` column blocks
 //     x*cpb .. of its expert one after the other (the host sizes the grid to
 //     one block per CU), and the stage sequence runs on across their
@@ -947,35 +945,47 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(
 //     in the loop would share the vmcnt counter with the DMA loads without
 //     completing in order with them, and the loop's wait counts assume
 //     loads only.
+//   - Row groups: in the second product the block takes every group of 16*NMT
+//     rows of its expert in turn (a new stage sequence each; between two, the
+//     stores drain and the ring restarts); in the first, only group
+//     blockIdx.z / splits.
+//     The second product uses 16-row groups (both planes of a 32-row group and
+//     three stages would not fit in the LDS), so an expert with more rows
+//     streams its weights once per group.
+// Rows past the group's last are clamped (their data is never used); m-tiles
+// past it issue no MFMA.  Sum order is fixed per block (bitwise repeatable).
 // ---------------------------------------------------------------------------
 constexpr int kLdsRun = 512;                   // bytes of each row per stage
 constexpr int kLdsStageK = kLdsRun / 2;        // bf16 elements per stage
 constexpr int kLdsDepth = 3;
 constexpr int kLdsMaxCpb = 8;                  // column blocks per block, at most
 
-template <bool SPLIT, int NMT>
+template <bool UP, bool SPLIT, int NMT>
 __global__ __launch_bounds__(256) void ffn_stream_lds_kernel(
-    const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets,
-    const uint16_t* __restrict__ W, const uint16_t* __restrict__ bias, void* __restrict__ out,
-    size_t out_plane, int E, int N, int K, int splits, float* __restrict__ partial, int rows_cap,
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ A_lo,
+    const int32_t* __restrict__ offsets, const uint16_t* __restrict__ W,
+    const uint16_t* __restrict__ bias, void* __restrict__ out, size_t out_plane, int E, int N,
+    int K, int splits, float* __restrict__ partial, int rows_cap,
     const int32_t* __restrict__ gather, int gather_k, int cpb) {
+  constexpr int kPlanes = (SPLIT && !UP) ? 2 : 1;
+  constexpr bool kLoopGroups = !UP;              // the second product loops over row groups
   constexpr int kMR = 16 * NMT;
   constexpr int kWBytes = 64 * kLdsRun;          // W part of a stage: 32 KB
-  constexpr int kABytes = kMR * kLdsRun;         // A part: 8 KB per m-tile
+  constexpr int kAPlane = kMR * kLdsRun;         // A part: 8 KB per m-tile and plane
+  constexpr int kABytes = kPlanes * kAPlane;
   constexpr int kWI = kWBytes / 4096;            // 1 KB DMA instructions per wave per stage
   constexpr int kAI = kABytes / 4096;
   constexpr int kPieces = kLdsRun / 16;
-  static_assert(kWI * 4096 == kWBytes && kAI * 4096 == kABytes && kLdsRun <= 1024 &&
-                kPieces >= 16, "DMA plan");
+  static_assert(kWI * 4096 == kWBytes && kAI * 4096 == kABytes && kAPlane % 1024 == 0 &&
+                kLdsRun <= 1024 && kPieces >= 16, "DMA plan");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsDepth * (kWBytes + kABytes)];
 
   const int e = blockIdx.y;
   const int split = blockIdx.z % splits;
   const int seg0 = offsets[e], seg1 = offsets[e + 1];
-  const int r0 = seg0 + (blockIdx.z / splits) * kMR;
-  if (r0 >= seg1) return;
-  const int r1 = min(seg1, r0 + kMR);
-  const int mt_active = (r1 - r0 + 15) >> 4;
+  const int g0 = kLoopGroups ? 0 : blockIdx.z / splits;
+  const int g1 = kLoopGroups ? (seg1 - seg0 + kMR - 1) / kMR : g0 + 1;
+  if (seg0 + g0 * kMR >= seg1) return;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -985,8 +995,8 @@ __global__ __launch_bounds__(256) void ffn_stream_lds_kernel(
   if (ncb <= 0) return;
 
   // DMA plan (see above): with R = 1024 / kLdsRun rows per instruction, lane L
-  // of instruction i writes physical piece L % kPieces of row R*g + L / kPieces,
-  // i.e. loads logical piece (L % kPieces) ^ (row & 15).
+  // of instruction i writes physical piece L % kPieces of row R*g + L / kPieces
+  // of its part, i.e. loads logical piece (L % kPieces) ^ (row & 15).
   constexpr int kRowsPerInst = 1024 / kLdsRun;
   auto plan_row = [&](int i) { return kRowsPerInst * (i * 4 + wave) + lane / kPieces; };
   const int piece = lane % kPieces;
@@ -996,118 +1006,140 @@ __global__ __launch_bounds__(256) void ffn_stream_lds_kernel(
     const int row = plan_row(i);
     w_off[i] = (uint32_t)(((size_t)row * K + (piece ^ (row & 15)) * 8) * 2);
   }
-  int arow[kAI];
-#pragma unroll
-  for (int i = 0; i < kAI; ++i) arow[i] = min(r0 + plan_row(i), r1 - 1);
-  a_rows<kAI>(gather, gather_k, arow);
-  const uint16_t* a_src[kAI];
-#pragma unroll
-  for (int i = 0; i < kAI; ++i)
-    a_src[i] = A + (size_t)arow[i] * K + ((piece ^ (plan_row(i) & 15)) * 8);
   const uint16_t* w_base = W + ((size_t)e * N + (size_t)cb0 * 64) * K;
-
-  f32x4 acc[kLdsMaxCpb][NMT];
-#pragma unroll
-  for (int j = 0; j < kLdsMaxCpb; ++j)
-#pragma unroll
-    for (int i = 0; i < NMT; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nst_all = K / kLdsStageK;
   const int s0 = (int)((long)split * nst_all / splits);
   const int nst = (int)((long)(split + 1) * nst_all / splits) - s0;
+  const int total = ncb * nst;
   const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
-  // Stage t of the block's sequence: column block t / nst, k stage t % nst.
-  auto issue = [&](int slot, int t) {
-    const int j = t / nst, st = t - j * nst;
-    const int k0 = (s0 + st) * kLdsStageK;
-    const uint32_t wl = lds0 + slot * kWBytes, al = lds0 + kLdsDepth * kWBytes + slot * kABytes;
-#pragma unroll
-    for (int i = 0; i < kAI; ++i) load_lds16_raw(a_src[i] + k0, al + (i * 4 + wave) * 1024);
-    const uint16_t* wb = w_base + (size_t)j * 64 * K + k0;
-#pragma unroll
-    for (int i = 0; i < kWI; ++i) load_lds16_sv(wb, w_off[i], wl + (i * 4 + wave) * 1024);
-  };
-  // Every fragment read of the stage is issued before its MFMAs; the active
-  // m-tile count picks one of two unrolled bodies (a uniform branch).
-  constexpr int kQ = kPieces / 4;                // MFMAs per m-tile per stage
-  auto compute = [&](int slot, f32x4 (&acc_j)[NMT]) {
-    const uint8_t* ws = lds + slot * kWBytes;
-    const uint8_t* as = lds + kLdsDepth * kWBytes + slot * kABytes;
-    const int wrow = wave * 16 + fr;
-    u32x4 wf[kQ];
-#pragma unroll
-    for (int q = 0; q < kQ; ++q) wf[q] = ld16(ws + wrow * kLdsRun + (((q * 4 + fc) ^ (wrow & 15)) << 4));
-    auto tiles = [&](auto mt_c) {
-      constexpr int MT = decltype(mt_c)::value;
-      u32x4 af[MT][kQ];
-#pragma unroll
-      for (int i = 0; i < MT; ++i) {
-        const int row = i * 16 + fr;
-#pragma unroll
-        for (int q = 0; q < kQ; ++q) af[i][q] = ld16(as + row * kLdsRun + (((q * 4 + fc) ^ (row & 15)) << 4));
-      }
-#pragma unroll
-      for (int q = 0; q < kQ; ++q)
-#pragma unroll
-        for (int i = 0; i < MT; ++i) acc_j[i] = mfma_bf16(af[i][q], wf[q], acc_j[i]);
-    };
-    if (NMT == 1 || mt_active == 1) tiles(std::integral_constant<int, 1>{});
-    else tiles(std::integral_constant<int, NMT>{});
-  };
-
+  constexpr int kQ = kPieces / 4;                // MFMAs per m-tile and plane per stage
   // Loads complete in issue order: in steady state kLdsDepth - 2 stages were
   // issued after stage t, so waiting for at most that many instructions lands
-  // it; near the end (fewer issued after it) wait for all.  The column-block
-  // loop is unrolled so that each one's accumulators stay in registers.
+  // it; near the end (fewer issued after it) wait for all.
   constexpr int kSteadyWait = (kLdsDepth - 2) * (kWI + kAI);
-  const int total = ncb * nst;
-#pragma unroll
-  for (int d = 0; d < kLdsDepth - 1; ++d)
-    if (d < total) issue(d, d);
-#pragma unroll
-  for (int j = 0; j < kLdsMaxCpb; ++j) {
-    if (j < ncb) {
-      for (int st = 0; st < nst; ++st) {
-        const int t = j * nst + st;
-        if (t + kLdsDepth - 2 < total) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kSteadyWait));
-        else __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
-        __syncthreads();
-        if (t + kLdsDepth - 1 < total) issue((t + kLdsDepth - 1) % kLdsDepth, t + kLdsDepth - 1);
-        compute(t % kLdsDepth, acc[j]);
-      }
-    }
-  }
 
-  // Epilogue, as ffn_stream_kernel's, per column block: lane (fr, fc) holds
-  // column 64 * (cb0 + j) + 16 * wave + fr of rows 4fc + v of each m-tile.  The
-  // bias words of every column block are loaded first (clamped indices, one
-  // wait), not one load and wait per column block behind the stores.
-  float bvs[kLdsMaxCpb];
+  for (int g = g0; g < g1; ++g) {
+    const int r0 = seg0 + g * kMR;
+    const int r1 = min(seg1, r0 + kMR);
+    const int mt_active = (r1 - r0 + 15) >> 4;
+    if (g > g0) {
+      // The previous group's stores drain before this group's loads are
+      // counted, and every wave is past its last LDS read before the ring
+      // is reused.
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+      __syncthreads();
+    }
+    // A plan: instruction i covers plane (row' / kMR), row row' % kMR.
+    int arow[kAI];
 #pragma unroll
-  for (int j = 0; j < kLdsMaxCpb; ++j) bvs[j] = 0.f;
-  if (bias && split == 0) {
-    uint16_t braw[kLdsMaxCpb];
+    for (int i = 0; i < kAI; ++i) arow[i] = min(r0 + plan_row(i) % kMR, r1 - 1);
+    if constexpr (UP) a_rows<kAI>(gather, gather_k, arow);
+    const uint16_t* a_src[kAI];
+#pragma unroll
+    for (int i = 0; i < kAI; ++i) {
+      const int pr = plan_row(i);
+      const uint16_t* base = (kPlanes == 2 && pr >= kMR) ? A_lo : A;
+      a_src[i] = base + (size_t)arow[i] * K + ((piece ^ ((pr % kMR) & 15)) * 8);
+    }
+
+    // Stage t of the group's sequence: column block t / nst, k stage t % nst.
+    auto issue = [&](int slot, int t) {
+      const int j = t / nst, st = t - j * nst;
+      const int k0 = (s0 + st) * kLdsStageK;
+      const uint32_t wl = lds0 + slot * kWBytes, al = lds0 + kLdsDepth * kWBytes + slot * kABytes;
+#pragma unroll
+      for (int i = 0; i < kAI; ++i) load_lds16_raw(a_src[i] + k0, al + (i * 4 + wave) * 1024);
+      const uint16_t* wb = w_base + (size_t)j * 64 * K + k0;
+#pragma unroll
+      for (int i = 0; i < kWI; ++i) load_lds16_sv(wb, w_off[i], wl + (i * 4 + wave) * 1024);
+    };
+    // Every fragment read of the stage is issued before its MFMAs; the active
+    // m-tile count picks one of two unrolled bodies (a uniform branch).
+    auto compute = [&](int slot, f32x4 (&acc_j)[NMT]) {
+      const uint8_t* ws = lds + slot * kWBytes;
+      const uint8_t* as = lds + kLdsDepth * kWBytes + slot * kABytes;
+      const int wrow = wave * 16 + fr;
+      u32x4 wf[kQ];
+#pragma unroll
+      for (int q = 0; q < kQ; ++q) wf[q] = ld16(ws + wrow * kLdsRun + (((q * 4 + fc) ^ (wrow & 15)) << 4));
+      auto tiles = [&](auto mt_c) {
+        constexpr int MT = decltype(mt_c)::value;
+        u32x4 af[kPlanes][MT][kQ];
+#pragma unroll
+        for (int p = 0; p < kPlanes; ++p)
+#pragma unroll
+          for (int i = 0; i < MT; ++i) {
+            const int row = i * 16 + fr;
+#pragma unroll
+            for (int q = 0; q < kQ; ++q)
+              af[p][i][q] = ld16(as + p * kAPlane + row * kLdsRun + (((q * 4 + fc) ^ (row & 15)) << 4));
+          }
+#pragma unroll
+        for (int q = 0; q < kQ; ++q)
+#pragma unroll
+          for (int i = 0; i < MT; ++i)
+#pragma unroll
+            for (int p = 0; p < kPlanes; ++p) acc_j[i] = mfma_bf16(af[p][i][q], wf[q], acc_j[i]);
+      };
+      if (NMT == 1 || mt_active == 1) tiles(std::integral_constant<int, 1>{});
+      else tiles(std::integral_constant<int, NMT>{});
+    };
+
+    // The column-block loop is unrolled so that each one's accumulators stay
+    // in registers.
+    f32x4 acc[kLdsMaxCpb][NMT];
 #pragma unroll
     for (int j = 0; j < kLdsMaxCpb; ++j)
-      braw[j] = bias[(size_t)e * N + (cb0 + min(j, ncb - 1)) * 64 + wave * 16 + fr];
 #pragma unroll
-    for (int j = 0; j < kLdsMaxCpb; ++j) bvs[j] = bf16_to_f32(braw[j]);
-  }
+      for (int i = 0; i < NMT; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int j = 0; j < kLdsMaxCpb; ++j) {
-    if (j < ncb) {
-      const int col = (cb0 + j) * 64 + wave * 16 + fr;
-      const float bv = bvs[j];
+    for (int d = 0; d < kLdsDepth - 1; ++d)
+      if (d < total) issue(d, d);
 #pragma unroll
-      for (int i = 0; i < NMT; ++i) {
+    for (int j = 0; j < kLdsMaxCpb; ++j) {
+      if (j < ncb) {
+        for (int st = 0; st < nst; ++st) {
+          const int t = j * nst + st;
+          if (t + kLdsDepth - 2 < total) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kSteadyWait));
+          else __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+          __syncthreads();
+          if (t + kLdsDepth - 1 < total) issue((t + kLdsDepth - 1) % kLdsDepth, t + kLdsDepth - 1);
+          compute(t % kLdsDepth, acc[j]);
+        }
+      }
+    }
+
+    // Epilogue, as ffn_stream_kernel's, per column block: lane (fr, fc) holds
+    // column 64 * (cb0 + j) + 16 * wave + fr of rows 4fc + v of each m-tile.
+    // The bias words of every column block are loaded first (clamped indices,
+    // one wait), not one load and wait per column block behind the stores.
+    float bvs[kLdsMaxCpb];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int row = r0 + i * 16 + 4 * fc + v;
-          if (row < r1) {
-            if (splits > 1)
-              partial[((size_t)split * rows_cap + row) * N + col] = acc[j][i][v] + bv;
-            else
-              emit<uint16_t, true, SPLIT>(out, out_plane, (size_t)row * N + col, acc[j][i][v] + bv);
+    for (int j = 0; j < kLdsMaxCpb; ++j) bvs[j] = 0.f;
+    if (bias && split == 0) {
+      uint16_t braw[kLdsMaxCpb];
+#pragma unroll
+      for (int j = 0; j < kLdsMaxCpb; ++j)
+        braw[j] = bias[(size_t)e * N + (cb0 + min(j, ncb - 1)) * 64 + wave * 16 + fr];
+#pragma unroll
+      for (int j = 0; j < kLdsMaxCpb; ++j) bvs[j] = bf16_to_f32(braw[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < kLdsMaxCpb; ++j) {
+      if (j < ncb) {
+        const int col = (cb0 + j) * 64 + wave * 16 + fr;
+#pragma unroll
+        for (int i = 0; i < NMT; ++i) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int row = r0 + i * 16 + 4 * fc + v;
+            if (row < r1) {
+              if (splits > 1)
+                partial[((size_t)split * rows_cap + row) * N + col] = acc[j][i][v] + bvs[j];
+              else
+                emit<uint16_t, UP, SPLIT>(out, out_plane, (size_t)row * N + col, acc[j][i][v] + bvs[j]);
+            }
           }
         }
       }
@@ -1138,7 +1170,7 @@ __global__ __launch_bounds__(256) void ffn_splitk_reduce(
 // descriptor alone (never from device data).
 struct StreamShape {
   int nmt, nwn, groups, splits;
-  bool lds;   // ffn_stream_lds_kernel (bf16 first product, at most 32 rows per block)
+  bool lds;   // ffn_stream_lds_kernel (bf16, at most 32 rows per expert)
 };
 static StreamShape stream_shape(bool bf16, bool up, bool split, int E, int N, int K,
                                 int max_rows_per_expert) {
@@ -1149,7 +1181,13 @@ static StreamShape stream_shape(bool bf16, bool up, bool split, int E, int N, in
   const int bound = max_rows_per_expert;
   sh.nmt = bound <= 16 ? 1 : bound <= 32 ? 2 : bound <= 64 ? 4 : 10;
   sh.groups = (bound + 16 * sh.nmt - 1) / (16 * sh.nmt);
-  sh.lds = bf16 && up && sh.nmt <= 2 && K % kLdsStageK == 0 && N % 64 == 0;
+  // bf16 layers with at most 32 rows per expert stream through LDS; the
+  // second product there takes 16-row groups, looped inside the block.
+  sh.lds = bf16 && bound <= 32 && K % kLdsStageK == 0 && N % 64 == 0;
+  if (sh.lds && !up) {
+    sh.nmt = 1;
+    sh.groups = 1;
+  }
   sh.nwn = (!sh.lds && sh.nmt < 10 && (long)E * (N / 128) >= 1024) ? 2 : 1;
   // Split the k range when the grid is too small to keep enough weight loads
   // in flight (fewer than kStreamMinBlocks / 2 blocks), up to about
@@ -1160,8 +1198,14 @@ static StreamShape stream_shape(bool bf16, bool up, bool split, int E, int N, in
   const long blocks = (long)(N / (64 * sh.nwn)) * E * sh.groups;
   const int max_splits = std::max(1, std::min(8, K / chunk / 8));
   sh.splits = 1;
-  if (blocks < kStreamMinBlocks / 2)
+  if (sh.lds) {
+    // One persistent block per CU: split only when there are fewer column
+    // blocks than CUs.
+    const long cus = kXcds * kCusPerXcd;
+    if (blocks < cus) sh.splits = (int)std::min<long>(max_splits, (cus + blocks - 1) / blocks);
+  } else if (blocks < kStreamMinBlocks / 2) {
     while (sh.splits < max_splits && blocks * sh.splits < kStreamMinBlocks) ++sh.splits;
+  }
   return sh;
 }
 
@@ -1197,7 +1241,7 @@ static void launch_stream_nmt(const FfnArgs& a, const StreamShape& sh, hipStream
   }
 }
 
-template <bool SPLIT, int NMT>
+template <bool UP, bool SPLIT, int NMT>
 static void launch_stream_lds(const FfnArgs& a, const StreamShape& sh, hipStream_t s) {
   // One block per CU: each block streams cpb column blocks of its expert, cpb
   // the smallest that brings the grid down to one block per CU (at most
@@ -1206,13 +1250,14 @@ static void launch_stream_lds(const FfnArgs& a, const StreamShape& sh, hipStream
   const int cpb = (int)std::min<long>(kLdsMaxCpb, std::max<long>(1, (cbs + kXcds * kCusPerXcd - 1) /
                                                                        (kXcds * kCusPerXcd)));
   const dim3 grid((a.N / 64 + cpb - 1) / cpb, a.E, sh.groups * sh.splits);
-  ffn_stream_lds_kernel<SPLIT, NMT><<<grid, 256, 0, s>>>(
-      static_cast<const uint16_t*>(a.a), a.offsets, static_cast<const uint16_t*>(a.w),
+  const uint16_t* A = static_cast<const uint16_t*>(a.a);
+  ffn_stream_lds_kernel<UP, SPLIT, NMT><<<grid, 256, 0, s>>>(
+      A, (SPLIT && !UP) ? A + a.plane : nullptr, a.offsets, static_cast<const uint16_t*>(a.w),
       static_cast<const uint16_t*>(a.bias), a.out, a.plane, a.E, a.N, a.K, sh.splits, a.partial,
       a.max_rows, a.gather, a.gather_k, cpb);
-  if (sh.splits > 1) {
+  if (sh.splits > 1 && !(a.defer_reduce && !UP)) {
     const size_t quads = (size_t)a.max_rows * (a.N / 4);
-    ffn_splitk_reduce<uint16_t, true, SPLIT><<<(unsigned)((quads + 255) / 256), 256, 0, s>>>(
+    ffn_splitk_reduce<uint16_t, UP, SPLIT><<<(unsigned)((quads + 255) / 256), 256, 0, s>>>(
         a.partial, a.offsets, a.E, a.N, sh.splits, a.max_rows, a.out, a.plane);
   }
 }
@@ -1220,10 +1265,14 @@ static void launch_stream_lds(const FfnArgs& a, const StreamShape& sh, hipStream
 template <typename T, bool UP, bool SPLIT>
 static void launch_stream(const FfnArgs& a, hipStream_t s) {
   const StreamShape sh = stream_shape(a.bf16, UP, SPLIT, a.E, a.N, a.K, a.max_rows_per_expert);
-  if constexpr (std::is_same<T, uint16_t>::value && UP) {
+  if constexpr (std::is_same<T, uint16_t>::value) {
     if (sh.lds) {
-      if (sh.nmt == 1) launch_stream_lds<SPLIT, 1>(a, sh, s);
-      else launch_stream_lds<SPLIT, 2>(a, sh, s);
+      if constexpr (UP) {
+        if (sh.nmt == 1) launch_stream_lds<UP, SPLIT, 1>(a, sh, s);
+        else launch_stream_lds<UP, SPLIT, 2>(a, sh, s);
+      } else {
+        launch_stream_lds<UP, SPLIT, 1>(a, sh, s);
+      }
       return;
     }
   }
