@@ -19,9 +19,9 @@
 //     registers in the MFMA operand layout, while the block's (at most
 //     16*NMT) rows of A are staged through LDS once per k-chunk and shared by
 //     the four waves.  Weight bytes are read once.
-//   * ffn_stream_lds_kernel -- the same blocks for a bf16 first product with at
-//     most 32 rows per block, both operands staged through LDS by DMA in whole
-//     512 B runs of each row.
+//   * ffn_stream_lds_kernel -- the same blocks for bf16 layers with at most 32
+//     rows per expert, both operands staged through LDS by DMA in whole 512 B
+//     runs of each row, one persistent block per CU.
 // The first product applies bias + exact-erf GELU in its epilogue and stores
 // dtype h; the second adds its bias and stores fp32 o.
 #include <algorithm>
