@@ -205,7 +205,7 @@ size_t elem_bytes(const moe_desc* d) { return d->dtype == MOE_DTYPE_BF16 ? 2 : 4
 
 // Workspace carving: every region starts on a 256-byte boundary.
 struct Layout {
-  size_t part_psum, part_top1, part_z, blk_hist, blk_base;
+  size_t part_psum, part_top1, part_z, part_logit, blk_hist, blk_base;
   size_t topk_idx, topk_w, counts, offsets, dest, src, top1, prob_mean;
   size_t h, o, partial;
   size_t sh_offsets, h_sh, o_sh;   // shared expert (d_ff_shared > 0)
@@ -219,12 +219,14 @@ Layout layout_of(const moe_desc* d) {
   Layout L{};
   const size_t T = d->tokens, E = d->n_experts, k = d->top_k, A = T * k;
   const size_t rb = moe::router_blocks(d->tokens), pb = moe::permute_blocks((int)A);
-  const size_t s = elem_bytes(d);
   size_t p = 0;
   auto take = [&](size_t bytes) { size_t at = p; p += up256(bytes); return at; };
   L.part_psum = take(rb * E * sizeof(double));
   L.part_top1 = take(rb * E * sizeof(int32_t));
   L.part_z = take(rb * sizeof(double));
+  L.part_logit = take(moe::router_small_part_bytes(d->tokens, d->d_model, d->n_experts,
+                                                   d->dtype == MOE_DTYPE_BF16,
+                                                   d->capacity_policy == MOE_CAPACITY_REROUTE));
   L.blk_hist = take(pb * E * sizeof(int32_t));
   L.blk_base = take(pb * E * sizeof(int32_t));
   L.topk_idx = take(A * 4);
@@ -428,6 +430,7 @@ int launch_route(const moe_desc* d, const void* x, const moe_weights* w, int32_t
   a.part_psum = at<double>(ws, L.part_psum);
   a.part_top1 = at<int32_t>(ws, L.part_top1);
   a.part_z = at<double>(ws, L.part_z);
+  a.part_logit = at<float>(ws, L.part_logit);
   a.top1_count = top1;
   a.prob_mean = pmean;
   a.aux = aux;

@@ -982,11 +982,6 @@ __global__ __launch_bounds__(256) void ffn_stream_lds_kernel(
 
   const int e = blockIdx.y;
   const int split = blockIdx.z % splits;
-  const int seg0 = offsets[e], seg1 = offsets[e + 1];
-  const int g0 = kLoopGroups ? 0 : blockIdx.z / splits;
-  const int g1 = kLoopGroups ? (seg1 - seg0 + kMR - 1) / kMR : g0 + 1;
-  if (seg0 + g0 * kMR >= seg1) return;
-
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int fr = lane & 15, fc = lane >> 4;
@@ -1013,6 +1008,32 @@ __global__ __launch_bounds__(256) void ffn_stream_lds_kernel(
   const int nst = (int)((long)(split + 1) * nst_all / splits) - s0;
   const int total = ncb * nst;
   const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
+
+  // The W part of stage t of a group's sequence: column block t / nst, k stage
+  // t % nst.  It depends on the block index only, so the first group's first
+  // kLdsDepth - 1 W stages are issued before the routing is read: their latency
+  // overlaps the dependent loads of the offsets and gathered row indices.  A
+  // block whose expert turns out to have no rows here has read those stages
+  // (at most 64 KB) for nothing, and waits for them before it exits.
+  auto issue_w = [&](int slot, int t) {
+    const int j = t / nst, st = t - j * nst;
+    const int k0 = (s0 + st) * kLdsStageK;
+    const uint32_t wl = lds0 + slot * kWBytes;
+    const uint16_t* wb = w_base + (size_t)j * 64 * K + k0;
+#pragma unroll
+    for (int i = 0; i < kWI; ++i) load_lds16_sv(wb, w_off[i], wl + (i * 4 + wave) * 1024);
+  };
+#pragma unroll
+  for (int d = 0; d < kLdsDepth - 1; ++d)
+    if (d < total) issue_w(d, d);
+
+  const int seg0 = offsets[e], seg1 = offsets[e + 1];
+  const int g0 = kLoopGroups ? 0 : blockIdx.z / splits;
+  const int g1 = kLoopGroups ? (seg1 - seg0 + kMR - 1) / kMR : g0 + 1;
+  if (seg0 + g0 * kMR >= seg1) {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));   // no DMA into LDS outlives the block
+    return;
+  }
   constexpr int kQ = kPieces / 4;                // MFMAs per m-tile and plane per stage
   // Loads complete in issue order: in steady state kLdsDepth - 2 stages were
   // issued after stage t, so waiting for at most that many instructions lands
@@ -1043,16 +1064,17 @@ __global__ __launch_bounds__(256) void ffn_stream_lds_kernel(
       a_src[i] = base + (size_t)arow[i] * K + ((piece ^ ((pr % kMR) & 15)) * 8);
     }
 
-    // Stage t of the group's sequence: column block t / nst, k stage t % nst.
-    auto issue = [&](int slot, int t) {
-      const int j = t / nst, st = t - j * nst;
+    // Stage t of the group's sequence: its A part, then its W part.
+    auto issue_a = [&](int slot, int t) {
+      const int st = t - (t / nst) * nst;
       const int k0 = (s0 + st) * kLdsStageK;
-      const uint32_t wl = lds0 + slot * kWBytes, al = lds0 + kLdsDepth * kWBytes + slot * kABytes;
+      const uint32_t al = lds0 + kLdsDepth * kWBytes + slot * kABytes;
 #pragma unroll
       for (int i = 0; i < kAI; ++i) load_lds16_raw(a_src[i] + k0, al + (i * 4 + wave) * 1024);
-      const uint16_t* wb = w_base + (size_t)j * 64 * K + k0;
-#pragma unroll
-      for (int i = 0; i < kWI; ++i) load_lds16_sv(wb, w_off[i], wl + (i * 4 + wave) * 1024);
+    };
+    auto issue = [&](int slot, int t) {
+      issue_a(slot, t);
+      issue_w(slot, t);
     };
     // Every fragment read of the stage is issued before its MFMAs; the active
     // m-tile count picks one of two unrolled bodies (a uniform branch).
@@ -1093,16 +1115,28 @@ __global__ __launch_bounds__(256) void ffn_stream_lds_kernel(
     for (int j = 0; j < kLdsMaxCpb; ++j)
 #pragma unroll
       for (int i = 0; i < NMT; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // Prologue.  First group: the W parts are in flight already, so the issue
+    // order is W0 W1 A0 A1 and stage 0 has landed once at most A1's kAI
+    // instructions are outstanding.  Later groups: A0 W0 A1 W1, as in the loop.
+    const bool w_early = g == g0;
 #pragma unroll
-    for (int d = 0; d < kLdsDepth - 1; ++d)
-      if (d < total) issue(d, d);
+    for (int d = 0; d < kLdsDepth - 1; ++d) {
+      if (d < total) {
+        if (w_early) issue_a(d, d);
+        else issue(d, d);
+      }
+    }
 #pragma unroll
     for (int j = 0; j < kLdsMaxCpb; ++j) {
       if (j < ncb) {
         for (int st = 0; st < nst; ++st) {
           const int t = j * nst + st;
-          if (t + kLdsDepth - 2 < total) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kSteadyWait));
-          else __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+          if (t + kLdsDepth - 2 < total) {
+            if (t == 0 && w_early) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0((kLdsDepth - 2) * kAI));
+            else __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kSteadyWait));
+          } else {
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+          }
           __syncthreads();
           if (t + kLdsDepth - 1 < total) issue((t + kLdsDepth - 1) % kLdsDepth, t + kLdsDepth - 1);
           compute(t % kLdsDepth, acc[j]);

@@ -18,6 +18,7 @@ struct RouterArgs {
   double* part_psum;       // [router_blocks(T)][E]
   int32_t* part_top1;      // [router_blocks(T)][E]
   double* part_z;          // [router_blocks(T)]
+  float* part_logit;       // router_small_part_bytes(): partial logit tiles of small batches
   int32_t* top1_count;     // optional
   float* prob_mean;        // optional
   float* aux;              // optional
@@ -39,6 +40,8 @@ struct RouterArgs {
 // Whether RouterArgs::perm may be used for T*k assignments.
 bool router_can_permute(int assignments);
 int router_blocks(int T);
+// Bytes of RouterArgs::part_logit a router launch needs (0 when its path uses none).
+size_t router_small_part_bytes(int T, int d, int E, bool bf16, bool rr);
 // Blocks (partial-sum rows) a router launch for T tokens and E experts uses.
 int router_launch_blocks(int T, int E);
 hipError_t launch_router(const RouterArgs& a, hipStream_t s);

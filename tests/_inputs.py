@@ -68,6 +68,12 @@ SMALL = {
                                      "bf16", capacity_policy="reroute"),
     "batch64_top1_bf16": Workload("batch64_top1_bf16", 64, 384, 640, 16, 1, False, 0, False,
                                   "bf16"),
+    # the small-batch router (64 tokens at most) with many experts and slots, a router
+    # bias and a selection bias: 64 experts top-6 (bf16), 24 experts top-3 (fp32)
+    "batch20_fine_bias_bf16": Workload("batch20_fine_bias_bf16", 20, 256, 256, 64, 6, True, 0,
+                                       True, "bf16", router_bias=True, selection_bias=True),
+    "batch57_e24_k3_fp32": Workload("batch57_e24_k3_fp32", 57, 128, 256, 24, 3, True, 0, True,
+                                    "f32", selection_bias=True),
     # every token's first choice is one expert (a logit bias of +6 on it): that expert's
     # segment holds all T rows -- the longest run of m-tiles the tile schedule sees --
     # on the stream path (fp32), the 128-row tiled path (top-1) and the 256-row tiled
