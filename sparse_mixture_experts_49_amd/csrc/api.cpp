@@ -130,9 +130,11 @@ struct Plan {
 
 // AUTO: bf16 layers averaging >= 64 rows per expert (by the host's bound) run
 // the LDS-tiled kernel, the rest stream the weights.  h is one bf16 plane on
-// the tiled path at >= 256 rows per expert (MFMA-bound prefill) and two planes
-// below that, where the products are weight-bound and the second plane's
-// MFMAs and bytes cost little.
+// the tiled path at >= 256 rows per expert (MFMA-bound prefill) and on the
+// weight-streaming path when no expert can hold more than 32 rows (decode:
+// there the second plane's DMA costs ~2% of the second product, measured on
+// MI355X), and two planes in between.  Top-1 layers without renormalisation
+// always keep two planes (bf16 h alone misses the bar there).
 int resolve(const moe_desc* d, Plan& p) {
   const bool bf16 = d->dtype == MOE_DTYPE_BF16;
   const double avg = (double)max_rows(d) / d->n_experts;
@@ -144,9 +146,10 @@ int resolve(const moe_desc* d, Plan& p) {
     return MOE_OK;
   }
   p.h_mode = d->h_mode;
-  if (p.h_mode == MOE_H_AUTO)
-    p.h_mode = (p.path == MOE_FFN_TILED && avg >= 256.0 && renormalised_or_multi(d)) ? MOE_H_BF16
-                                                                                    : MOE_H_SPLIT;
+  if (p.h_mode == MOE_H_AUTO) {
+    const bool one_plane = p.path == MOE_FFN_TILED ? avg >= 256.0 : row_bound(d) <= 32;
+    p.h_mode = (one_plane && renormalised_or_multi(d)) ? MOE_H_BF16 : MOE_H_SPLIT;
+  }
   p.h_elem = p.h_mode == MOE_H_SPLIT ? 4 : 2;
   return MOE_OK;
 }

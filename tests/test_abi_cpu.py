@@ -141,14 +141,21 @@ def test_missing_library_fails_loudly(tmp_path):
 
 def test_plan_resolution_of_the_named_workloads():
     """AUTO: tiled kernel + bf16 h for prefill-sized layers, tiled kernel + split h for
-    medium ones (64..255 rows per expert), weight streaming + split h below; h_bytes
-    follows the mode."""
+    medium ones (64..255 rows per expert), weight streaming below: bf16 h when no
+    expert can hold more than 32 rows (decode), split h otherwise; h_bytes follows
+    the mode."""
     import synth
     want = {"toy_fp32": (B.MOE_FFN_STREAM, B.MOE_H_AUTO, 4),
             "mid_bf16": (B.MOE_FFN_TILED, B.MOE_H_BF16, 2),
             "mixtral_prefill_bf16": (B.MOE_FFN_TILED, B.MOE_H_BF16, 2),
             "switch_capacity_bf16": (B.MOE_FFN_TILED, B.MOE_H_SPLIT, 4),
-            "decode_bf16": (B.MOE_FFN_STREAM, B.MOE_H_SPLIT, 4)}
+            "decode_bf16": (B.MOE_FFN_STREAM, B.MOE_H_BF16, 2)}
+    streaming = {(32, 1, False): B.MOE_H_SPLIT,     # top-1 without renormalisation
+                 (48, 2, True): B.MOE_H_SPLIT,      # 48 rows per expert possible
+                 (32, 1, True): B.MOE_H_BF16}
+    for (T, k, renorm), hm in streaming.items():
+        p = moe.moe_query_plan(moe.Desc(T, 512, 1024, 8, k, renorm))
+        assert (p["ffn_path"], p["h_mode"]) == (B.MOE_FFN_STREAM, hm), (T, k, renorm)
     for name, (path, hm, eb) in want.items():
         s = synth.WORKLOADS[name]
         d = moe.Desc(s.tokens, s.d_model, s.d_ff, s.n_experts, s.top_k, s.renormalize,
