@@ -158,8 +158,19 @@ int resolve(const moe_desc* d, Plan& p) {
 // 256 rows and h is one bf16 plane (prefill, MFMA-bound), else 128.  Measured
 // on MI355X for the switch-style layer (64 experts, capacity 160), 128-row
 // tiles also beat 192-row ones when rerouting fills every expert to 160 rows.
-int tile_rows(bool split, int path_rows, int experts) {
-  return (!split && path_rows >= 256L * experts) ? 256 : 128;
+// A product whose 256-row tiles would not fill three rounds of the 256 CUs
+// takes 192-row tiles instead: there the last, partly idle round and each
+// expert's ragged last tile set the time, and shorter tiles cut both.  The
+// estimate counts about half a ragged tile per expert.  Measured on MI355X for
+// the mid-size layer (16 experts, 460-570 rows each): first product 121 -> 105
+// us (3 rounds of 192 rows instead of 3 of 256), second 90 -> 75 us (one round
+// of 192 tiles instead of one of 160); the fine-grained layer (4.9 and 6.3
+// rounds) kept 256 (within 5% either way), and 128-row tiles were slower on both.
+int tile_rows(bool split, int path_rows, int experts, int n) {
+  if (split || path_rows < 256L * experts) return 128;
+  const long mt = (path_rows + 255L) / 256 + experts / 2;
+  const long tiles = mt * ((n + 255L) / 256);
+  return tiles < 3L * 256 ? 192 : 256;
 }
 
 // The shared expert is one dense product over all T tokens: the LDS-tiled
@@ -525,7 +536,7 @@ int launch_one_ffn(const moe_desc* d, bool up, const void* in, const int32_t* of
   a.max_rows_per_expert = row_bound(d);
   a.max_rows = max_rows(d);
   a.path = plan.path;
-  a.tile_rows = tile_rows(a.split, a.max_rows, a.E);
+  a.tile_rows = tile_rows(a.split, a.max_rows, a.E, a.N);
   a.partial = at<float>(ws, L.partial);
   a.gather = gather;
   a.gather_k = d->top_k;

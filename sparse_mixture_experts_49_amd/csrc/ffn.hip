@@ -1377,13 +1377,17 @@ static void launch_tiled_bm(const FfnArgs& a, hipStream_t s) {
   else launch_tiled_t<UP, SPLIT, BM, 128>(a, s);
 }
 
-// Rows per tile (FfnArgs::tile_rows, chosen by the caller): 256 (one h plane
-// only) or 128, both run as 2 x 2 waves.
+// Rows per tile (FfnArgs::tile_rows, chosen by the caller): 256 or 192 (one
+// h plane only) or 128, all run as 2 x 2 waves.
 template <bool UP, bool SPLIT>
 static void launch_tiled(const FfnArgs& a, hipStream_t s) {
   if constexpr (!SPLIT) {
     if (a.tile_rows == 256) {
       launch_tiled_bm<UP, false, 256>(a, s);
+      return;
+    }
+    if (a.tile_rows == 192) {
+      launch_tiled_bm<UP, false, 192>(a, s);
       return;
     }
   }
