@@ -1359,8 +1359,11 @@ static void launch_tiled_t(const FfnArgs& a, hipStream_t s) {
   const uint16_t* B = static_cast<const uint16_t*>(a.bias);
   ffn_tiled_kernel<UP, SPLIT, BM, BN, WM, WS, OCC><<<per_xcd * kXcds, 256, 0, s>>>(
       A, A_lo, a.offsets, W, B, a.out, a.plane, a.E, a.N, a.K, a.partial, a.gather, a.gather_k);
-  ffn_tile_reduce<UP, SPLIT, BM, BN><<<kPartialSlots, 256, 0, s>>>(a.offsets, B, a.out, a.plane,
-                                                                   a.E, a.N, a.K, a.partial);
+  // Only a k range of at least kSplitMinSteps steps is ever split (tile_job);
+  // shorter ones need no reduce launch (measured: ~5 us per product).
+  if (a.K / kTBK >= kSplitMinSteps)
+    ffn_tile_reduce<UP, SPLIT, BM, BN><<<kPartialSlots, 256, 0, s>>>(a.offsets, B, a.out, a.plane,
+                                                                     a.E, a.N, a.K, a.partial);
 }
 
 // Column tile: 256 when N >= 256, else 128.  A 256-wide tile moves half the
