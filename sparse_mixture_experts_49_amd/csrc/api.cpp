@@ -1,6 +1,7 @@
 // C ABI of the MoE layer forward: argument validation, workspace carving and
 // the launch sequence.  Kernels live in router.hip, permute.hip, ffn.hip and
 // combine.hip.  No call allocates, frees or synchronises.
+#include <cmath>
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
@@ -158,19 +159,27 @@ int resolve(const moe_desc* d, Plan& p) {
 // 256 rows and h is one bf16 plane (prefill, MFMA-bound), else 128.  Measured
 // on MI355X for the switch-style layer (64 experts, capacity 160), 128-row
 // tiles also beat 192-row ones when rerouting fills every expert to 160 rows.
-// A product whose 256-row tiles would not fill three rounds of the 256 CUs
-// takes 192-row tiles instead: there the last, partly idle round and each
-// expert's ragged last tile set the time, and shorter tiles cut both.  The
-// estimate counts about half a ragged tile per expert.  Measured on MI355X for
-// the mid-size layer (16 experts, 460-570 rows each): first product 121 -> 105
-// us (3 rounds of 192 rows instead of 3 of 256), second 90 -> 75 us (one round
-// of 192 tiles instead of one of 160); the fine-grained layer (4.9 and 6.3
-// rounds) kept 256 (within 5% either way), and 128-row tiles were slower on both.
+// With one h plane the choice is between 256- and 192-row tiles, by the
+// estimated time of the product: rounds of the 256 CUs times the tile height,
+// a 192-row round costing 1.15x a 256-row one per row (measured on MI355X: the
+// mid-size layer's products ran 1.11-1.16x slower per row and round).  Tiles
+// per expert are estimated from the average rows per expert plus 10% for the
+// uneven loads of routed experts (exact for one expert, the shared one).  Where
+// the last round is partly idle or each expert's ragged last tile is a large
+// share, 192-row tiles win.  Measured for the mid-size layer (16 experts,
+// 460-570 rows each): first product 121 -> 105 us (3 rounds of 192 rows instead
+// of 3 of 256), second 90 -> 75 us (one round of 192 tiles instead of one of
+// 160); the prefill and fine-grained layers keep 256, and 128-row tiles were
+// slower on both.
 int tile_rows(bool split, int path_rows, int experts, int n) {
   if (split || path_rows < 256L * experts) return 128;
-  const long mt = (path_rows + 255L) / 256 + experts / 2;
-  const long tiles = mt * ((n + 255L) / 256);
-  return tiles < 3L * 256 ? 192 : 256;
+  const double per_expert = (double)path_rows / experts * (experts > 1 ? 1.1 : 1.0);
+  const long ntn = (n + 255L) / 256;
+  auto est = [&](int bm) {
+    const long tiles = (long)experts * (long)std::ceil(per_expert / bm) * ntn;
+    return (double)((tiles + 255) / 256) * bm * (bm == 256 ? 1.0 : 1.15);
+  };
+  return est(192) < est(256) ? 192 : 256;
 }
 
 // The shared expert is one dense product over all T tokens: the LDS-tiled
@@ -569,7 +578,6 @@ int launch_shared(const moe_desc* d, const void* x, const moe_weights* w, float*
   a.max_rows_per_expert = d->tokens;
   a.max_rows = d->tokens;
   a.path = sh.path;
-  a.tile_rows = a.split || d->tokens < 256 ? 128 : 256;
   a.partial = at<float>(ws, L.partial);
   void* h = at<void>(ws, L.h_sh);
   a.up = true;
@@ -579,6 +587,7 @@ int launch_shared(const moe_desc* d, const void* x, const moe_weights* w, float*
   a.out = h;
   a.N = d->d_ff_shared;
   a.K = d->d_model;
+  a.tile_rows = tile_rows(a.split, d->tokens, 1, a.N);
   if (int st = hip_status(moe::launch_ffn(a, s), "shared ffn up launch")) return st;
   a.up = false;
   a.a = h;
@@ -587,6 +596,7 @@ int launch_shared(const moe_desc* d, const void* x, const moe_weights* w, float*
   a.out = o_sh;
   a.N = d->d_model;
   a.K = d->d_ff_shared;
+  a.tile_rows = tile_rows(a.split, d->tokens, 1, a.N);
   return hip_status(moe::launch_ffn(a, s), "shared ffn down launch");
 }
 
