@@ -97,8 +97,9 @@ __device__ __forceinline__ f32x16 mfma32_bf16(u32x4 a, u32x4 b, f32x16 c) {
 // Abramowitz & Stegun, Handbook of Mathematical Functions, formula 7.1.26
 // (after Hastings): for a >= 0, erfc(a) ~= t P(t) exp(-a^2) with t = 1/(1 + p a)
 // and P a fourth-degree polynomial; |error| <= 1.5e-7.  With a = |z| / sqrt 2
-// and m = (z / 2) erfc(a):  GELU(z) = z - m for z >= 0 and m for z < 0
-// (1 + erf(-a) = erfc(a)), so there is no cancellation and GELU's absolute
+// and r = erfc(a) / 2:  GELU(z) = z - z r for z >= 0 and z r for z < 0
+// (1 + erf(-a) = erfc(a)), i.e. max(z, 0) - |z| r in both cases (one fused
+// multiply-add, no select), so there is no cancellation and GELU's absolute
 // error stays below ~1e-7 |z|.  The 1/sqrt 2 is folded into p, the 1/2 into
 // P's coefficients, and exp(-a^2) = exp2(-z^2 log2(e) / 2).
 __device__ __forceinline__ float gelu_erf(float z) {
@@ -112,8 +113,7 @@ __device__ __forceinline__ float gelu_erf(float z) {
   q = fmaf(q, t, c1);
   q *= t;
   const float e = __builtin_amdgcn_exp2f(z * z * -0.72134752044448170368f);
-  const float m = z * (q * e);
-  return z < 0.f ? m : z - m;
+  return fmaf(-fabsf(z), q * e, fmaxf(z, 0.f));
 }
 
 // Two fp32 values rounded to bf16 (nearest, ties to even) and packed, lo in
