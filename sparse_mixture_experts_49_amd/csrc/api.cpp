@@ -247,8 +247,7 @@ Layout layout_of(const moe_desc* d) {
   L.part_psum = take(rb * E * sizeof(double));
   L.part_top1 = take(rb * E * sizeof(int32_t));
   L.part_z = take(rb * sizeof(double));
-  L.part_logit = take(moe::router_small_part_bytes(d->tokens, d->d_model, d->n_experts,
-                                                   d->dtype == MOE_DTYPE_BF16,
+  L.part_logit = take(moe::router_small_part_bytes(d->tokens, d->n_experts,
                                                    d->capacity_policy == MOE_CAPACITY_REROUTE));
   L.blk_hist = take(pb * E * sizeof(int32_t));
   L.blk_base = take(pb * E * sizeof(int32_t));

@@ -41,7 +41,7 @@ struct RouterArgs {
 bool router_can_permute(int assignments);
 int router_blocks(int T);
 // Bytes of RouterArgs::part_logit a router launch needs (0 when its path uses none).
-size_t router_small_part_bytes(int T, int d, int E, bool bf16, bool rr);
+size_t router_small_part_bytes(int T, int E, bool rr);
 // Blocks (partial-sum rows) a router launch for T tokens and E experts uses.
 int router_launch_blocks(int T, int E);
 hipError_t launch_router(const RouterArgs& a, hipStream_t s);

@@ -576,7 +576,7 @@ static void small_split(int d, bool bf16, int& slices, int& cpc) {
   slices = (nch + cpc - 1) / cpc;
 }
 
-size_t router_small_part_bytes(int T, int d, int E, bool bf16, bool rr) {
+size_t router_small_part_bytes(int T, int E, bool rr) {
   if (!router_small(T, rr)) return 0;
   return (size_t)kSmallSlices * ((T + 15) / 16) * 16 * ((E + 15) / 16) * 16 * sizeof(float);
 }
