@@ -966,7 +966,7 @@ __global__ __launch_bounds__(256) void ffn_stream_lds_kernel(
     const int32_t* __restrict__ offsets, const uint16_t* __restrict__ W,
     const uint16_t* __restrict__ bias, void* __restrict__ out, size_t out_plane, int E, int N,
     int K, int splits, float* __restrict__ partial, int rows_cap,
-    const int32_t* __restrict__ gather, int gather_k, int cpb) {
+    const int32_t* __restrict__ gather, int gather_k, int cpb, int early) {
   constexpr int kPlanes = (SPLIT && !UP) ? 2 : 1;
   constexpr bool kLoopGroups = !UP;              // the second product loops over row groups
   constexpr int kMR = 16 * NMT;
@@ -1010,11 +1010,13 @@ __global__ __launch_bounds__(256) void ffn_stream_lds_kernel(
   const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
 
   // The W part of stage t of a group's sequence: column block t / nst, k stage
-  // t % nst.  It depends on the block index only, so the first group's first
-  // kLdsDepth - 1 W stages are issued before the routing is read: their latency
-  // overlaps the dependent loads of the offsets and gathered row indices.  A
-  // block whose expert turns out to have no rows here has read those stages
-  // (at most 64 KB) for nothing, and waits for them before it exits.
+  // t % nst.  It depends on the block index only, so with `early` (the host
+  // sets it when there are at least as many rows as experts, so few experts
+  // are empty) the first group's first kLdsDepth - 1 W stages are issued
+  // before the routing is read: their latency overlaps the dependent loads of
+  // the offsets and gathered row indices.  A block whose expert turns out to
+  // have no rows has then read those stages (at most 64 KB) for nothing, and
+  // waits for them before it exits.
   auto issue_w = [&](int slot, int t) {
     const int j = t / nst, st = t - j * nst;
     const int k0 = (s0 + st) * kLdsStageK;
@@ -1023,9 +1025,11 @@ __global__ __launch_bounds__(256) void ffn_stream_lds_kernel(
 #pragma unroll
     for (int i = 0; i < kWI; ++i) load_lds16_sv(wb, w_off[i], wl + (i * 4 + wave) * 1024);
   };
+  if (early) {
 #pragma unroll
-  for (int d = 0; d < kLdsDepth - 1; ++d)
-    if (d < total) issue_w(d, d);
+    for (int d = 0; d < kLdsDepth - 1; ++d)
+      if (d < total) issue_w(d, d);
+  }
 
   const int seg0 = offsets[e], seg1 = offsets[e + 1];
   const int g0 = kLoopGroups ? 0 : blockIdx.z / splits;
@@ -1115,10 +1119,11 @@ __global__ __launch_bounds__(256) void ffn_stream_lds_kernel(
     for (int j = 0; j < kLdsMaxCpb; ++j)
 #pragma unroll
       for (int i = 0; i < NMT; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // Prologue.  First group: the W parts are in flight already, so the issue
-    // order is W0 W1 A0 A1 and stage 0 has landed once at most A1's kAI
-    // instructions are outstanding.  Later groups: A0 W0 A1 W1, as in the loop.
-    const bool w_early = g == g0;
+    // Prologue.  First group with `early`: the W parts are in flight already,
+    // so the issue order is W0 W1 A0 A1 and stage 0 has landed once at most
+    // A1's kAI instructions are outstanding.  Otherwise A0 W0 A1 W1, as in the
+    // loop.
+    const bool w_early = early && g == g0;
 #pragma unroll
     for (int d = 0; d < kLdsDepth - 1; ++d) {
       if (d < total) {
@@ -1288,7 +1293,7 @@ static void launch_stream_lds(const FfnArgs& a, const StreamShape& sh, hipStream
   ffn_stream_lds_kernel<UP, SPLIT, NMT><<<grid, 256, 0, s>>>(
       A, (SPLIT && !UP) ? A + a.plane : nullptr, a.offsets, static_cast<const uint16_t*>(a.w),
       static_cast<const uint16_t*>(a.bias), a.out, a.plane, a.E, a.N, a.K, sh.splits, a.partial,
-      a.max_rows, a.gather, a.gather_k, cpb);
+      a.max_rows, a.gather, a.gather_k, cpb, a.max_rows >= a.E ? 1 : 0);
   if (sh.splits > 1 && !(a.defer_reduce && !UP)) {
     const size_t quads = (size_t)a.max_rows * (a.N / 4);
     ffn_splitk_reduce<uint16_t, UP, SPLIT><<<(unsigned)((quads + 255) / 256), 256, 0, s>>>(
