@@ -414,7 +414,7 @@ __global__ __launch_bounds__(kAuxThreads) void aux_finalize_kernel(
 // its time pulling its ~190 KB of x and W_r into one CU (measured: ~6.8 us of
 // loads at d = 4096, the same with 16 waves as with 8).  Here the dot products
 // are split along d instead: one wave per (d-range, token tile) computes a
-// partial logit tile from one or two 256-byte chunks of each row, so every load
+// partial logit tile from a few 256-byte chunks of each row, so every load
 // of the layer is in flight at once across the chip; then a single block sums
 // the partial tiles in d order, finishes the tokens (route_finish), reduces the
 // aux loss and z-loss directly from its own LDS, and lays out the dispatch --
